@@ -1,0 +1,196 @@
+"""Seeded synthetic inputs for the gated delta-rule scan.
+
+This module only draws random numbers and lays them out; it holds none of the
+recurrence's arithmetic.  Both the HIP path (tests, bench) and the float64
+oracle receive exactly the arrays made here, so the two sides always see the
+same values.
+
+Shapes and distributions follow the five workloads the library is measured on:
+
+  tiny       fp32, N=1, T=64, 4 heads, dk=dv=32, S0 = none
+  decode     bf16, N=256 sequences, 16 QK / 32 V heads, dk=dv=128, one token,
+             fp32 state S ~ N(0, 0.05) updated in place (512 MiB)
+  prefill    bf16, N=1, T=8192, 16 heads, dk=dv=128, S0 = none
+  qwen3next  bf16, N=4, T=16384, 16 QK / 32 V heads, dk=dv=128, S0 ~ N(0, 0.05)
+  varlen     bf16, 64 sequences with log-uniform lengths in [128, 32768] plus one
+             sequence of 262144 tokens; 16 QK / 32 V heads; 10% of tokens have
+             g = 0 and (independently) 10% have beta = 1
+
+Recipe shared by all of them: q, k ~ N(0, 1), each (token, head) vector scaled to
+unit L2 norm in float32 (the workloads state that q and k arrive normalised);
+v ~ N(0, 1); g = log(sigmoid(x)) with x ~ N(mu, sd), so alpha = exp(g) lies in
+(0, 1]; beta = sigmoid(N(0, 1)).  bf16 values are fp32 draws rounded to nearest
+even.  The head shapes (dk = dv = 128, 16 QK heads shared by 32 V heads) are the
+Qwen3-Next layer quoted on the learn-llm page "13_linear_attention_viz"
+(hybrid-layout widget); the gate ranges follow the handbook page
+"7. Gated DeltaNet: the token-by-token recurrence" (section "Run it", gate
+ranges measured on real input) and the learn-llm page's note that the gate bias
+starts at 3.0 (alpha ~ 0.95).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+BF16 = "bf16"
+F32 = "f32"
+
+
+# ---------------------------------------------------------------- bf16 helpers
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even); return raw uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    out = ((u + bias) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = np.uint16(0x7FC0)
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen raw bfloat16 bits to float32 exactly."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# ---------------------------------------------------------------- containers
+@dataclasses.dataclass
+class Inputs:
+    """One batch of packed inputs.
+
+    Layout (row-major, last index fastest):
+      q, k   [total_T, HQK, dk]   raw bf16 bits (uint16) or float32
+      v      [total_T, HV, dv]    raw bf16 bits (uint16) or float32
+      g, beta[total_T, HV]        float32 (log-decay <= 0, write strength in [0, 1])
+      cu_seqlens [N + 1] int32    sequence i owns tokens [cu[i], cu[i+1])
+      S0     [N, HV, dk, dv] float32 or None
+    """
+
+    name: str
+    dtype: str
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    g: np.ndarray
+    beta: np.ndarray
+    cu_seqlens: np.ndarray
+    S0: Optional[np.ndarray]
+    HQK: int
+    HV: int
+    dk: int
+    dv: int
+    scale: float = 1.0
+
+    @property
+    def N(self) -> int:
+        return int(self.cu_seqlens.shape[0] - 1)
+
+    @property
+    def total_T(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    def as_f64(self, name: str) -> np.ndarray:
+        """The exact values of one input tensor, widened to float64."""
+        a = getattr(self, name)
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            a = bf16_bits_to_f32(a)
+        return a.astype(np.float64)
+
+
+# ---------------------------------------------------------------- draws
+def _unit_rows(rng: np.random.Generator, shape) -> np.ndarray:
+    x = rng.standard_normal(shape, dtype=np.float32)
+    n = np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=-1, keepdims=True)).astype(np.float32)
+    return x / np.maximum(n, np.float32(1e-12))
+
+
+def _log_sigmoid(x: np.ndarray) -> np.ndarray:
+    # log(sigmoid(x)) = -log1p(exp(-x)), written to stay finite for any x
+    x = x.astype(np.float64)
+    return (np.minimum(x, 0.0) - np.log1p(np.exp(-np.abs(x)))).astype(np.float32)
+
+
+def _sigmoid(x: np.ndarray) -> np.ndarray:
+    return (1.0 / (1.0 + np.exp(-x.astype(np.float64)))).astype(np.float32)
+
+
+def _pack(x: np.ndarray, dtype: str) -> np.ndarray:
+    return f32_to_bf16_bits(x) if dtype == BF16 else np.ascontiguousarray(x, dtype=np.float32)
+
+
+def make_inputs(name: str, seed: int, seqlens, HQK: int, HV: int, dk: int, dv: int, dtype: str,
+                g_mu: float, g_sd: float, s0_sd: Optional[float], p_g0: float = 0.0,
+                p_beta1: float = 0.0, scale: float = 1.0) -> Inputs:
+    """Draw one packed batch with the shared recipe (see the module docstring)."""
+    rng = np.random.default_rng(seed)
+    seqlens = np.asarray(seqlens, dtype=np.int64)
+    cu = np.zeros(len(seqlens) + 1, dtype=np.int64)
+    np.cumsum(seqlens, out=cu[1:])
+    if cu[-1] >= 2**31:
+        raise ValueError("total length exceeds int32 cu_seqlens")
+    T = int(cu[-1])
+    q = _pack(_unit_rows(rng, (T, HQK, dk)), dtype)
+    k = _pack(_unit_rows(rng, (T, HQK, dk)), dtype)
+    v = _pack(rng.standard_normal((T, HV, dv), dtype=np.float32), dtype)
+    g = _log_sigmoid(rng.normal(g_mu, g_sd, size=(T, HV)).astype(np.float32))
+    beta = _sigmoid(rng.standard_normal((T, HV), dtype=np.float32))
+    if p_g0 > 0.0:
+        g[rng.random(T) < p_g0, :] = 0.0
+    if p_beta1 > 0.0:
+        beta[rng.random(T) < p_beta1, :] = 1.0
+    S0 = None
+    if s0_sd is not None:
+        S0 = (rng.standard_normal((len(seqlens), HV, dk, dv), dtype=np.float32) * np.float32(s0_sd))
+    return Inputs(name, dtype, q, k, v, g, beta, cu.astype(np.int32), S0, HQK, HV, dk, dv, scale)
+
+
+def varlen_lengths(seed: int = 5, n: int = 64, lo: int = 128, hi: int = 32768, tail: int = 262144):
+    """64 lengths log-uniform in [lo, hi] (rounded), then one long sequence appended last."""
+    rng = np.random.default_rng(seed + 1000)
+    lens = np.round(np.exp(rng.uniform(math.log(lo), math.log(hi), size=n))).astype(np.int64)
+    return list(lens) + ([tail] if tail else [])
+
+
+# ---------------------------------------------------------------- named workloads
+def tiny(seed: int = 1) -> Inputs:
+    """fp32, N=1, T=64, 4 heads (no sharing), dk=dv=32, S0 = none, alpha ~ 0.95."""
+    return make_inputs("tiny", seed, [64], 4, 4, 32, 32, F32, 3.0, 1.0, None)
+
+
+def decode(seed: int = 2, N: int = 256, HQK: int = 16, HV: int = 32, d: int = 128,
+           dtype: str = BF16) -> Inputs:
+    """One decode token for N sequences; state S ~ N(0, 0.05) passed as S0 (updated in place)."""
+    return make_inputs("decode", seed, [1] * N, HQK, HV, d, d, dtype, 3.0, 1.0, 0.05)
+
+
+def prefill(seed: int = 3, T: int = 8192, H: int = 16, d: int = 128, dtype: str = BF16) -> Inputs:
+    """Single sequence, HQK = HV = H, S0 = none, g = log sigmoid(N(2, 1.5))."""
+    return make_inputs("prefill", seed, [T], H, H, d, d, dtype, 2.0, 1.5, None)
+
+
+def qwen3next(seed: int = 4, N: int = 4, T: int = 16384, HQK: int = 16, HV: int = 32, d: int = 128,
+              dtype: str = BF16) -> Inputs:
+    """N sequences of T tokens, 16 QK heads shared by 32 V heads, S0 ~ N(0, 0.05)."""
+    return make_inputs("qwen3next", seed, [T] * N, HQK, HV, d, d, dtype, 2.0, 1.5, 0.05)
+
+
+def varlen(seed: int = 5, n: int = 64, lo: int = 128, hi: int = 32768, tail: int = 262144,
+           HQK: int = 16, HV: int = 32, d: int = 128, dtype: str = BF16) -> Inputs:
+    """Packed variable-length batch with 10% alpha=1 tokens and 10% beta=1 tokens."""
+    lens = varlen_lengths(seed, n, lo, hi, tail)
+    return make_inputs("varlen", seed, lens, HQK, HV, d, d, dtype, 2.0, 1.5, 0.05,
+                       p_g0=0.1, p_beta1=0.1)
+
+
+def random_small(seed: int, seqlens, HQK: int, HV: int, dk: int, dv: int, dtype: str = BF16,
+                 s0: bool = True, g_mu: float = 2.0, g_sd: float = 1.5, p_g0: float = 0.0,
+                 p_beta1: float = 0.0) -> Inputs:
+    """Small random batch for parity tests (any lengths, including zero)."""
+    return make_inputs("random", seed, seqlens, HQK, HV, dk, dv, dtype, g_mu, g_sd,
+                       0.05 if s0 else None, p_g0=p_g0, p_beta1=p_beta1)

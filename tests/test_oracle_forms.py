@@ -1,0 +1,107 @@
+"""Self-consistency of the oracle's three float64 statements and its batching rules.
+
+* the C token loop equals the numpy twin;
+* the chunked rewriting equals the token loop for any chunk size (including
+  partial last chunks) -- this pins the algebra the GPU prefill implements;
+* V head h reads QK head h // (HV / HQK), the repeat_interleave of the handbook
+  page "7. Gated DeltaNet: the token-by-token recurrence" (qwen/deltanet.py listing);
+* a packed variable-length batch equals independent runs, and carrying the final
+  state into the next call equals one long call (the delta_rule listing returns
+  the table so the next call can start from it).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gated_deltanet_recurrence_rule_amd import workloads as W
+
+
+def _seq(inp, n):
+    t0, t1 = int(inp.cu_seqlens[n]), int(inp.cu_seqlens[n + 1])
+    f = {x: inp.as_f64(x)[t0:t1] for x in ("q", "k", "v", "g", "beta")}
+    s0 = None if inp.S0 is None else inp.as_f64("S0")[n]
+    return t0, t1, f, s0
+
+
+@pytest.mark.parametrize("seed,lens,HQK,HV,d", [(1, [37, 0, 70], 2, 4, 16), (2, [5], 1, 3, 8),
+                                                (3, [129, 1], 4, 4, 32)])
+def test_c_oracle_equals_numpy_twin(seed, lens, HQK, HV, d):
+    inp = W.random_small(seed, lens, HQK, HV, d, d // 2 if d > 8 else d, dtype=W.BF16)
+    o, S = oracle.run_inputs(inp)
+    for n in range(inp.N):
+        t0, t1, f, s0 = _seq(inp, n)
+        o2, S2 = oracle.delta_rule_np(f["q"], f["k"], f["v"], f["g"], f["beta"], s0)
+        np.testing.assert_allclose(o[t0:t1], o2, atol=1e-13)
+        np.testing.assert_allclose(S[n], S2, atol=1e-13)
+
+
+@pytest.mark.parametrize("C", [1, 4, 16, 64])
+@pytest.mark.parametrize("lens", [[64], [63], [65], [130, 7, 0, 1]])
+def test_chunked_form_equals_token_loop(C, lens):
+    inp = W.random_small(100 + C, lens, 2, 4, 32, 16, dtype=W.BF16)
+    o, S = oracle.run_inputs(inp)
+    for n in range(inp.N):
+        t0, t1, f, s0 = _seq(inp, n)
+        o2, S2 = oracle.chunked_np(f["q"], f["k"], f["v"], f["g"], f["beta"], s0, C=C)
+        np.testing.assert_allclose(o[t0:t1], o2, atol=1e-12)
+        np.testing.assert_allclose(S[n], S2, atol=1e-12)
+
+
+def test_chunked_form_with_unit_gates():
+    """alpha = 1 and beta = 1 tokens (the varlen workload's special tokens) in the chunk algebra."""
+    inp = W.random_small(7, [200], 1, 2, 16, 16, dtype=W.BF16, p_g0=0.3, p_beta1=0.3)
+    o, S = oracle.run_inputs(inp)
+    _, _, f, s0 = _seq(inp, 0)
+    o2, S2 = oracle.chunked_np(f["q"], f["k"], f["v"], f["g"], f["beta"], s0, C=64)
+    np.testing.assert_allclose(o, o2, atol=1e-11)
+    np.testing.assert_allclose(S[0], S2, atol=1e-11)
+
+
+def test_gqa_equals_explicit_repeat_interleave():
+    inp = W.random_small(21, [40, 17], 3, 6, 16, 16, dtype=W.BF16)
+    o, S = oracle.run_inputs(inp)
+    rep = inp.HV // inp.HQK
+    q = np.repeat(inp.as_f64("q"), rep, axis=1)
+    k = np.repeat(inp.as_f64("k"), rep, axis=1)
+    o2, S2 = oracle.run(q, k, inp.as_f64("v"), inp.as_f64("g"), inp.as_f64("beta"),
+                        inp.cu_seqlens, inp.as_f64("S0"))
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(S, S2)
+    # and not the other plausible mapping (h % HQK)
+    q3 = np.tile(inp.as_f64("q"), (1, rep, 1))
+    k3 = np.tile(inp.as_f64("k"), (1, rep, 1))
+    o3, _ = oracle.run(q3, k3, inp.as_f64("v"), inp.as_f64("g"), inp.as_f64("beta"),
+                       inp.cu_seqlens, inp.as_f64("S0"))
+    assert np.abs(o3 - o).max() > 1e-3
+
+
+def test_varlen_equals_independent_runs():
+    inp = W.random_small(22, [33, 0, 1, 64, 65], 2, 4, 16, 8, dtype=W.BF16)
+    o, S = oracle.run_inputs(inp)
+    for n in range(inp.N):
+        t0, t1, f, s0 = _seq(inp, n)
+        o2, S2 = oracle.run(f["q"], f["k"], f["v"], f["g"], f["beta"], [0, t1 - t0],
+                            s0[None])
+        np.testing.assert_array_equal(o[t0:t1], o2)
+        np.testing.assert_array_equal(S[n], S2[0])
+    # an empty sequence hands its start state through unchanged
+    np.testing.assert_array_equal(S[1], inp.as_f64("S0")[1])
+
+
+def test_state_carry_equals_one_long_call():
+    inp = W.random_small(23, [150], 2, 2, 16, 16, dtype=W.BF16)
+    f = {x: inp.as_f64(x) for x in ("q", "k", "v", "g", "beta")}
+    o, S = oracle.run_inputs(inp)
+    cut = 61
+    a = {x: f[x][:cut] for x in f}
+    b = {x: f[x][cut:] for x in f}
+    o1, S1 = oracle.run(a["q"], a["k"], a["v"], a["g"], a["beta"], [0, cut], inp.as_f64("S0"))
+    o2, S2 = oracle.run(b["q"], b["k"], b["v"], b["g"], b["beta"], [0, 150 - cut], S1)
+    np.testing.assert_allclose(np.concatenate([o1, o2]), o, atol=1e-13)
+    np.testing.assert_allclose(S2, S, atol=1e-13)
+
+
+def test_oracle_rejects_bad_sizes():
+    inp = W.random_small(24, [4], 2, 3, 8, 8, dtype=W.BF16)  # HV % HQK != 0
+    with pytest.raises(ValueError):
+        oracle.run_inputs(inp)
