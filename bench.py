@@ -1,0 +1,194 @@
+#!/usr/bin/env python3
+"""Throughput of the gated delta-rule scan on one MI355X.
+
+One step = one pass of the whole hot path on synthetic inputs already resident
+in HBM:
+  * prefill of the Qwen3-Next-shaped batch: 4 sequences x 16384 tokens, 16 QK
+    heads shared by 32 V heads, dk = dv = 128, bf16 q/k/v/o, fp32 S0 -> S_T;
+  * one decode step of 256 sequences with the same head layout, fp32 state
+    (512 MiB) updated in place.
+
+`value` is the prefill throughput in Mtok/s (prefill tokens / prefill time);
+the decode leg is reported beside it as state GB/s (2 |S| / time).  Kernel
+times come from HIP events recorded on the stream the library launches on.
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0     # dense bf16 MFMA
+PEAK_FP32_VALU_TFLOPS = 157.3  # fp32 vector
+CHUNK_REF = 64                # chunk length the algorithmic flop count is quoted at
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_alg(N, T, HQK, HV, dk, dv, e, with_s0):
+    """Algorithmic bytes and flops of one prefill call (inputs read once, outputs written once)."""
+    r = HV // HQK
+    tok_head = N * T * HV
+    bytes_ = tok_head * ((2 * dk * e) / r + 2 * dv * e + 8) + N * HV * dk * dv * 4 * (2 if with_s0 else 1)
+    flops_chunk = tok_head * (10 * CHUNK_REF * dk + 6 * dk * dv)
+    flops_rec = tok_head * 7 * dk * dv
+    return int(bytes_), int(flops_chunk), int(flops_rec)
+
+
+def decode_alg(N, HQK, HV, dk, dv, e):
+    bytes_ = N * HV * 2 * dk * dv * 4 + N * HQK * 2 * dk * e + N * HV * 2 * dv * e + N * HV * 8
+    return int(bytes_), int(N * HV * 7 * dk * dv), int(N * HV * 2 * dk * dv * 4)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=8192,
+                    help="tokens of sequence 0 (all V heads) the CPU oracle runs on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
+              "the scan shards by (sequence, head) with no exchange, so there is nothing "
+              "multi-GPU to time here.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from gated_deltanet_recurrence_rule_amd import binding, workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = binding.load()
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    t0 = time.time()
+    pf = W.qwen3next()
+    dc = W.decode()
+    log(f"inputs generated in {time.time() - t0:.1f} s")
+    P = dict(q=up(pf.q), k=up(pf.k), v=up(pf.v), g=up(pf.g), beta=up(pf.beta),
+             cu=up(pf.cu_seqlens), S0=up(pf.S0))
+    D = dict(q=up(dc.q), k=up(dc.k), v=up(dc.v), g=up(dc.g), beta=up(dc.beta), S=up(dc.S0))
+    N, T = pf.N, pf.total_T // pf.N
+    o_p = torch.empty((pf.total_T, pf.HV, pf.dv), dtype=torch.bfloat16, device=dev)
+    S_T = torch.empty((pf.N, pf.HV, pf.dk, pf.dv), dtype=torch.float32, device=dev)
+    o_d = torch.empty((dc.N, dc.HV, dc.dv), dtype=torch.bfloat16, device=dev)
+    ws_bytes = binding.prefill_workspace_size(pf.N, pf.total_T, pf.HQK, pf.HV, pf.dk, pf.dv,
+                                              torch.bfloat16)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def prefill():
+        binding.prefill(P["q"], P["k"], P["v"], P["g"], P["beta"], cu_seqlens=P["cu"],
+                        S0=P["S0"], o=o_p, S_T=S_T, workspace=ws)
+
+    def decode():
+        binding.decode_step(D["q"], D["k"], D["v"], D["g"], D["beta"], D["S"], o=o_d)
+
+    for _ in range(args.warmup):
+        prefill()
+        decode()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        prefill()
+        e1.record(stream)
+        decode()
+        e2.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    pre_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    dec_ms = [b.elapsed_time(c) for _, b, c in ev]
+    step_ms = [a.elapsed_time(c) for a, _, c in ev]
+    pre_avg = float(np.mean(pre_ms))
+    dec_avg = float(np.mean(dec_ms))
+
+    e = 2  # bf16 bytes
+    pb, pf_chunk, pf_rec = prefill_alg(N, T, pf.HQK, pf.HV, pf.dk, pf.dv, e, True)
+    db, dflops, dstate = decode_alg(dc.N, dc.HQK, dc.HV, dc.dk, dc.dv, e)
+    kname = lib.gdn_prefill_kernel_name(pf.N, pf.total_T, pf.HQK, pf.HV, pf.dk, pf.dv, 0).decode() \
+        if hasattr(lib, "gdn_prefill_kernel_name") else "prefill_recurrent"
+    if "chunk" in kname:
+        pre_roof = {"bound": "mfma", "achieved": pf_chunk / (pre_avg * 1e-3) / 1e12,
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        pre_roof = {"bound": "alu", "achieved": pf_rec / (pre_avg * 1e-3) / 1e12,
+                    "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s"}
+    pre_roof["frac"] = pre_roof["achieved"] / pre_roof["peak"]
+    pre_roof["traffic"] = None
+    pre_roof["kernel"] = kname
+    dec_gbps = db / (dec_avg * 1e-3) / 1e9
+    dec_roof = {"bound": "hbm", "achieved": dec_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": dec_gbps / PEAK_HBM_GBPS, "traffic": None, "kernel": "decode"}
+    pre_hbm_frac = pb / (pre_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS
+    value = N * T / (pre_avg * 1e-3) / 1e6
+    state_gbps = dstate / (dec_avg * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        ts = min(args.cpu_sample_tokens, T)
+        sl = slice(0, ts)
+        f64 = {x: pf.as_f64(x)[sl] for x in ("q", "k", "v", "g", "beta")}
+        s0 = pf.as_f64("S0")[:1]
+        t0 = time.perf_counter()
+        oracle.run(f64["q"], f64["k"], f64["v"], f64["g"], f64["beta"], [0, ts], s0)
+        tc = time.perf_counter() - t0
+        d64 = {x: dc.as_f64(x) for x in ("q", "k", "v", "g", "beta", "S0")}
+        t1 = time.perf_counter()
+        oracle.run(d64["q"], d64["k"], d64["v"], d64["g"], d64["beta"], dc.cu_seqlens, d64["S0"])
+        td = time.perf_counter() - t1
+        cpu = {"value": ts / tc / 1e6, "unit": "Mtok/s", "cores": oracle.threads(), "kind": "oracle",
+               "sample": f"float64 token loop on sequence 0 of the prefill batch, first {ts} tokens, "
+                         f"all {pf.HV} V heads ({tc:.2f} s); decode leg: full 256-sequence step "
+                         f"({td:.2f} s)",
+               "decode_state_GBps": dstate / td / 1e9}
+        log(f"cpu oracle: {ts} tokens in {tc:.2f} s, decode step in {td:.2f} s")
+
+    out = {
+        "metric": "prefill Mtok/s + decode state GB/s on 1 GPU, as % of MFMA/HBM roofline",
+        "value": value, "unit": "Mtok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": float(np.mean(step_ms)),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Qwen3-Next-shaped prefill (4 x 16384 tokens, 16 QK / 32 V heads, "
+                               "dk=dv=128, bf16, fp32 S0) + decode step (256 sequences, same heads, "
+                               "512 MiB fp32 state)",
+                   "prefill_tokens": N * T, "decode_sequences": dc.N, "parallelism": "none"},
+        "prefill_ms": pre_avg, "prefill_hbm_frac": pre_hbm_frac,
+        "decode_us": dec_avg * 1e3, "decode_state_GBps": state_gbps,
+        "roofline": pre_roof if pre_avg >= dec_avg else dec_roof,
+        "roofline_prefill": pre_roof, "roofline_decode": dec_roof,
+        "cpu_baseline": cpu,
+        "wall_s_timed": wall,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

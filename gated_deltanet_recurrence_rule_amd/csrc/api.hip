@@ -1,0 +1,144 @@
+// api.hip -- the C ABI of libgdn: argument checks, then kernel launches.
+//
+// Every check runs before anything is enqueued, so a failing call writes
+// nothing.  The declarations and their contracts are in include/gdn.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "gdn.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+gdn_status fail(gdn_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool dim_ok(int32_t d) { return d == 32 || d == 64 || d == 128; }
+
+// `tokens` is the number of tokens the call touches; with none, the token
+// arrays may be NULL (an empty tensor has no storage).
+gdn_status check_common(const void *q, const void *k, const void *v, const float *g,
+                        const float *beta, const void *o, int32_t N, int32_t HQK, int32_t HV,
+                        int32_t dk, int32_t dv, gdn_dtype dtype, int64_t tokens) {
+    if (dtype != GDN_BF16 && dtype != GDN_F32) return fail(GDN_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+    if (N < 0) return fail(GDN_ERR_SHAPE, "N = %d is negative", N);
+    if (HQK <= 0 || HV <= 0) return fail(GDN_ERR_SHAPE, "head counts must be positive (HQK=%d, HV=%d)", HQK, HV);
+    if (HV % HQK != 0) return fail(GDN_ERR_SHAPE, "HV (%d) is not a multiple of HQK (%d)", HV, HQK);
+    if (!dim_ok(dk) || !dim_ok(dv))
+        return fail(GDN_ERR_UNSUPPORTED, "dk=%d, dv=%d: each must be 32, 64 or 128", dk, dv);
+    if (tokens == 0) return GDN_OK;
+    if (!q || !k || !v || !g || !beta || !o) return fail(GDN_ERR_NULL, "q, k, v, g, beta and o must be non-NULL");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+        return fail(GDN_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
+    if (!aligned(g, 4) || !aligned(beta, 4)) return fail(GDN_ERR_ALIGN, "g and beta must be 4-byte aligned");
+    return GDN_OK;
+}
+
+gdn_status hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return GDN_OK;
+    return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gdn_status_str(gdn_status s) {
+    switch (s) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_NULL: return "null pointer";
+        case GDN_ERR_SHAPE: return "bad shape";
+        case GDN_ERR_DTYPE: return "bad dtype";
+        case GDN_ERR_UNSUPPORTED: return "unsupported head dimension";
+        case GDN_ERR_ALIGN: return "misaligned pointer";
+        case GDN_ERR_SEQLENS: return "bad sequence lengths";
+        case GDN_ERR_WORKSPACE: return "workspace too small";
+        case GDN_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *gdn_last_error(void) { return g_last_error; }
+
+int32_t gdn_version(void) { return 100; /* 0.1.0 */ }
+
+gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, float *S, void *o, int32_t N, int32_t HQK,
+                           int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype, float scale,
+                           hipStream_t stream) {
+    g_last_error[0] = 0;
+    gdn_status st = check_common(q, k, v, g, beta, o, N, HQK, HV, dk, dv, dtype, N);
+    if (st != GDN_OK) return st;
+    if (N == 0) return GDN_OK;
+    if (!S) return fail(GDN_ERR_NULL, "S must be non-NULL");
+    if (!aligned(S, 16)) return fail(GDN_ERR_ALIGN, "S must be 16-byte aligned");
+    if ((int64_t)N * HV > 0x7fffffffLL) return fail(GDN_ERR_SHAPE, "N * HV exceeds the grid limit");
+    gdn::DecodeArgs a{q, k, v, g, beta, S, o, N, HQK, HV, dk, dv, scale};
+    return hip_status(gdn::launch_decode(a, dtype == GDN_BF16, stream), "decode launch");
+}
+
+size_t gdn_prefill_workspace_size(int32_t N, int64_t total_T, int32_t HQK, int32_t HV,
+                                  int32_t dk, int32_t dv, gdn_dtype dtype) {
+    (void)N; (void)total_T; (void)HQK; (void)HV; (void)dk; (void)dv; (void)dtype;
+    return 0;
+}
+
+gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float *g,
+                       const float *beta, const int32_t *cu_seqlens,
+                       const int32_t *cu_seqlens_host, int32_t N, int64_t total_T,
+                       const float *S0, void *o, float *S_T, int32_t HQK, int32_t HV, int32_t dk,
+                       int32_t dv, gdn_dtype dtype, float scale, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+    g_last_error[0] = 0;
+    if (total_T < 0) return fail(GDN_ERR_SHAPE, "total_T = %lld is negative", (long long)total_T);
+    gdn_status st = check_common(q, k, v, g, beta, o, N, HQK, HV, dk, dv, dtype, total_T);
+    if (st != GDN_OK) return st;
+    if (S0 && !aligned(S0, 16)) return fail(GDN_ERR_ALIGN, "S0 must be 16-byte aligned");
+    if (S_T && !aligned(S_T, 16)) return fail(GDN_ERR_ALIGN, "S_T must be 16-byte aligned");
+    if (cu_seqlens && !aligned(cu_seqlens, 4)) return fail(GDN_ERR_ALIGN, "cu_seqlens must be 4-byte aligned");
+    if ((int64_t)N * HV > 0x7fffffffLL) return fail(GDN_ERR_SHAPE, "N * HV exceeds the grid limit");
+    if (total_T > 0x7fffffffLL) return fail(GDN_ERR_SHAPE, "total_T must fit in int32");
+
+    int64_t eq_len = 0;
+    if (cu_seqlens_host) {
+        if (N > 0 && cu_seqlens_host[0] != 0) return fail(GDN_ERR_SEQLENS, "cu_seqlens[0] must be 0");
+        for (int32_t i = 0; i < N; ++i)
+            if (cu_seqlens_host[i + 1] < cu_seqlens_host[i])
+                return fail(GDN_ERR_SEQLENS, "cu_seqlens decreases at %d", i);
+        if (N > 0 && (int64_t)cu_seqlens_host[N] != total_T)
+            return fail(GDN_ERR_SEQLENS, "cu_seqlens[N] = %d but total_T = %lld", cu_seqlens_host[N],
+                        (long long)total_T);
+    }
+    if (!cu_seqlens) {
+        if (N == 0) {
+            if (total_T != 0) return fail(GDN_ERR_SEQLENS, "N = 0 with total_T = %lld", (long long)total_T);
+        } else {
+            if (total_T % N != 0)
+                return fail(GDN_ERR_SEQLENS, "cu_seqlens is NULL and N (%d) does not divide total_T (%lld)",
+                            N, (long long)total_T);
+            eq_len = total_T / N;
+        }
+    }
+    const size_t need = gdn_prefill_workspace_size(N, total_T, HQK, HV, dk, dv, dtype);
+    if (workspace_bytes < need)
+        return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    if (need > 0 && !workspace) return fail(GDN_ERR_NULL, "workspace must be non-NULL");
+    if (workspace && !aligned(workspace, 16)) return fail(GDN_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if (N == 0) return GDN_OK;
+
+    gdn::PrefillArgs a{q, k, v, g, beta, cu_seqlens, eq_len, N, total_T, S0, o, S_T,
+                       HQK, HV, dk, dv, scale, workspace, workspace_bytes};
+    return hip_status(gdn::launch_prefill_recurrent(a, dtype == GDN_BF16, stream), "prefill launch");
+}
+
+}  // extern "C"

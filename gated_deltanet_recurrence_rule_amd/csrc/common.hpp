@@ -1,0 +1,57 @@
+// common.hpp -- small device helpers shared by the libgdn kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------------ bf16 <-> fp32
+// bf16 is carried as raw uint16 bits.  Widening is exact; narrowing rounds to
+// nearest, ties to even, and keeps NaN quiet.
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Element access for the two I/O types (float, or bf16 bits in uint16_t).
+template <typename T> struct elem;
+template <> struct elem<float> {
+    static __device__ __forceinline__ float ld(const float *p) { return *p; }
+    static __device__ __forceinline__ void st(float *p, float x) { *p = x; }
+};
+template <> struct elem<uint16_t> {
+    static __device__ __forceinline__ float ld(const uint16_t *p) { return bf16_to_f32(*p); }
+    static __device__ __forceinline__ void st(uint16_t *p, float x) { *p = f32_to_bf16(x); }
+};
+
+// ------------------------------------------------------------------ wave64 reductions
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// 1 / max(sqrt(ss), eps): the L2-normalisation factor x / max(|x|, eps).
+__device__ __forceinline__ float inv_norm(float ss) {
+    const float n = sqrtf(ss);
+    return 1.0f / fmaxf(n, 1e-12f);
+}
+
+// ------------------------------------------------------------------ streaming access
+// The state is touched exactly once per decode step: keep it out of the caches.
+__device__ __forceinline__ f32x4 ld_stream(const float *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+}
+__device__ __forceinline__ void st_stream(float *p, f32x4 x) {
+    __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>(p));
+}
+
+}  // namespace gdn

@@ -1,0 +1,39 @@
+// kernels.hpp -- host-side launchers of the libgdn kernels (internal, not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Arguments shared by the launchers, already validated by the C-ABI layer.
+struct DecodeArgs {
+    const void *q, *k, *v;
+    const float *g, *beta;
+    float *S;
+    void *o;
+    int32_t N, HQK, HV, dk, dv;
+    float scale;
+};
+
+struct PrefillArgs {
+    const void *q, *k, *v;
+    const float *g, *beta;
+    const int32_t *cu_seqlens;  // device, or nullptr => equal lengths eq_len
+    int64_t eq_len;
+    int32_t N;
+    int64_t total_T;
+    const float *S0;
+    void *o;
+    float *S_T;
+    int32_t HQK, HV, dk, dv;
+    float scale;
+    void *workspace;
+    size_t workspace_bytes;
+};
+
+// Each returns hipSuccess or the launch error.  `bf16` selects the I/O type.
+hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t stream);
+hipError_t launch_prefill_recurrent(const PrefillArgs &a, bool bf16, hipStream_t stream);
+
+}  // namespace gdn

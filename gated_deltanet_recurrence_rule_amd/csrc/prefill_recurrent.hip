@@ -1,0 +1,139 @@
+// prefill_recurrent.hip -- token-serial prefill with fp32 arithmetic throughout.
+//
+// This is the direct form of the handbook's delta_rule (page "7. Gated DeltaNet:
+// the token-by-token recurrence", qwen/deltanet.py listing and section "The
+// formula"): for each token, decay, look up, write the difference, read.  It is
+// the library's path for fp32 inputs (where every product must stay fp32) and
+// for shapes the chunked MFMA kernel does not cover.
+//
+// Mapping: one wave per (sequence, V head, 64-column slice of dv).  Lane j owns
+// column j of the table, all DK rows of it in VGPRs, so both reductions over the
+// key dimension (S^T k and S^T q) are lane-local; the only cross-lane work per
+// token is the L2 norm of q and k, done with wave reductions, and a broadcast of
+// the normalised vectors through LDS.  Per token and lane:
+//   p = S^T k^,  r = S^T q^  (from the undecayed table)
+//   d = b (v - a p),  o = a r + (q^ . k^) d,  S <- a S + k^ d
+// (the same identity as the decode step: the new table is a S + k^ d^T).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace gdn {
+
+namespace {
+
+template <int DK, typename T>
+__global__ __launch_bounds__(64) void prefill_recurrent_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const float *__restrict__ g, const float *__restrict__ beta,
+    const int32_t *__restrict__ cu_seqlens, int64_t eq_len, const float *__restrict__ S0,
+    T *__restrict__ o, float *__restrict__ S_T, int HV, int DV, int rep, float scale) {
+    constexpr int EPL = (DK + 63) / 64;  // q/k elements per lane
+    __shared__ float kh_s[DK];
+    __shared__ float qh_s[DK];
+
+    const int unit = blockIdx.x;  // n * HV + h
+    const int h = unit % HV;
+    const int n = unit / HV;
+    const int hq = h / rep;
+    const int HQK = HV / rep;
+    const int lane = threadIdx.x;
+    const int j = blockIdx.y * 64 + lane;
+    const bool active = j < DV;
+
+    int64_t t0, t1;
+    if (cu_seqlens) {
+        t0 = cu_seqlens[n];
+        t1 = cu_seqlens[n + 1];
+    } else {
+        t0 = (int64_t)n * eq_len;
+        t1 = t0 + eq_len;
+    }
+
+    float s[DK];
+    const size_t tab = (size_t)unit * DK * DV;
+#pragma unroll
+    for (int i = 0; i < DK; ++i) s[i] = (S0 && active) ? S0[tab + (size_t)i * DV + j] : 0.f;
+
+    for (int64_t t = t0; t < t1; ++t) {
+        const T *qp = q + ((size_t)t * HQK + hq) * DK;
+        const T *kp = k + ((size_t)t * HQK + hq) * DK;
+        float qx[EPL], kx[EPL];
+        float sq = 0.f, sk = 0.f, sqk = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const int i = lane + 64 * e;
+            qx[e] = i < DK ? elem<T>::ld(qp + i) : 0.f;
+            kx[e] = i < DK ? elem<T>::ld(kp + i) : 0.f;
+            sq += qx[e] * qx[e];
+            sk += kx[e] * kx[e];
+            sqk += qx[e] * kx[e];
+        }
+        sq = wave_sum(sq);
+        sk = wave_sum(sk);
+        sqk = wave_sum(sqk);
+        const float rq = inv_norm(sq) * scale;
+        const float rk = inv_norm(sk);
+        const float qk = sqk * rq * rk;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const int i = lane + 64 * e;
+            if (i < DK) {
+                qh_s[i] = qx[e] * rq;
+                kh_s[i] = kx[e] * rk;
+            }
+        }
+        __syncthreads();
+
+        const size_t tv = (size_t)t * HV + h;
+        const float a = expf(g[tv]);
+        const float b = beta[tv];
+        const float vj = active ? elem<T>::ld(v + tv * DV + j) : 0.f;
+
+        float p = 0.f, r = 0.f;
+#pragma unroll
+        for (int i = 0; i < DK; ++i) {
+            p += s[i] * kh_s[i];
+            r += s[i] * qh_s[i];
+        }
+        const float d = b * (vj - a * p);
+#pragma unroll
+        for (int i = 0; i < DK; ++i) s[i] = a * s[i] + kh_s[i] * d;
+        if (active) elem<T>::st(o + tv * DV + j, a * r + qk * d);
+        __syncthreads();  // kh_s / qh_s are rewritten by the next token
+    }
+
+    if (S_T && active) {
+#pragma unroll
+        for (int i = 0; i < DK; ++i) S_T[tab + (size_t)i * DV + j] = s[i];
+    }
+}
+
+template <int DK, typename T>
+hipError_t launch(const PrefillArgs &a, hipStream_t stream) {
+    const int rep = a.HV / a.HQK;
+    dim3 grid((unsigned)((int64_t)a.N * a.HV), (unsigned)((a.dv + 63) / 64));
+    hipLaunchKernelGGL((prefill_recurrent_kernel<DK, T>), grid, dim3(64), 0, stream,
+                       static_cast<const T *>(a.q), static_cast<const T *>(a.k),
+                       static_cast<const T *>(a.v), a.g, a.beta, a.cu_seqlens, a.eq_len, a.S0,
+                       static_cast<T *>(a.o), a.S_T, a.HV, a.dv, rep, a.scale);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch(const PrefillArgs &a, hipStream_t stream) {
+    switch (a.dk) {
+        case 32: return launch<32, T>(a, stream);
+        case 64: return launch<64, T>(a, stream);
+        case 128: return launch<128, T>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_recurrent(const PrefillArgs &a, bool bf16, hipStream_t stream) {
+    if (a.N == 0) return hipSuccess;
+    return bf16 ? dispatch<uint16_t>(a, stream) : dispatch<float>(a, stream);
+}
+
+}  // namespace gdn

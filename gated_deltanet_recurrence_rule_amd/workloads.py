@@ -29,8 +29,10 @@ starts at 3.0 (alpha ~ 0.95).
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import Optional
 
 import numpy as np
@@ -104,10 +106,46 @@ class Inputs:
 
 
 # ---------------------------------------------------------------- draws
+# Large arrays are drawn in row blocks, each from its own generator seeded by
+# (seed, array id, block index), so the values do not depend on how many
+# threads fill them.
+_BLOCK_ELEMS = 1 << 21
+_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def _block_rng(seed: int, array_id: int, block: int) -> np.random.Generator:
+    return np.random.default_rng([seed, array_id, block])
+
+
+def _fill_blocks(seed: int, array_id: int, shape, out_dtype, make):
+    """out[rows of block b] = make(rng_b, block_shape) for every block, in parallel."""
+    shape = tuple(int(x) for x in shape)
+    out = np.empty(shape, dtype=out_dtype)
+    rows = shape[0]
+    per_row = int(np.prod(shape[1:], dtype=np.int64)) if len(shape) > 1 else 1
+    brows = max(1, _BLOCK_ELEMS // max(1, per_row))
+    nblk = (rows + brows - 1) // brows
+
+    def job(b):
+        r0, r1 = b * brows, min(rows, (b + 1) * brows)
+        out[r0:r1] = make(_block_rng(seed, array_id, b), (r1 - r0,) + shape[1:])
+
+    if nblk <= 1:
+        for b in range(nblk):
+            job(b)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=_THREADS) as ex:
+            list(ex.map(job, range(nblk)))
+    return out
+
+
 def _unit_rows(rng: np.random.Generator, shape) -> np.ndarray:
+    """Standard-normal vectors (last axis) scaled to unit length in float32."""
     x = rng.standard_normal(shape, dtype=np.float32)
-    n = np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=-1, keepdims=True)).astype(np.float32)
-    return x / np.maximum(n, np.float32(1e-12))
+    flat = x.reshape(-1, shape[-1])
+    n = np.sqrt(np.einsum("ij,ij->i", flat, flat))[:, None]
+    flat /= np.maximum(n, np.float32(1e-12))
+    return x
 
 
 def _log_sigmoid(x: np.ndarray) -> np.ndarray:
@@ -128,25 +166,31 @@ def make_inputs(name: str, seed: int, seqlens, HQK: int, HV: int, dk: int, dv: i
                 g_mu: float, g_sd: float, s0_sd: Optional[float], p_g0: float = 0.0,
                 p_beta1: float = 0.0, scale: float = 1.0) -> Inputs:
     """Draw one packed batch with the shared recipe (see the module docstring)."""
-    rng = np.random.default_rng(seed)
     seqlens = np.asarray(seqlens, dtype=np.int64)
     cu = np.zeros(len(seqlens) + 1, dtype=np.int64)
     np.cumsum(seqlens, out=cu[1:])
     if cu[-1] >= 2**31:
         raise ValueError("total length exceeds int32 cu_seqlens")
     T = int(cu[-1])
-    q = _pack(_unit_rows(rng, (T, HQK, dk)), dtype)
-    k = _pack(_unit_rows(rng, (T, HQK, dk)), dtype)
-    v = _pack(rng.standard_normal((T, HV, dv), dtype=np.float32), dtype)
-    g = _log_sigmoid(rng.normal(g_mu, g_sd, size=(T, HV)).astype(np.float32))
-    beta = _sigmoid(rng.standard_normal((T, HV), dtype=np.float32))
+    io = np.uint16 if dtype == BF16 else np.float32
+    q = _fill_blocks(seed, 0, (T, HQK, dk), io, lambda r, s: _pack(_unit_rows(r, s), dtype))
+    k = _fill_blocks(seed, 1, (T, HQK, dk), io, lambda r, s: _pack(_unit_rows(r, s), dtype))
+    v = _fill_blocks(seed, 2, (T, HV, dv), io,
+                     lambda r, s: _pack(r.standard_normal(s, dtype=np.float32), dtype))
+    g = _fill_blocks(seed, 3, (T, HV), np.float32,
+                     lambda r, s: _log_sigmoid(r.normal(g_mu, g_sd, size=s).astype(np.float32)))
+    beta = _fill_blocks(seed, 4, (T, HV), np.float32,
+                        lambda r, s: _sigmoid(r.standard_normal(s, dtype=np.float32)))
+    rng = np.random.default_rng([seed, 5])
     if p_g0 > 0.0:
         g[rng.random(T) < p_g0, :] = 0.0
     if p_beta1 > 0.0:
         beta[rng.random(T) < p_beta1, :] = 1.0
     S0 = None
-    if s0_sd is not None:
-        S0 = (rng.standard_normal((len(seqlens), HV, dk, dv), dtype=np.float32) * np.float32(s0_sd))
+    if s0_sd is not None and len(seqlens) > 0:
+        S0 = _fill_blocks(seed, 6, (len(seqlens) * HV, dk, dv), np.float32,
+                          lambda r, s: r.standard_normal(s, dtype=np.float32) * np.float32(s0_sd))
+        S0 = S0.reshape(len(seqlens), HV, dk, dv)
     return Inputs(name, dtype, q, k, v, g, beta, cu.astype(np.int32), S0, HQK, HV, dk, dv, scale)
 
 

@@ -1,0 +1,143 @@
+/*
+ * gdn.h -- C ABI of libgdn, the gated delta-rule scan on MI355X (gfx950).
+ *
+ * The operation (handbook page "7. Gated DeltaNet: the token-by-token
+ * recurrence", section "The formula", and the figure "one step of the delta
+ * rule"): each V head keeps a dk x dv fp32 memory table S.  Every token t,
+ * with unit-normalised key k_t and query q_t, decay alpha_t = exp(g_t) and
+ * write strength beta_t, does
+ *
+ *     S_t = alpha_t S_{t-1} + beta_t k_t (v_t - alpha_t S_{t-1}^T k_t)^T
+ *     o_t = S_t^T (scale * q_t)
+ *
+ * i.e. decay the table, look k_t up, write beta times the difference into k_t's
+ * row, read with q_t.  The learn-llm page 13_linear_attention_viz states the
+ * same rule transposed (its update-rule table, Gated DeltaNet row); this
+ * library uses the handbook's orientation: S is [dk, dv], dv contiguous.
+ *
+ * Normalisation is done inside the library: q and k are divided by
+ * max(|x|_2, 1e-12) per (token, QK head) before use (the handbook's
+ * "Why are q and k normalized to unit length first?").  `scale` multiplies the
+ * normalised query; the handbook's listing uses 1/sqrt(dk), its formula uses 1.
+ *
+ * Head sharing: V head h reads QK head h / (HV / HQK) (the repeat_interleave of
+ * the handbook's qwen/deltanet.py listing).  g and beta are per V head.
+ *
+ * Conventions for every entry point
+ *  - Tensor pointers are DEVICE pointers to contiguous row-major arrays (last
+ *    index fastest), 16-byte aligned, owned by the caller.  g and beta need
+ *    4-byte alignment, cu_seqlens 4-byte alignment.
+ *  - q, k, v and o share one element type (gdn_dtype).  g, beta, S, S0 and S_T
+ *    are always fp32 (the handbook keeps the table in fp32 because bf16 cannot
+ *    hold hundreds of accumulated steps).
+ *  - dk and dv must each be 32, 64 or 128.  HV must be a multiple of HQK.
+ *  - Calls are asynchronous: work is enqueued on `stream` and the call returns.
+ *    Outputs are valid after the stream is synchronised; inputs must not change
+ *    before that.  The library allocates no device memory and keeps no state
+ *    between calls other than a per-device property cache.
+ *  - Every argument is checked before anything is enqueued.  On any error the
+ *    call returns a negative gdn_status, enqueues nothing and writes nothing;
+ *    gdn_last_error() then gives a message (thread-local).
+ *  - Values are not checked: g <= 0 and 0 <= beta <= 1 are the caller's contract
+ *    (alpha = exp(g) in (0, 1]); NaN and Inf propagate through the arithmetic.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL = -1,        /* a required pointer is NULL                           */
+    GDN_ERR_SHAPE = -2,       /* negative size, HV % HQK != 0, mismatched lengths      */
+    GDN_ERR_DTYPE = -3,       /* unknown gdn_dtype                                     */
+    GDN_ERR_UNSUPPORTED = -4, /* dk or dv not in {32, 64, 128}                         */
+    GDN_ERR_ALIGN = -5,       /* a pointer breaks the alignment rule above             */
+    GDN_ERR_SEQLENS = -6,     /* cu_seqlens_host malformed, or N does not divide T     */
+    GDN_ERR_WORKSPACE = -7,   /* workspace smaller than gdn_prefill_workspace_size()   */
+    GDN_ERR_HIP = -8          /* the HIP runtime reported an error at launch           */
+} gdn_status;
+
+typedef enum {
+    GDN_BF16 = 0, /* q, k, v, o are bfloat16; o is rounded to nearest even */
+    GDN_F32 = 1   /* q, k, v, o are float32                                */
+} gdn_dtype;
+
+/*
+ * gdn_decode_step -- advance every sequence and V head by one token, in place.
+ * (The handbook's delta_rule with one token and a kept table; its chapter
+ * notes that the table is carried from call to call.)
+ *
+ *   q, k   [N, HQK, dk]      dtype      this token's query and key (any norm)
+ *   v      [N, HV, dv]       dtype      this token's value
+ *   g      [N, HV]           fp32       log-decay (alpha = exp(g))
+ *   beta   [N, HV]           fp32       write strength
+ *   S      [N, HV, dk, dv]   fp32       in: S_{t-1}; out: S_t (updated in place)
+ *   o      [N, HV, dv]       dtype      out: S_t^T (scale * q^)
+ *
+ * N = 0 is a valid no-op.  o must not overlap any input.
+ */
+gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, float *S, void *o, int32_t N, int32_t HQK,
+                           int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype, float scale,
+                           hipStream_t stream);
+
+/*
+ * gdn_prefill_workspace_size -- bytes of device workspace gdn_prefill needs for
+ * these sizes (0 means the workspace pointer may be NULL).
+ */
+size_t gdn_prefill_workspace_size(int32_t N, int64_t total_T, int32_t HQK, int32_t HV,
+                                  int32_t dk, int32_t dv, gdn_dtype dtype);
+
+/*
+ * gdn_prefill -- run whole sequences of a packed batch (the handbook's
+ * delta_rule(q, k, v, g, beta, S) -> (out, S) over a batch of sequences).
+ *
+ *   q, k        [total_T, HQK, dk]  dtype  tokens of all sequences, packed
+ *   v           [total_T, HV, dv]   dtype
+ *   g, beta     [total_T, HV]       fp32
+ *   cu_seqlens  [N + 1] int32, device: sequence i owns tokens
+ *               [cu_seqlens[i], cu_seqlens[i+1]); cu[0] = 0, non-decreasing,
+ *               cu[N] = total_T.  Empty sequences are allowed.  NULL means N
+ *               equal sequences of total_T / N tokens (N must divide total_T).
+ *   cu_seqlens_host  optional host copy of the same array.  When given it is
+ *               validated (GDN_ERR_SEQLENS) and used to schedule long sequences
+ *               first; when NULL the device array is trusted as is.
+ *   S0          [N, HV, dk, dv] fp32 start tables, or NULL for empty tables
+ *   o           [total_T, HV, dv] dtype, out: per-token reads
+ *   S_T         [N, HV, dk, dv] fp32, out: final tables, or NULL to skip.
+ *               S_T may be the same pointer as S0 (in-place carry); any other
+ *               overlap between outputs and inputs is not allowed.
+ *   workspace   device scratch of at least gdn_prefill_workspace_size() bytes,
+ *               16-byte aligned (may be NULL when that size is 0).
+ *
+ * N = 0 is a valid no-op.
+ */
+gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float *g,
+                       const float *beta, const int32_t *cu_seqlens,
+                       const int32_t *cu_seqlens_host, int32_t N, int64_t total_T,
+                       const float *S0, void *o, float *S_T, int32_t HQK, int32_t HV, int32_t dk,
+                       int32_t dv, gdn_dtype dtype, float scale, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/* Static text for a status code. */
+const char *gdn_status_str(gdn_status s);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char *gdn_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

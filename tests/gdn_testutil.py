@@ -30,3 +30,47 @@ def read_golden_rows(name):
             if line:
                 rows.append(line.split())
     return rows
+
+
+# ---------------------------------------------------------------- device transfer
+def to_device(inp, device="cuda"):
+    """Upload a workloads.Inputs batch; bf16 bits are reinterpreted, never re-rounded."""
+    import torch
+
+    def tok(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+    d = dict(q=tok(inp.q), k=tok(inp.k), v=tok(inp.v),
+             g=torch.from_numpy(inp.g).to(device), beta=torch.from_numpy(inp.beta).to(device),
+             cu=torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(device))
+    d["S0"] = None if inp.S0 is None else torch.from_numpy(inp.S0).to(device)
+    return d
+
+
+def to_f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+# ---------------------------------------------------------------- parity gate
+def tolerances(dtype):
+    """(output max-abs factor on |v|, state relative Frobenius bound)."""
+    return (2e-3, 1e-3) if dtype == "bf16" else (1e-5, 1e-5)
+
+
+def assert_parity(o, S, o_ref, S_ref, v_ref, dtype, what=""):
+    """bf16 inputs: max|o - o_ref| <= 2e-3 |v| and |S - S_ref|_F / |S_ref|_F <= 1e-3;
+    fp32 inputs: both bounds 1e-5.  |v| is the RMS per-vector norm of v."""
+    import oracle
+
+    fo, fs = tolerances(dtype)
+    vn = oracle.v_norm(v_ref)
+    if o_ref.size:
+        err_o = float(np.abs(o - o_ref).max())
+        assert np.isfinite(o).all(), f"{what}: non-finite output"
+        assert err_o <= fo * vn, f"{what}: output max-abs error {err_o:.3e} > {fo * vn:.3e}"
+    if S_ref is not None and S_ref.size:
+        den = float(np.linalg.norm(S_ref))
+        err_s = float(np.linalg.norm(S - S_ref)) / max(den, 1e-30)
+        assert err_s <= fs, f"{what}: state relative Frobenius error {err_s:.3e} > {fs:.1e}"

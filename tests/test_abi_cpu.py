@@ -1,0 +1,161 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared entry
+point, and rejects every malformed argument before touching the device.
+
+Validation runs before any HIP call, so these run on a machine without a GPU.
+The pointers passed are host addresses of poisoned buffers: the library must
+return the error and leave them untouched.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "gated_deltanet_recurrence_rule_amd", "libgdn.so")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_SEQ, E_WS, E_HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libgdn.so is not built (run __graft_entry__.build())")
+    from gated_deltanet_recurrence_rule_amd import binding
+    return binding.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) >= {"gdn_decode_step", "gdn_prefill", "gdn_prefill_workspace_size",
+                          "gdn_status_str", "gdn_last_error", "gdn_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_SEQ, E_WS, E_HIP):
+        assert lib.gdn_status_str(s)
+    assert lib.gdn_version() >= 100
+
+
+class Bufs:
+    """Poisoned host buffers standing in for device tensors (never dereferenced)."""
+
+    def __init__(self, T=8, N=2, HQK=2, HV=4, dk=32, dv=32):
+        self.T, self.N, self.HQK, self.HV, self.dk, self.dv = T, N, HQK, HV, dk, dv
+        self.q = np.full(T * HQK * dk + 16, 7.0, np.float32)
+        self.k = np.full_like(self.q, 7.0)
+        self.v = np.full(T * HV * dv + 16, 7.0, np.float32)
+        self.g = np.full(T * HV + 16, 7.0, np.float32)
+        self.b = np.full_like(self.g, 7.0)
+        self.o = np.full_like(self.v, 7.0)
+        self.S = np.full(N * HV * dk * dv + 16, 7.0, np.float32)
+        self.ST = np.full_like(self.S, 7.0)
+        cu = np.linspace(0, T, N + 1).astype(np.int32)
+        self.cu = cu
+
+    def p(self, a, off=0):
+        return ctypes.c_void_p(a.ctypes.data + off)
+
+    def untouched(self):
+        return all(np.all(x == 7.0) for x in (self.q, self.k, self.v, self.g, self.b, self.o,
+                                               self.S, self.ST))
+
+
+def _prefill(lib, B, **kw):
+    a = dict(q=B.p(B.q), k=B.p(B.k), v=B.p(B.v), g=B.p(B.g), b=B.p(B.b), cu=B.p(B.cu),
+             cu_host=B.p(B.cu), N=B.N, T=B.T, S0=B.p(B.S), o=B.p(B.o), ST=B.p(B.ST), HQK=B.HQK,
+             HV=B.HV, dk=B.dk, dv=B.dv, dtype=1, scale=1.0, ws=None, ws_bytes=0)
+    a.update(kw)
+    return lib.gdn_prefill(a["q"], a["k"], a["v"], a["g"], a["b"], a["cu"], a["cu_host"], a["N"],
+                           a["T"], a["S0"], a["o"], a["ST"], a["HQK"], a["HV"], a["dk"], a["dv"],
+                           a["dtype"], a["scale"], a["ws"], a["ws_bytes"], None)
+
+
+def _decode(lib, B, **kw):
+    a = dict(q=B.p(B.q), k=B.p(B.k), v=B.p(B.v), g=B.p(B.g), b=B.p(B.b), S=B.p(B.S), o=B.p(B.o),
+             N=B.N, HQK=B.HQK, HV=B.HV, dk=B.dk, dv=B.dv, dtype=1, scale=1.0)
+    a.update(kw)
+    return lib.gdn_decode_step(a["q"], a["k"], a["v"], a["g"], a["b"], a["S"], a["o"], a["N"],
+                               a["HQK"], a["HV"], a["dk"], a["dv"], a["dtype"], a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), E_NULL), (dict(k=None), E_NULL), (dict(v=None), E_NULL), (dict(g=None), E_NULL),
+    (dict(b=None), E_NULL), (dict(o=None), E_NULL), (dict(S=None), E_NULL),
+    (dict(N=-1), E_SHAPE), (dict(HQK=0), E_SHAPE), (dict(HQK=3), E_SHAPE), (dict(HV=-4), E_SHAPE),
+    (dict(dk=48), E_UNSUP), (dict(dv=256), E_UNSUP), (dict(dk=16), E_UNSUP),
+    (dict(dtype=7), E_DTYPE),
+])
+def test_decode_rejects(lib, kw, status):
+    B = Bufs()
+    assert _decode(lib, B, **kw) == status
+    assert lib.gdn_last_error()
+    assert B.untouched()
+
+
+def test_decode_rejects_misaligned(lib):
+    B = Bufs()
+    for name in ("q", "k", "v", "o", "S"):
+        assert _decode(lib, B, **{name: B.p(getattr(B, name), 4)}) == E_ALIGN
+    assert _decode(lib, B, g=B.p(B.g, 2)) == E_ALIGN
+    assert B.untouched()
+
+
+def test_decode_zero_sequences_is_a_noop(lib):
+    B = Bufs()
+    assert _decode(lib, B, N=0, q=None, k=None, v=None, g=None, b=None, o=None, S=None) == OK
+    assert B.untouched()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), E_NULL), (dict(o=None), E_NULL), (dict(g=None), E_NULL),
+    (dict(T=-1), E_SHAPE), (dict(N=-2), E_SHAPE), (dict(HQK=3), E_SHAPE),
+    (dict(dk=100), E_UNSUP), (dict(dtype=-1), E_DTYPE),
+    (dict(T=9), E_SEQ),                                     # cu[N] != total_T
+    (dict(cu=None, cu_host=None, N=3), E_SEQ),              # N does not divide total_T
+])
+def test_prefill_rejects(lib, kw, status):
+    B = Bufs()
+    assert _prefill(lib, B, **kw) == status
+    assert B.untouched()
+
+
+def test_prefill_rejects_bad_host_seqlens(lib):
+    B = Bufs(T=8, N=3)
+    for cu in ([1, 4, 6, 8], [0, 5, 4, 8], [0, 2, 4, 7]):
+        arr = np.array(cu, np.int32)
+        assert _prefill(lib, B, cu_host=B.p(arr)) == E_SEQ
+    assert B.untouched()
+
+
+def test_prefill_rejects_misaligned(lib):
+    B = Bufs()
+    for name, buf in (("q", B.q), ("v", B.v), ("o", B.o), ("S0", B.S), ("ST", B.ST)):
+        assert _prefill(lib, B, **{name: B.p(buf, 4)}) == E_ALIGN, name
+    assert _prefill(lib, B, cu=B.p(B.cu, 2)) == E_ALIGN
+    assert B.untouched()
+
+
+def test_prefill_workspace_contract(lib):
+    B = Bufs()
+    need = lib.gdn_prefill_workspace_size(B.N, B.T, B.HQK, B.HV, B.dk, B.dv, 0)
+    if need > 0:
+        assert _prefill(lib, B, dtype=0, ws=None, ws_bytes=need - 1) == E_WS
+    assert B.untouched()
+
+
+def test_prefill_zero_sequences_is_a_noop(lib):
+    B = Bufs()
+    z = np.zeros(1, np.int32)
+    assert _prefill(lib, B, N=0, T=0, cu=B.p(z), cu_host=B.p(z), q=None, k=None, v=None,
+                    g=None, b=None, o=None, S0=None, ST=None) == OK
+    assert B.untouched()
