@@ -130,8 +130,7 @@ def main():
     e = 2  # bf16 bytes
     pb, pf_chunk, pf_rec = prefill_alg(N, T, pf.HQK, pf.HV, pf.dk, pf.dv, e, True)
     db, dflops, dstate = decode_alg(dc.N, dc.HQK, dc.HV, dc.dk, dc.dv, e)
-    kname = lib.gdn_prefill_kernel_name(pf.N, pf.total_T, pf.HQK, pf.HV, pf.dk, pf.dv, 0).decode() \
-        if hasattr(lib, "gdn_prefill_kernel_name") else "prefill_recurrent"
+    kname = binding.prefill_kernel_name(pf.N, pf.total_T, pf.HQK, pf.HV, pf.dk, pf.dv, torch.bfloat16)
     if "chunk" in kname:
         pre_roof = {"bound": "mfma", "achieved": pf_chunk / (pre_avg * 1e-3) / 1e12,
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}

@@ -52,6 +52,8 @@ def load() -> ctypes.CDLL:
     lib.gdn_status_str.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
     lib.gdn_last_error.restype = ctypes.c_char_p
+    lib.gdn_prefill_kernel_name.argtypes = [i32, i64, i32, i32, i32, i32, ctypes.c_int]
+    lib.gdn_prefill_kernel_name.restype = ctypes.c_char_p
     lib.gdn_version.argtypes = []
     lib.gdn_version.restype = ctypes.c_int32
     _lib = lib
@@ -171,6 +173,12 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                            host_ptr, n_seq, total_T, _ptr(S0), _ptr(o), _ptr(S_T), HQK, HV, dk, dv,
                            code, float(scale), _ptr(workspace), ws_bytes, _stream(q.device)))
     return o, S_T
+
+
+def prefill_kernel_name(N: int, total_T: int, HQK: int, HV: int, dk: int, dv: int,
+                        dtype: torch.dtype) -> str:
+    code = GDN_BF16 if dtype == torch.bfloat16 else GDN_F32
+    return load().gdn_prefill_kernel_name(N, total_T, HQK, HV, dk, dv, code).decode()
 
 
 def version() -> int:

@@ -138,7 +138,17 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
 
     gdn::PrefillArgs a{q, k, v, g, beta, cu_seqlens, eq_len, N, total_T, S0, o, S_T,
                        HQK, HV, dk, dv, scale, workspace, workspace_bytes};
-    return hip_status(gdn::launch_prefill_recurrent(a, dtype == GDN_BF16, stream), "prefill launch");
+    const bool bf16 = dtype == GDN_BF16;
+    if (gdn::prefill_chunked_supported(dk, dv, bf16))
+        return hip_status(gdn::launch_prefill_chunked(a, stream), "chunked prefill launch");
+    return hip_status(gdn::launch_prefill_recurrent(a, bf16, stream), "prefill launch");
+}
+
+const char *gdn_prefill_kernel_name(int32_t N, int64_t total_T, int32_t HQK, int32_t HV, int32_t dk,
+                                    int32_t dv, gdn_dtype dtype) {
+    (void)N; (void)total_T; (void)HQK; (void)HV;
+    if (gdn::prefill_chunked_supported(dk, dv, dtype == GDN_BF16)) return "prefill_chunked";
+    return "prefill_recurrent";
 }
 
 }  // extern "C"

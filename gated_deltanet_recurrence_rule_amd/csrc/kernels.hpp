@@ -36,4 +36,8 @@ struct PrefillArgs {
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t stream);
 hipError_t launch_prefill_recurrent(const PrefillArgs &a, bool bf16, hipStream_t stream);
 
+// Chunked MFMA prefill: bf16 I/O, dk = 128, dv a multiple of 64.
+bool prefill_chunked_supported(int dk, int dv, bool bf16);
+hipError_t launch_prefill_chunked(const PrefillArgs &a, hipStream_t stream);
+
 }  // namespace gdn

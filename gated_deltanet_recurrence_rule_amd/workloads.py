@@ -95,6 +95,13 @@ class Inputs:
     def total_T(self) -> int:
         return int(self.cu_seqlens[-1])
 
+    def as_f64_rows(self, name: str, t0: int, t1: int) -> np.ndarray:
+        """Exact values of tokens [t0, t1) of q, k or v, widened to float64."""
+        a = getattr(self, name)[t0:t1]
+        if a.dtype == np.uint16:
+            a = bf16_bits_to_f32(a)
+        return a.astype(np.float64)
+
     def as_f64(self, name: str) -> np.ndarray:
         """The exact values of one input tensor, widened to float64."""
         a = getattr(self, name)

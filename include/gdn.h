@@ -127,6 +127,16 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
                        int32_t dv, gdn_dtype dtype, float scale, void *workspace,
                        size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * gdn_prefill_kernel_name -- which kernel gdn_prefill runs for these sizes
+ * (static text, for profiling and reports):
+ *   "prefill_chunked"    bf16, dk = 128, dv a multiple of 64: chunks of 64 tokens
+ *                        on bf16 MFMA with an fp32 table;
+ *   "prefill_recurrent"  every other case: token-serial, fp32 arithmetic.
+ */
+const char *gdn_prefill_kernel_name(int32_t N, int64_t total_T, int32_t HQK, int32_t HV,
+                                    int32_t dk, int32_t dv, gdn_dtype dtype);
+
 /* Static text for a status code. */
 const char *gdn_status_str(gdn_status s);
 

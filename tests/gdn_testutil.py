@@ -74,3 +74,30 @@ def assert_parity(o, S, o_ref, S_ref, v_ref, dtype, what=""):
         den = float(np.linalg.norm(S_ref))
         err_s = float(np.linalg.norm(S - S_ref)) / max(den, 1e-30)
         assert err_s <= fs, f"{what}: state relative Frobenius error {err_s:.3e} > {fs:.1e}"
+
+
+def oracle_units(inp, seqs, heads):
+    """Oracle on a subset of (sequence, V head) units of a batch.
+
+    Each selected V head gets its own copy of its QK head, so the subset runs as
+    an ungrouped batch.  Returns {(seq, head): (o [len, dv], S_T [dk, dv])}.
+    """
+    import oracle
+
+    rep = inp.HV // inp.HQK
+    heads = list(heads)
+    qk_idx = [h // rep for h in heads]
+    out = {}
+    S0 = inp.S0
+    for n in seqs:
+        t0, t1 = int(inp.cu_seqlens[n]), int(inp.cu_seqlens[n + 1])
+        q = inp.as_f64_rows("q", t0, t1)[:, qk_idx]
+        k = inp.as_f64_rows("k", t0, t1)[:, qk_idx]
+        v = inp.as_f64_rows("v", t0, t1)[:, heads]
+        g = inp.g[t0:t1][:, heads].astype(np.float64)
+        b = inp.beta[t0:t1][:, heads].astype(np.float64)
+        s0 = None if S0 is None else S0[n][heads].astype(np.float64)[None]
+        o, S = oracle.run(q, k, v, g, b, [0, t1 - t0], s0, scale=inp.scale)
+        for i, h in enumerate(heads):
+            out[(n, h)] = (o[:, i], S[0, i])
+    return out

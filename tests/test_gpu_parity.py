@@ -183,4 +183,4 @@ def test_prefill_rejects_bad_args_on_device():
     d = to_device(inp)
     with pytest.raises(binding.GdnError):
         binding.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu"],
-                        cu_seqlens_host=[0, 9, 16])
+                        cu_seqlens_host=[0, 9, 15])
