@@ -55,9 +55,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=8192,
-                    help="tokens of sequence 0 (all V heads) the CPU oracle runs on")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=2,
+                    help="prefill sequences (all V heads) the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after timing, run one 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -108,24 +110,32 @@ def main():
         decode()
     torch.cuda.synchronize()
 
+    # Timed region: K prefill calls back to back, then K decode steps back to back,
+    # bracketed by HIP events on the stream the library launches on.
     stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for e0, e1, e2 in ev:
-        e0.record(stream)
+    e0.record(stream)
+    for _ in range(args.steps):
         prefill()
-        e1.record(stream)
+    e1.record(stream)
+    for _ in range(args.steps):
         decode()
-        e2.record(stream)
+    e2.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    pre_ms = [a.elapsed_time(b) for a, b, _ in ev]
-    dec_ms = [b.elapsed_time(c) for _, b, c in ev]
-    step_ms = [a.elapsed_time(c) for a, _, c in ev]
-    pre_avg = float(np.mean(pre_ms))
-    dec_avg = float(np.mean(dec_ms))
+    pre_avg = e0.elapsed_time(e1) / args.steps
+    dec_avg = e1.elapsed_time(e2) / args.steps
+    step_ms = e0.elapsed_time(e2) / args.steps
+
+    if args.copy_probe:
+        # a plain device copy of known size, for scaling HBM counters (FETCH_SIZE/WRITE_SIZE)
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     e = 2  # bf16 bytes
     pb, pf_chunk, pf_rec = prefill_alg(N, T, pf.HQK, pf.HV, pf.dk, pf.dv, e, True)
@@ -151,20 +161,22 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
 
-        ts = min(args.cpu_sample_tokens, T)
-        sl = slice(0, ts)
-        f64 = {x: pf.as_f64(x)[sl] for x in ("q", "k", "v", "g", "beta")}
-        s0 = pf.as_f64("S0")[:1]
+        ns = max(1, min(args.cpu_sample_seqs, N))
+        ts = ns * T
+        f64 = {x: pf.as_f64_rows(x, 0, ts) for x in ("q", "k", "v")}
+        f64.update({x: getattr(pf, x)[:ts].astype(np.float64) for x in ("g", "beta")})
+        s0 = pf.S0[:ns].astype(np.float64)
         t0 = time.perf_counter()
-        oracle.run(f64["q"], f64["k"], f64["v"], f64["g"], f64["beta"], [0, ts], s0)
+        oracle.run(f64["q"], f64["k"], f64["v"], f64["g"], f64["beta"], pf.cu_seqlens[:ns + 1], s0)
         tc = time.perf_counter() - t0
         d64 = {x: dc.as_f64(x) for x in ("q", "k", "v", "g", "beta", "S0")}
         t1 = time.perf_counter()
         oracle.run(d64["q"], d64["k"], d64["v"], d64["g"], d64["beta"], dc.cu_seqlens, d64["S0"])
         td = time.perf_counter() - t1
         cpu = {"value": ts / tc / 1e6, "unit": "Mtok/s", "cores": oracle.threads(), "kind": "oracle",
-               "sample": f"float64 token loop on sequence 0 of the prefill batch, first {ts} tokens, "
-                         f"all {pf.HV} V heads ({tc:.2f} s); decode leg: full 256-sequence step "
+               "sample": f"float64 token loop on the first {ns} of the {N} prefill sequences "
+                         f"({ts} tokens, all {pf.HV} V heads, {tc:.2f} s); decode leg: the full "
+                         f"256-sequence step "
                          f"({td:.2f} s)",
                "decode_state_GBps": dstate / td / 1e9}
         log(f"cpu oracle: {ts} tokens in {tc:.2f} s, decode step in {td:.2f} s")
@@ -172,7 +184,7 @@ def main():
     out = {
         "metric": "prefill Mtok/s + decode state GB/s on 1 GPU, as % of MFMA/HBM roofline",
         "value": value, "unit": "Mtok/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": float(np.mean(step_ms)),
+        "warmup": args.warmup, "ms_per_step": step_ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "Qwen3-Next-shaped prefill (4 x 16384 tokens, 16 QK / 32 V heads, "

@@ -9,28 +9,40 @@
 // gamma_i = exp(G_i), r_k, r_q the per-token norm reciprocals (r_q includes
 // `scale`), and raw bf16 rows K, Q, V:
 //
-//   A_ij = b_i r_k,i r_k,j (K K^T)_ij exp(G_i - G_j)   j < i   (zero otherwise)
-//   P_ij = r_q,i r_k,j (Q K^T)_ij exp(G_i - G_j)       j <= i
-//   T    = (I + A)^{-1}                                 (unit lower triangular)
-//   Z_i  = b_i (v_i - gamma_i r_k,i (K S)_i)
-//   Delta = T Z
-//   O_i  = gamma_i r_q,i (Q S)_i + (P Delta)_i
-//   S'   = gamma_n S + K^T diag(r_k,i exp(G_n - G_i)) Delta
+//   A_ij  = b_i r_k,i r_k,j (K K^T)_ij exp(G_i - G_j)   j < i   (zero otherwise)
+//   P_ij  = r_q,i r_k,j (Q K^T)_ij exp(G_i - G_j)       j <= i
+//   Z_i   = b_i (v_i - gamma_i r_k,i (K S)_i)
+//   (I + A) Delta = Z                                   (unit lower triangular)
+//   O_i   = gamma_i r_q,i (Q S)_i + (P Delta)_i
+//   S'    = gamma_n S + K^T diag(r_k,i exp(G_n - G_i)) Delta
 //
 // Only exp(G_i - G_j) <= 1 and exp(G_n - G_i) <= 1 are formed, never 1/gamma.
+// The triangular system is split into two 32-token blocks:
+//   Delta_0 = T_0 Z_0,   Delta_1 = T_1 (Z_1 - A_10 Delta_0),   T_b = (I + A_bb)^{-1},
+// with T_b built in fp32 from 16x16 forward substitutions and one 16-block merge.
 //
-// Precision.  MFMA operands are bf16; a value that is not exactly bf16 is
-// either rounded once or carried as hi + lo (hi = bf16(x), lo = bf16(x - hi),
-// two or three MFMAs).  The raw q, k, v rows are exact bf16.  The table path is
-// carried hi + lo: S in K S, T and Z in T Z, and the scaled Delta in K^T D.
-// The output path rounds once: S in Q S, P and Delta in P Delta.  All
-// accumulation is fp32; T is built in fp32.
+// Precision.  MFMA operands are bf16; a value that is not exactly bf16 is either
+// rounded once or carried as hi + lo (hi = bf16(x), lo = bf16(x - hi); two or
+// three MFMAs).  Raw q, k, v rows are exact bf16.  The table path is carried
+// hi + lo: S in K S, T_b, A_10 and Z / Delta in the solve, the scaled Delta in
+// K^T D.  The output path rounds once: S in Q S, P and Delta in P Delta.  All
+// accumulation is fp32.
 //
-// Mapping.  One workgroup of 4 waves owns one (sequence, V head, 64-column
-// slice of dv) and walks its chunks in order, keeping its 128 x 64 slice of S
-// in MFMA accumulators (wave w holds table rows 32w..32w+31).  dv columns of S
-// evolve independently, so slices need no communication; each slice recomputes
-// its chunk's Gram matrices and T.  Everything else of a chunk lives in LDS.
+// Mapping.  One workgroup of 8 waves owns one (sequence, V head, 64-column
+// slice of dv) and walks its chunks in order; dv columns of S evolve
+// independently, so slices need no communication.
+//  * Waves 0-3 ("column waves") each own one 16-column tile of the slice and
+//    keep everything of it in MFMA accumulators: the 128 x 16 table slice, and
+//    per chunk K S, Q S, Z, Delta, D, O.  A K=32 MFMA whose B operand is two
+//    stacked 16-row accumulator tiles takes them as they are, provided the A
+//    operand enumerates its 32 k-values in the same order (tile t, row 4*(lane/16)+e);
+//    all such products here use that order.
+//  * Waves 4-7 ("Gram waves") compute the chunk's Gram tiles and write P, -A_10
+//    and T_0, T_1 into LDS already in that MFMA operand order (computing a Gram
+//    tile with the two operand roles swapped yields it transposed, which is the
+//    operand order directly).
+// Three workgroup barriers per chunk: load | Grams + (K S, Q S, Z) | solve + state.
+// The next chunk's q, k, v, g, beta are fetched into registers one chunk ahead.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -39,110 +51,105 @@ namespace gdn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int C = 64;       // chunk length
 constexpr int DK = 128;     // key dimension
 constexpr int DVS = 64;     // dv columns per workgroup
-constexpr int NT = 256;     // threads (4 waves)
+constexpr int NT = 512;     // threads (8 waves)
 
-// LDS row strides (elements), padded so 16 lanes reading 16 rows hit distinct banks.
-constexpr int LK = DK + 8;  // rows of K, Q, S^T (bf16)
-constexpr int LC = C + 8;   // rows of K^T, P, T, Z^T, D^T, Delta^T, V (bf16)
-constexpr int LF = C + 4;   // rows of A and T in fp32
+constexpr int LK = DK + 8;  // row stride (bf16) of K and Q in LDS
+constexpr int LT = C + 8;   // row stride (bf16) of K^T in LDS
+constexpr int LW = 33;      // row stride (fp32) of the Gram waves' private 32x32 blocks
 
-// LDS regions (bytes).  Regions are reused by phases that do not overlap in time.
-constexpr int R1 = 0;                              // K [C][LK] | merge scratch | Delta^T [DVS][LC]
-constexpr int R1_SZ = C * LK * 2;
-constexpr int R2 = R1 + R1_SZ;                     // Q [C][LK] | T fp32 [C][LF] | D^T hi,lo [DVS][LC]
-constexpr int R2_SZ = 2 * DVS * LC * 2;
-constexpr int R3 = R2 + R2_SZ;                     // K^T [DK][LC]
-constexpr int R3_SZ = DK * LC * 2;
-constexpr int R4 = R3 + R3_SZ;                     // S^T hi, lo [DVS][LK]
-constexpr int R4_SZ = 2 * DVS * LK * 2;
-constexpr int R5 = R4 + R4_SZ;                     // P [C][LC]
-constexpr int R5_SZ = C * LC * 2;
-constexpr int R6 = R5 + R5_SZ;                     // T hi, lo [C][LC]
-constexpr int R6_SZ = 2 * C * LC * 2;
-constexpr int R7 = R6 + R6_SZ;                     // A fp32 [C][LF] | Z^T hi, lo [DVS][LC]
-constexpr int R7_SZ = 2 * DVS * LC * 2;
-constexpr int R8 = R7 + R7_SZ;                     // V [C][LC] (DVS columns)
-constexpr int R8_SZ = C * LC * 2;
-constexpr int R9 = R8 + R8_SZ;                     // per-token scalars, 6 x C floats
-constexpr int R9_SZ = 6 * C * 4;
-constexpr int LDS_BYTES = R9 + R9_SZ;
-
-static_assert(C * LK * 2 >= 32 * 36 * 4, "merge scratch fits in R1");
-static_assert(R2_SZ >= C * LK * 2 && R2_SZ >= C * LF * 4, "R2 holds Q and fp32 T");
-static_assert(R7_SZ >= C * LF * 4, "R7 holds fp32 A");
-static_assert(R1_SZ >= DVS * LC * 2, "R1 holds Delta^T");
+// LDS layout (bytes)
+constexpr int OFF_K = 0;                                   // K  [C][LK] bf16, rows = tokens
+constexpr int OFF_Q = OFF_K + C * LK * 2;                  // Q  [C][LK]
+constexpr int OFF_KT = OFF_Q + C * LK * 2;                 // K^T [DK][LT], token index swizzled
+constexpr int OFF_OPT = OFF_KT + DK * LT * 2;              // T_b operands [2 b][2 rt][2 hi/lo][64][8]
+constexpr int OFF_OPA = OFF_OPT + 2 * 2 * 2 * 64 * 16;     // -A_10 operands [2 rt][2 hi/lo][64][8]
+constexpr int OFF_OPP = OFF_OPA + 2 * 2 * 64 * 16;         // P operands [6 (rt, ks)][64][8]
+constexpr int OFF_WP = OFF_OPP + 6 * 64 * 16;              // per Gram wave 4,5: Af, Tf [32][LW], Rf [16][17]
+constexpr int WP_SZ = (2 * 32 * LW + 16 * 17) * 4;
+constexpr int OFF_SC = OFF_WP + 2 * WP_SZ;                 // 6 x C fp32 scalars
+constexpr int LDS_BYTES = OFF_SC + 6 * C * 4;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
-__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ bf16x8 to_bf16(f32x8 x) { return __builtin_convertvector(x, bf16x8); }
+__device__ __forceinline__ f32x8 to_f32(bf16x8 x) { return __builtin_convertvector(x, f32x8); }
+__device__ __forceinline__ f32x8 cat(f32x4 a, f32x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ void split(f32x8 x, bf16x8 &hi, bf16x8 &lo) {
+    hi = to_bf16(x);
+    lo = to_bf16(x - to_f32(hi));
+}
+// hi*hi + hi*lo + lo*hi
+__device__ __forceinline__ f32x4 mfma32_x3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, f32x4 c) {
+    c = mfma32(ah, bh, c);
+    c = mfma32(ah, bl, c);
+    return mfma32(al, bh, c);
+}
 
-// MFMA 16x16x32 operand: lane l reads row r0 + l%16, elements k0 + 8(l/16) .. +7 of a
-// bf16 matrix stored with k contiguous (A row-major, or B stored as B^T row-major).
-__device__ __forceinline__ bf16x8 ld_op(const uint16_t *base, int stride, int r0, int k0, int lane) {
+// Standard-order operand: row r0 + lane%16, k = k0 + 8*(lane/16) .. +7 of a bf16 row-major matrix.
+__device__ __forceinline__ bf16x8 ld_std(const __bf16 *base, int stride, int r0, int k0, int lane) {
     return *reinterpret_cast<const bf16x8 *>(base + (r0 + (lane & 15)) * stride + k0 + 8 * (lane >> 4));
 }
-
-__device__ __forceinline__ void split_bf16(float x, uint16_t &hi, uint16_t &lo) {
-    hi = f32_to_bf16(x);
-    lo = f32_to_bf16(x - bf16_to_f32(hi));
+// Tile-order operand: row r0 + lane%16, k = k0 + 4*(lane/16) .. +3 then k0 + 16 + 4*(lane/16) .. +3.
+__device__ __forceinline__ bf16x8 ld_tile(const __bf16 *base, int stride, int r0, int k0, int lane) {
+    const __bf16 *p = base + (r0 + (lane & 15)) * stride + k0 + 4 * (lane >> 4);
+    return cat(*reinterpret_cast<const bf16x4 *>(p), *reinterpret_cast<const bf16x4 *>(p + 16));
 }
 
-// 16x16 fp32 product X * Y (+acc) with X, Y row-major fp32 blocks in LDS.
-__device__ __forceinline__ f32x4 mm16_f32(const float *X, int ldx, const float *Y, int ldy, f32x4 acc,
-                                          int lane) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const float a = X[(lane & 15) * ldx + 4 * k + (lane >> 4)];
-        const float b = Y[(4 * k + (lane >> 4)) * ldy + (lane & 15)];
-        acc = mfma_f32(a, b, acc);
-    }
-    return acc;
+// K^T token swizzle: 8-token groups are permuted per 8-row band of K^T so that the
+// 16 lanes writing one token row hit 16 different banks.  Groups of 4 stay contiguous.
+__device__ __forceinline__ int kt_col(int d, int tok) { return tok ^ (8 * ((d >> 3) & 7)); }
+
+// A copy of x the compiler cannot see through: lane-dependent addresses derived from
+// it are recomputed inside the chunk loop instead of being hoisted out and spilled.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
 }
 
-// Store a 16x16 fp32 accumulator tile (scaled) to a row-major fp32 block.
-__device__ __forceinline__ void st_tile_f32(float *Y, int ldy, f32x4 acc, float s, int lane) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Y[(4 * (lane >> 4) + e) * ldy + (lane & 15)] = s * acc[e];
+// Keeps the scheduler from hoisting loads of later iterations (bounds live registers).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Orders LDS writes before later LDS reads of the same wave (no workgroup barrier).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <typename T>
 __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
     const int32_t *__restrict__ cu_seqlens, int64_t eq_len, const float *__restrict__ S0,
     uint16_t *__restrict__ o, float *__restrict__ S_T, int HV, int DV, int rep, float scale) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
-    uint16_t *sK = reinterpret_cast<uint16_t *>(lds + R1);
-    float *sScr = reinterpret_cast<float *>(lds + R1);
-    uint16_t *sDelt = reinterpret_cast<uint16_t *>(lds + R1);
-    uint16_t *sQ = reinterpret_cast<uint16_t *>(lds + R2);
-    float *sTf = reinterpret_cast<float *>(lds + R2);
-    uint16_t *sDt_hi = reinterpret_cast<uint16_t *>(lds + R2);
-    uint16_t *sDt_lo = sDt_hi + DVS * LC;
-    uint16_t *sKt = reinterpret_cast<uint16_t *>(lds + R3);
-    uint16_t *sSt_hi = reinterpret_cast<uint16_t *>(lds + R4);
-    uint16_t *sSt_lo = sSt_hi + DVS * LK;
-    uint16_t *sP = reinterpret_cast<uint16_t *>(lds + R5);
-    uint16_t *sT_hi = reinterpret_cast<uint16_t *>(lds + R6);
-    uint16_t *sT_lo = sT_hi + C * LC;
-    float *sA = reinterpret_cast<float *>(lds + R7);
-    uint16_t *sZt_hi = reinterpret_cast<uint16_t *>(lds + R7);
-    uint16_t *sZt_lo = sZt_hi + DVS * LC;
-    uint16_t *sV = reinterpret_cast<uint16_t *>(lds + R8);
-    float *sG = reinterpret_cast<float *>(lds + R9);  // cumulative log-decay
-    float *sGam = sG + C;                             // exp(G_i)
-    float *sRk = sGam + C;                            // 1 / |k_i|
-    float *sRq = sRk + C;                             // scale / |q_i|
-    float *sB = sRq + C;                              // beta_i
-    float *sDn = sB + C;                              // r_k,i exp(G_n - G_i)
+    __bf16 *sK = reinterpret_cast<__bf16 *>(lds + OFF_K);
+    __bf16 *sQ = reinterpret_cast<__bf16 *>(lds + OFF_Q);
+    __bf16 *sKt = reinterpret_cast<__bf16 *>(lds + OFF_KT);
+    bf16x8 *opT = reinterpret_cast<bf16x8 *>(lds + OFF_OPT);  // [((b*2 + rt)*2 + hl)*64 + lane]
+    bf16x8 *opA = reinterpret_cast<bf16x8 *>(lds + OFF_OPA);  // [(rt*2 + hl)*64 + lane]
+    bf16x8 *opP = reinterpret_cast<bf16x8 *>(lds + OFF_OPP);  // [idx*64 + lane]
+    float *sG = reinterpret_cast<float *>(lds + OFF_SC);      // cumulative log-decay
+    float *sGam = sG + C;                                     // exp(G_i)
+    float *sRk = sGam + C;                                    // 1 / |k_i|
+    float *sRq = sRk + C;                                     // scale / |q_i|
+    float *sB = sRq + C;                                      // beta_i
+    float *sDn = sB + C;                                      // r_k,i exp(G_n - G_i)
 
     const int unit = blockIdx.x;  // n * HV + h
     const int h = unit % HV;
@@ -153,8 +160,9 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
-    const int lr = lane & 15;   // accumulator column within a tile
-    const int lq = lane >> 4;   // accumulator row group within a tile
+    const int lr = lane & 15;
+    const int lq = lane >> 4;
+    const bool colwave = w < 4;
 
     int64_t t0, t1;
     if (cu_seqlens) {
@@ -165,324 +173,388 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         t1 = t0 + eq_len;
     }
 
-    // Table slice in accumulators: wave w owns rows 32w..32w+31 as two 16-row tiles
-    // (dt = 0, 1) times four 16-column tiles (ct).  Element e of tile (dt, ct) is
-    // S[32w + 16dt + 4lq + e][col0 + 16ct + lr].
-    f32x4 S[2][4];
-    const size_t tab = (size_t)unit * DK * DV;
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int d = 32 * w + 16 * dt + 4 * lq + e;
-                S[dt][ct][e] = S0 ? S0[tab + (size_t)d * DV + col0 + 16 * ct + lr] : 0.f;
-            }
+    const int nchunks = (int)((t1 - t0 + C - 1) / C);
+    auto chunk_len = [&](int c) { return (int)((t1 - t0 - (int64_t)c * C) < C ? (t1 - t0 - (int64_t)c * C) : C); };
 
-    auto write_St = [&]() {
+    if (colwave) {
+        // ====================== column waves: the table and the per-chunk chain ======
+        // Element e of S[dt] is S[16 dt + 4 lq + e][col0 + 16 w + lr].
+        f32x4 S[8];
+        const size_t tab = (size_t)unit * DK * DV;
+        const int mycol = col0 + 16 * w + lr;
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
+        for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-                uint16_t hi[4], lo[4];
+            for (int e = 0; e < 4; ++e)
+                S[dt][e] = S0 ? S0[tab + (size_t)(16 * dt + 4 * lq + e) * DV + mycol] : 0.f;
+
+        // v[16 rt + 4 lq + e][mycol] of the next chunk, fetched one chunk ahead
+        uint16_t vreg[4][4];
+        auto prefetch_v = [&](int c) {
+            const int nn = chunk_len(c);
+            const int64_t cs = t0 + (int64_t)c * C;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) split_bf16(S[dt][ct][e], hi[e], lo[e]);
-                const int off = (16 * ct + lr) * LK + 32 * w + 16 * dt + 4 * lq;
-                *reinterpret_cast<uint2 *>(sSt_hi + off) =
-                    make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
-                *reinterpret_cast<uint2 *>(sSt_lo + off) =
-                    make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * rt + 4 * lq + e;
+                    vreg[rt][e] = (i < nn) ? v[((size_t)(cs + i) * HV + h) * DV + mycol] : (uint16_t)0;
+                }
+        };
+        if (nchunks > 0) prefetch_v(0);
+
+        for (int c = 0; c < nchunks; ++c) {
+            const int ln = opaque(lane);
+            const int lrr = ln & 15, lqq = ln >> 4;
+            const int64_t c0 = t0 + (int64_t)c * C;
+            const int n = chunk_len(c);
+            __syncthreads();  // (1) previous chunk done with LDS
+            float vcur[4][4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vcur[rt][e] = bf16_to_f32(vreg[rt][e]);
+            if (c + 1 < nchunks) prefetch_v(c + 1);
+            __syncthreads();  // (2) K, Q, K^T and the scalars are in LDS
+
+            // ---- Y = K S (hi + lo), Oacc = Q S (hi), Z = beta (v - gamma r_k Y)
+            f32x4 Z[4], Oacc[4];
+            {
+                bf16x8 Sh[4], Sl[4];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) split(cat(S[2 * ks], S[2 * ks + 1]), Sh[ks], Sl[ks]);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    f32x4 y = {0.f, 0.f, 0.f, 0.f}, oa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const bf16x8 kk = ld_tile(sK, LK, 16 * rt, 32 * ks, ln);
+                        const bf16x8 qq = ld_tile(sQ, LK, 16 * rt, 32 * ks, ln);
+                        y = mfma32(kk, Sh[ks], y);
+                        y = mfma32(kk, Sl[ks], y);
+                        oa = mfma32(qq, Sh[ks], oa);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 16 * rt + 4 * lqq + e;
+                        Z[rt][e] = sB[i] * (vcur[rt][e] - sGam[i] * sRk[i] * y[e]);
+                    }
+                    Oacc[rt] = oa;
+                    sched_fence();
+                }
             }
+            __syncthreads();  // (3) P, -A_10, T_0, T_1 and r_k exp(G_n - G) are in LDS
+
+            // ---- Delta_0 = T_0 Z_0;  Delta_1 = T_1 (Z_1 - A_10 Delta_0)
+            f32x4 Dl[4];
+            {
+                bf16x8 zh, zl;
+                split(cat(Z[0], Z[1]), zh, zl);
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                    Dl[rt] = mfma32_x3(opT[(rt * 2 + 0) * 64 + ln], opT[(rt * 2 + 1) * 64 + ln], zh, zl, zero);
+                }
+                bf16x8 dh, dl;
+                split(cat(Dl[0], Dl[1]), dh, dl);
+                f32x4 r1[2];
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+                    r1[rt] = mfma32_x3(opA[(rt * 2 + 0) * 64 + ln], opA[(rt * 2 + 1) * 64 + ln], dh, dl, Z[2 + rt]);
+                bf16x8 rh, rl;
+                split(cat(r1[0], r1[1]), rh, rl);
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                    Dl[2 + rt] = mfma32_x3(opT[((2 + rt) * 2 + 0) * 64 + ln], opT[((2 + rt) * 2 + 1) * 64 + ln],
+                                           rh, rl, zero);
+                }
+            }
+            // ---- O = gamma r_q (Q S) + P Delta
+            {
+                bf16x8 Dsg[2];
+                Dsg[0] = to_bf16(cat(Dl[0], Dl[1]));
+                Dsg[1] = to_bf16(cat(Dl[2], Dl[3]));
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    f32x4 pd = {0.f, 0.f, 0.f, 0.f};
+                    const int base = rt == 0 ? 0 : (rt == 1 ? 1 : (rt == 2 ? 2 : 4));
+#pragma unroll
+                    for (int ks = 0; ks <= (rt >> 1); ++ks) pd = mfma32(opP[(base + ks) * 64 + ln], Dsg[ks], pd);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 16 * rt + 4 * lqq + e;
+                        if (i < n) {
+                            const float ov = sGam[i] * sRq[i] * Oacc[rt][e] + pd[e];
+                            o[((size_t)(c0 + i) * HV + h) * DV + mycol] = __builtin_bit_cast(uint16_t, (__bf16)ov);
+                        }
+                    }
+                    sched_fence();
+                }
+            }
+            // ---- S <- gamma_n S + K^T D,  D = diag(r_k exp(G_n - G)) Delta
+            {
+                bf16x8 Dh[2], Dlo[2];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    f32x8 x = cat(Dl[2 * ks], Dl[2 * ks + 1]);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[4 * t + e] *= sDn[32 * ks + 16 * t + 4 * lqq + e];
+                    split(x, Dh[ks], Dlo[ks]);
+                }
+                const float gam_n = sGam[C - 1];
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) {
+                    f32x4 acc = S[dt] * gam_n;
+                    const int d = 16 * dt + lrr;
+                    const __bf16 *rowp = sKt + d * LT;
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        const int tk = 32 * ks + 4 * lqq;
+                        const bf16x8 kt = cat(*reinterpret_cast<const bf16x4 *>(rowp + kt_col(d, tk)),
+                                              *reinterpret_cast<const bf16x4 *>(rowp + kt_col(d, tk + 16)));
+                        acc = mfma32(kt, Dh[ks], acc);
+                        acc = mfma32(kt, Dlo[ks], acc);
+                    }
+                    S[dt] = acc;
+                    sched_fence();
+                }
+            }
+        }
+        if (S_T) {
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) S_T[tab + (size_t)(16 * dt + 4 * lq + e) * DV + mycol] = S[dt][e];
+        }
+        return;
+    }
+
+    // ====================== Gram waves: chunk loads, norms, decay, P, A, T ===========
+    const int gt = tid - 256;  // 0..255
+    const int gw = w - 4;      // 0..3
+    // q, k of the next chunk: rows r = gt/16 + 16 p (p = 0..3), 16-byte segment s = gt % 16
+    const int seg_s = gt & 15;
+    uint4 kreg[4], qreg[4];
+    float greg = 0.f, breg = 0.f;  // Gram wave 3 (w == 7): token = lane
+    auto prefetch_qk = [&](int c) {
+        const int nn = chunk_len(c);
+        const int64_t cs = t0 + (int64_t)c * C;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int r = (gt >> 4) + 16 * p;
+            kreg[p] = make_uint4(0, 0, 0, 0);
+            qreg[p] = make_uint4(0, 0, 0, 0);
+            if (r < nn) {
+                const size_t off = ((size_t)(cs + r) * HQK + hq) * DK + 8 * seg_s;
+                kreg[p] = *reinterpret_cast<const uint4 *>(k + off);
+                qreg[p] = *reinterpret_cast<const uint4 *>(q + off);
+            }
+        }
+        if (gw == 3) {
+            const bool ok = lane < nn;
+            greg = ok ? g[(size_t)(cs + lane) * HV + h] : 0.f;
+            breg = ok ? beta[(size_t)(cs + lane) * HV + h] : 0.f;
+        }
     };
-    write_St();
+    if (nchunks > 0) prefetch_qk(0);
 
-    for (int64_t c0 = t0; c0 < t1; c0 += C) {
-        const int n = (int)((t1 - c0) < C ? (t1 - c0) : C);
-        __syncthreads();  // the previous chunk is done with every LDS region
-
-        // ---- S1: load the chunk's K, Q (row-major and K^T), V slice, g, beta
+    for (int c = 0; c < nchunks; ++c) {
+        const int ln = opaque(lane);
+        const int lrr = ln & 15, lqq = ln >> 4;
+        const int gtt = opaque(gt);
+        const int sgs = gtt & 15;
+        __syncthreads();  // (1) previous chunk done with LDS
+        // ---- registers -> LDS (K, Q row-major, K^T swizzled), norms, cumulative decay
 #pragma unroll
-        for (int p = 0; p < (C * DK / 8) / NT; ++p) {
-            const int seg = tid + NT * p;
-            const int r = seg / (DK / 8), s = seg % (DK / 8);
-            uint4 kv = make_uint4(0, 0, 0, 0), qv = make_uint4(0, 0, 0, 0);
-            if (r < n) {
-                const size_t off = ((size_t)(c0 + r) * HQK + hq) * DK + 8 * s;
-                kv = *reinterpret_cast<const uint4 *>(k + off);
-                qv = *reinterpret_cast<const uint4 *>(q + off);
-            }
-            *reinterpret_cast<uint4 *>(sK + r * LK + 8 * s) = kv;
-            *reinterpret_cast<uint4 *>(sQ + r * LK + 8 * s) = qv;
-            const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                sKt[(8 * s + e) * LC + r] = (uint16_t)(kw[e >> 1] >> (16 * (e & 1)));
-        }
-#pragma unroll
-        for (int p = 0; p < (C * DVS / 8) / NT; ++p) {
-            const int seg = tid + NT * p;
-            const int r = seg / (DVS / 8), s = seg % (DVS / 8);
-            uint4 vv = make_uint4(0, 0, 0, 0);
-            if (r < n) vv = *reinterpret_cast<const uint4 *>(v + ((size_t)(c0 + r) * HV + h) * DV + col0 + 8 * s);
-            *reinterpret_cast<uint4 *>(sV + r * LC + 8 * s) = vv;
-        }
-        if (tid < C) {
-            const bool ok = tid < n;
-            sG[tid] = ok ? g[(size_t)(c0 + tid) * HV + h] : 0.f;
-            sB[tid] = ok ? beta[(size_t)(c0 + tid) * HV + h] : 0.f;
-        }
-        __syncthreads();
-
-        // ---- S2: cumulative log-decay (wave 0) and the norms of q and k (all)
-        if (w == 0) {
-            float x = sG[lane];
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off, 64);
-                if (lane >= off) x += y;
-            }
-            sG[lane] = x;
-            sGam[lane] = expf(x);
-        }
-        {
-            const int r = tid >> 2, part = tid & 3;
+        for (int p = 0; p < 4; ++p) {
+            const int r = (gtt >> 4) + 16 * p;
+            *reinterpret_cast<uint4 *>(sK + r * LK + 8 * sgs) = kreg[p];
+            *reinterpret_cast<uint4 *>(sQ + r * LK + 8 * sgs) = qreg[p];
+            const uint32_t kw[4] = {kreg[p].x, kreg[p].y, kreg[p].z, kreg[p].w};
+            const uint32_t qw[4] = {qreg[p].x, qreg[p].y, qreg[p].z, qreg[p].w};
             float sk = 0.f, sq = 0.f;
 #pragma unroll
-            for (int e = 0; e < DK / 4; ++e) {
-                const float kx = bf16_to_f32(sK[r * LK + part * (DK / 4) + e]);
-                const float qx = bf16_to_f32(sQ[r * LK + part * (DK / 4) + e]);
+            for (int e = 0; e < 8; ++e) {
+                const uint16_t kb = (uint16_t)(kw[e >> 1] >> (16 * (e & 1)));
+                const uint16_t qb = (uint16_t)(qw[e >> 1] >> (16 * (e & 1)));
+                const int d = 8 * sgs + e;
+                reinterpret_cast<uint16_t *>(sKt)[d * LT + kt_col(d, r)] = kb;
+                const float kx = bf16_to_f32(kb), qx = bf16_to_f32(qb);
                 sk += kx * kx;
                 sq += qx * qx;
             }
-            sk += __shfl_xor(sk, 1, 64);
-            sk += __shfl_xor(sk, 2, 64);
-            sq += __shfl_xor(sq, 1, 64);
-            sq += __shfl_xor(sq, 2, 64);
-            if (part == 0) {
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) {
+                sk += __shfl_xor(sk, off, 64);
+                sq += __shfl_xor(sq, off, 64);
+            }
+            if (sgs == 0) {
                 sRk[r] = inv_norm(sk);
                 sRq[r] = inv_norm(sq) * scale;
             }
+            sched_fence();
         }
-        __syncthreads();
+        if (gw == 3) {
+            float x = greg;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(x, off, 64);
+                if (ln >= off) x += y;
+            }
+            sG[ln] = x;
+            sGam[ln] = expf(x);
+            sB[ln] = breg;
+        }
+        if (c + 1 < nchunks) prefetch_qk(c + 1);
+        __syncthreads();  // (2)
 
-        // ---- S3: Gram tiles -> A (fp32), P (bf16); Y = K S (hi+lo); Oacc = Q S (hi)
-        // 20 lower-triangular tile jobs: j < 10 are K K^T tiles, j >= 10 are Q K^T tiles.
-        for (int job = w; job < 20; job += 4) {
-            const bool isA = job < 10;
-            int tt = isA ? job : job - 10;
-            int ti = 0;
-            while (tt > ti) { tt -= ti + 1; ++ti; }
-            const int tj = tt;  // ti >= tj
-            const uint16_t *X = isA ? sK : sQ;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (gw < 2) {
+            // ---- T_b = (I + A_bb)^{-1} for the 32-token block b = gw
+            const int b = gw;
+            float *Af = reinterpret_cast<float *>(lds + OFF_WP + b * WP_SZ);
+            float *Tf = Af + 32 * LW;
+            float *Rf = Tf + 32 * LW;
 #pragma unroll
-            for (int ks = 0; ks < DK / 32; ++ks)
-                acc = mfma_bf16(ld_op(X, LK, 16 * ti, 32 * ks, lane), ld_op(sK, LK, 16 * tj, 32 * ks, lane), acc);
-            const int j = 16 * tj + lr;
-            const float Gj = sG[j], rkj = sRk[j];
+            for (int job = 0; job < 3; ++job) {
+                const int li = job == 0 ? 0 : 1, lj = job == 2 ? 1 : 0;
+                const int ti = 2 * b + li, tj = 2 * b + lj;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * ti + 4 * lq + e;
-                const float dec = expf(sG[i] - Gj);
-                if (isA) {
-                    sA[i * LF + j] = (j < i) ? sB[i] * sRk[i] * rkj * acc[e] * dec : 0.f;
-                } else {
-                    sP[i * LC + j] = f32_to_bf16((j <= i) ? sRq[i] * rkj * acc[e] * dec : 0.f);
-                }
-            }
-        }
-        // zero the strictly-upper tiles of P (read by the P Delta product's diagonal k-steps)
-        for (int idx = tid; idx < 6 * 256; idx += NT) {
-            const int tile = idx >> 8, el = idx & 255;
-            const int ti = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
-            const int tj = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
-            sP[(16 * ti + (el >> 4)) * LC + 16 * tj + (el & 15)] = 0;
-        }
-        f32x4 Y[4], Oacc[4];
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            f32x4 y = {0.f, 0.f, 0.f, 0.f}, oa = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < DK / 32; ++ks) {
-                const bf16x8 kk = ld_op(sK, LK, 16 * w, 32 * ks, lane);
-                const bf16x8 qq = ld_op(sQ, LK, 16 * w, 32 * ks, lane);
-                const bf16x8 shi = ld_op(sSt_hi, LK, 16 * ct, 32 * ks, lane);
-                const bf16x8 slo = ld_op(sSt_lo, LK, 16 * ct, 32 * ks, lane);
-                y = mfma_bf16(kk, shi, y);
-                y = mfma_bf16(kk, slo, y);
-                oa = mfma_bf16(qq, shi, oa);
-            }
-            Y[ct] = y;
-            Oacc[ct] = oa;
-        }
-        __syncthreads();
-
-        // ---- S4: T = (I + A)^{-1} in fp32.  (a) the four 16x16 diagonal blocks by
-        // forward substitution, one column per lane of wave 0.
-        if (w == 0) {
-            const int b = lane >> 4, c = lane & 15;
-            const float *Ab = sA + (16 * b) * LF + 16 * b;
-            float x[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) x[i] = (i == c) ? 1.f : 0.f;
-#pragma unroll
-            for (int i = 1; i < 16; ++i) {
-                float acc = 0.f;
-#pragma unroll
-                for (int j = 0; j < i; ++j) acc += Ab[i * LF + j] * x[j];
-                if (i > c) x[i] = -acc;
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sTf[(16 * b + i) * LF + 16 * b + c] = x[i];
-        }
-        // zero the strictly-upper blocks of T
-        for (int idx = tid; idx < 6 * 256; idx += NT) {
-            const int tile = idx >> 8, el = idx & 255;
-            const int ti = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
-            const int tj = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
-            sTf[(16 * ti + (el >> 4)) * LF + 16 * tj + (el & 15)] = 0.f;
-        }
-        __syncthreads();
-        // (b) pairs: T_10 = -T_11 A_10 T_00 (wave 0), T_32 = -T_33 A_32 T_22 (wave 1)
-        constexpr int LS = 36;  // scratch row stride (fp32)
-        if (w < 2) {
-            const int b0 = 2 * w;  // blocks (b0+1, b0)
-            f32x4 r = {0.f, 0.f, 0.f, 0.f};
-            r = mm16_f32(sA + (16 * (b0 + 1)) * LF + 16 * b0, LF, sTf + (16 * b0) * LF + 16 * b0, LF, r, lane);
-            st_tile_f32(sScr + 16 * w, LS, r, 1.f, lane);
-        }
-        __syncthreads();
-        if (w < 2) {
-            const int b0 = 2 * w;
-            f32x4 r = {0.f, 0.f, 0.f, 0.f};
-            r = mm16_f32(sTf + (16 * (b0 + 1)) * LF + 16 * (b0 + 1), LF, sScr + 16 * w, LS, r, lane);
-            st_tile_f32(sTf + (16 * (b0 + 1)) * LF + 16 * b0, LF, r, -1.f, lane);
-        }
-        __syncthreads();
-        // (c) halves: T[32:64, 0:32] = -T[32:64, 32:64] (A[32:64, 0:32] T[0:32, 0:32]);
-        // wave w computes the 16x16 output tile (w / 2, w % 2) of each product.
-        {
-            const int ri = w >> 1, cj = w & 1;
-            f32x4 r = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                r = mm16_f32(sA + (32 + 16 * ri) * LF + 16 * kb, LF, sTf + (16 * kb) * LF + 16 * cj, LF, r, lane);
-            st_tile_f32(sScr + (16 * ri) * LS + 16 * cj, LS, r, 1.f, lane);
-        }
-        __syncthreads();
-        {
-            const int ri = w >> 1, cj = w & 1;
-            f32x4 r = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                r = mm16_f32(sTf + (32 + 16 * ri) * LF + 32 + 16 * kb, LF, sScr + (16 * kb) * LS + 16 * cj, LS, r,
-                             lane);
-            st_tile_f32(sTf + (32 + 16 * ri) * LF + 16 * cj, LF, r, -1.f, lane);
-        }
-        __syncthreads();
-        // (d) T -> hi + lo bf16; Z = beta (V - gamma r_k Y) -> Z^T hi + lo (A is dead now)
-        for (int idx = tid; idx < C * C; idx += NT) {
-            const int i = idx >> 6, j = idx & 63;
-            uint16_t hi, lo;
-            split_bf16(sTf[i * LF + j], hi, lo);
-            sT_hi[i * LC + j] = hi;
-            sT_lo[i * LC + j] = lo;
-        }
-        __syncthreads();  // sA (aliased by Z^T) and sTf are fully read
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            uint16_t hi[4], lo[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * w + 4 * lq + e;
-                const float vv = bf16_to_f32(sV[i * LC + 16 * ct + lr]);
-                const float z = sB[i] * (vv - sGam[i] * sRk[i] * Y[ct][e]);
-                split_bf16(z, hi[e], lo[e]);
-            }
-            const int off = (16 * ct + lr) * LC + 16 * w + 4 * lq;
-            *reinterpret_cast<uint2 *>(sZt_hi + off) =
-                make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
-            *reinterpret_cast<uint2 *>(sZt_lo + off) =
-                make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
-        }
-        if (tid < C) sDn[tid] = sRk[tid] * expf(sG[C - 1] - sG[tid]);
-        __syncthreads();
-
-        // ---- S6: Delta = T Z (three passes); D = diag(r_k exp(G_n - G)) Delta
-        const int nks = (w >> 1) + 1;  // 32-token k-steps needed by row tile w (T is lower triangular)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            f32x4 dl = {0.f, 0.f, 0.f, 0.f};
-            for (int ks = 0; ks < nks; ++ks) {
-                const bf16x8 th = ld_op(sT_hi, LC, 16 * w, 32 * ks, lane);
-                const bf16x8 tl = ld_op(sT_lo, LC, 16 * w, 32 * ks, lane);
-                const bf16x8 zh = ld_op(sZt_hi, LC, 16 * ct, 32 * ks, lane);
-                const bf16x8 zl = ld_op(sZt_lo, LC, 16 * ct, 32 * ks, lane);
-                dl = mfma_bf16(th, zh, dl);
-                dl = mfma_bf16(th, zl, dl);
-                dl = mfma_bf16(tl, zh, dl);
-            }
-            uint16_t dh[4], dlo[4], dsg[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * w + 4 * lq + e;
-                dsg[e] = f32_to_bf16(dl[e]);
-                split_bf16(sDn[i] * dl[e], dh[e], dlo[e]);
-            }
-            const int off = (16 * ct + lr) * LC + 16 * w + 4 * lq;
-            *reinterpret_cast<uint2 *>(sDelt + off) =
-                make_uint2(dsg[0] | ((uint32_t)dsg[1] << 16), dsg[2] | ((uint32_t)dsg[3] << 16));
-            *reinterpret_cast<uint2 *>(sDt_hi + off) =
-                make_uint2(dh[0] | ((uint32_t)dh[1] << 16), dh[2] | ((uint32_t)dh[3] << 16));
-            *reinterpret_cast<uint2 *>(sDt_lo + off) =
-                make_uint2(dlo[0] | ((uint32_t)dlo[1] << 16), dlo[2] | ((uint32_t)dlo[3] << 16));
-        }
-        __syncthreads();
-
-        // ---- S7: O = gamma r_q (Q S) + P Delta -> global; S <- gamma_n S + K^T D
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            f32x4 pd = {0.f, 0.f, 0.f, 0.f};
-            for (int ks = 0; ks < nks; ++ks)
-                pd = mfma_bf16(ld_op(sP, LC, 16 * w, 32 * ks, lane), ld_op(sDelt, LC, 16 * ct, 32 * ks, lane), pd);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * w + 4 * lq + e;
-                if (i < n) {
-                    const float ov = sGam[i] * sRq[i] * Oacc[ct][e] + pd[e];
-                    o[((size_t)(c0 + i) * HV + h) * DV + col0 + 16 * ct + lr] = f32_to_bf16(ov);
-                }
-            }
-        }
-        const float gam_n = sGam[C - 1];
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-                f32x4 s = S[dt][ct] * gam_n;
-#pragma unroll
-                for (int ks = 0; ks < C / 32; ++ks) {
-                    const bf16x8 kt = ld_op(sKt, LC, 32 * w + 16 * dt, 32 * ks, lane);
-                    s = mfma_bf16(kt, ld_op(sDt_hi, LC, 16 * ct, 32 * ks, lane), s);
-                    s = mfma_bf16(kt, ld_op(sDt_lo, LC, 16 * ct, 32 * ks, lane), s);
-                }
-                S[dt][ct] = s;
-            }
-        __syncthreads();  // every wave is done reading S^T before it is rewritten
-        write_St();
-    }
-
-    if (S_T) {
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
+                for (int ks = 0; ks < DK / 32; ++ks)
+                    acc = mfma32(ld_std(sK, LK, 16 * ti, 32 * ks, ln), ld_std(sK, LK, 16 * tj, 32 * ks, ln), acc);
+                const int j = 16 * tj + lrr;
+                const float Gj = sG[j], rkj = sRk[j];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int d = 32 * w + 16 * dt + 4 * lq + e;
-                    S_T[tab + (size_t)d * DV + col0 + 16 * ct + lr] = S[dt][ct][e];
+                    const int i = 16 * ti + 4 * lqq + e;
+                    const float a = (j < i) ? sB[i] * sRk[i] * rkj * acc[e] * expf(sG[i] - Gj) : 0.f;
+                    Af[(i - 32 * b) * LW + (j - 32 * b)] = a;
                 }
+                sched_fence();
+            }
+            wave_lds_sync();
+            // 16x16 diagonal inverses by forward substitution, one column per ln
+            // (ln = (block, column c)), swept by columns of A so that only one
+            // column of A is live at a time.
+            {
+                const int blk = (ln >> 4) & 1, cc = ln & 15;
+                const float *Ab = Af + (16 * blk) * LW + 16 * blk;
+                float x[16], acc[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    x[j] = (j == cc) ? 1.f : (j > cc ? -acc[j] : 0.f);
+#pragma unroll
+                    for (int i = j + 1; i < 16; ++i) acc[i] += Ab[i * LW + j] * x[j];
+                    sched_fence();
+                }
+                if (ln < 32) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) Tf[(16 * blk + i) * LW + 16 * blk + cc] = x[i];
+                } else {
+                    // the upper 16x16 block of T_b is zero
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) Tf[(8 * ((ln - 32) >> 4) + i) * LW + 16 + (ln & 15)] = 0.f;
+                }
+            }
+            wave_lds_sync();
+            // merge: T_10 = -T_11 (A_10 T_00), fp32 MFMA
+            {
+                f32x4 r = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    r = mfma_f32(Af[(16 + lrr) * LW + 4 * kk + lqq], Tf[(4 * kk + lqq) * LW + lrr], r);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Rf[(4 * lqq + e) * 17 + lrr] = r[e];
+                wave_lds_sync();
+                f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    t = mfma_f32(Tf[(16 + lrr) * LW + 16 + 4 * kk + lqq], Rf[(4 * kk + lqq) * 17 + lrr], t);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Tf[(16 + 4 * lqq + e) * LW + lrr] = -t[e];
+            }
+            wave_lds_sync();
+            // T_b -> tile-order operands (hi, lo) for row tiles rt = 0, 1
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const float *row = Tf + (16 * rt + lrr) * LW + 4 * lqq;
+                f32x8 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[e] = row[e];
+                    x[4 + e] = row[16 + e];
+                }
+                bf16x8 hi, lo;
+                split(x, hi, lo);
+                opT[((2 * b + rt) * 2 + 0) * 64 + ln] = hi;
+                opT[((2 * b + rt) * 2 + 1) * 64 + ln] = lo;
+            }
+        } else if (gw == 2) {
+            // ---- -A_10 (rows 32..63, columns 0..31) in tile order, from role-swapped Gram tiles
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                f32x8 x;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < DK / 32; ++ks)
+                        acc = mfma32(ld_std(sK, LK, 16 * t, 32 * ks, ln),
+                                     ld_std(sK, LK, 32 + 16 * rt, 32 * ks, ln), acc);
+                    const int i = 32 + 16 * rt + lrr;
+                    const float ci = sB[i] * sRk[i], Gi = sG[i];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int j = 16 * t + 4 * lqq + e;
+                        x[4 * t + e] = -ci * sRk[j] * acc[e] * expf(Gi - sG[j]);
+                    }
+                    sched_fence();
+                }
+                bf16x8 hi, lo;
+                split(x, hi, lo);
+                opA[(rt * 2 + 0) * 64 + ln] = hi;
+                opA[(rt * 2 + 1) * 64 + ln] = lo;
+            }
+            sDn[ln] = sRk[ln] * expf(sG[C - 1] - sG[ln]);
+        } else {
+            // ---- P in tile order, operand (rt, ks) for ks <= rt / 2
+#pragma unroll
+            for (int idx = 0; idx < 6; ++idx) {
+                const int rt = idx == 0 ? 0 : (idx == 1 ? 1 : (idx < 4 ? 2 : 3));
+                const int ks = (idx == 3 || idx == 5) ? 1 : 0;
+                f32x8 x;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int kt = 2 * ks + t;
+                    if (kt > rt) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[4 * t + e] = 0.f;
+                        continue;
+                    }
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kq = 0; kq < DK / 32; ++kq)
+                        acc = mfma32(ld_std(sK, LK, 16 * kt, 32 * kq, ln), ld_std(sQ, LK, 16 * rt, 32 * kq, ln),
+                                     acc);
+                    const int i = 16 * rt + lrr;
+                    const float ci = sRq[i], Gi = sG[i];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int j = 16 * kt + 4 * lqq + e;
+                        x[4 * t + e] = (j <= i) ? ci * sRk[j] * acc[e] * expf(Gi - sG[j]) : 0.f;
+                    }
+                    sched_fence();
+                }
+                opP[idx * 64 + ln] = to_bf16(x);
+                sched_fence();
+            }
+        }
+        __syncthreads();  // (3)
     }
 }
 
@@ -494,10 +566,10 @@ hipError_t launch_prefill_chunked(const PrefillArgs &a, hipStream_t stream) {
     if (a.N == 0) return hipSuccess;
     const int rep = a.HV / a.HQK;
     dim3 grid((unsigned)((int64_t)a.N * a.HV), (unsigned)(a.dv / DVS));
-    hipLaunchKernelGGL((prefill_chunked_kernel<uint16_t>), grid, dim3(NT), 0, stream,
-                       static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
-                       static_cast<const uint16_t *>(a.v), a.g, a.beta, a.cu_seqlens, a.eq_len, a.S0,
-                       static_cast<uint16_t *>(a.o), a.S_T, a.HV, a.dv, rep, a.scale);
+    hipLaunchKernelGGL(prefill_chunked_kernel, grid, dim3(NT), 0, stream, static_cast<const uint16_t *>(a.q),
+                       static_cast<const uint16_t *>(a.k), static_cast<const uint16_t *>(a.v), a.g, a.beta,
+                       a.cu_seqlens, a.eq_len, a.S0, static_cast<uint16_t *>(a.o), a.S_T, a.HV, a.dv, rep,
+                       a.scale);
     return hipGetLastError();
 }
 
