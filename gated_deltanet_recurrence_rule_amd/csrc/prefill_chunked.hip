@@ -66,14 +66,16 @@ constexpr int LW = 33;      // row stride (fp32) of the Gram waves' private 32x3
 // LDS layout (bytes)
 constexpr int OFF_K = 0;                                   // K  [C][LK] bf16, rows = tokens
 constexpr int OFF_Q = OFF_K + C * LK * 2;                  // Q  [C][LK]
-constexpr int OFF_KT = OFF_Q + C * LK * 2;                 // K^T [DK][LT], token index swizzled
-constexpr int OFF_OPT = OFF_KT + DK * LT * 2;              // T_b operands [2 b][2 rt][2 hi/lo][64][8]
+constexpr int OFF_KT = OFF_Q + C * LK * 2;                 // K^T [2 chunk parity][DK][LT], swizzled
+constexpr int OFF_OPT = OFF_KT + 2 * DK * LT * 2;          // T_b operands [2 b][2 rt][2 hi/lo][64][8]
 constexpr int OFF_OPA = OFF_OPT + 2 * 2 * 2 * 64 * 16;     // -A_10 operands [2 rt][2 hi/lo][64][8]
 constexpr int OFF_OPP = OFF_OPA + 2 * 2 * 64 * 16;         // P operands [6 (rt, ks)][64][8]
 constexpr int OFF_WP = OFF_OPP + 6 * 64 * 16;              // per Gram wave 4,5: Af, Tf [32][LW], Rf [16][17]
 constexpr int WP_SZ = (2 * 32 * LW + 16 * 17) * 4;
-constexpr int OFF_SC = OFF_WP + 2 * WP_SZ;                 // 6 x C fp32 scalars
-constexpr int LDS_BYTES = OFF_SC + 6 * C * 4;
+constexpr int SC_SZ = 6 * C;                               // fp32 per-token scalars of one chunk
+constexpr int OFF_SC = OFF_WP + 2 * WP_SZ;                 // scalars [2 chunk parity][SC_SZ]
+constexpr int OFF_OST = OFF_SC + 2 * SC_SZ * 4;            // per column wave: one 16x16 bf16 output tile
+constexpr int LDS_BYTES = OFF_OST + 4 * 16 * 16 * 2;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -105,15 +107,30 @@ __device__ __forceinline__ f32x4 mfma32_x3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16
 __device__ __forceinline__ bf16x8 ld_std(const __bf16 *base, int stride, int r0, int k0, int lane) {
     return *reinterpret_cast<const bf16x8 *>(base + (r0 + (lane & 15)) * stride + k0 + 8 * (lane >> 4));
 }
-// Tile-order operand: row r0 + lane%16, k = k0 + 4*(lane/16) .. +3 then k0 + 16 + 4*(lane/16) .. +3.
-__device__ __forceinline__ bf16x8 ld_tile(const __bf16 *base, int stride, int r0, int k0, int lane) {
-    const __bf16 *p = base + (r0 + (lane & 15)) * stride + k0 + 4 * (lane >> 4);
-    return cat(*reinterpret_cast<const bf16x4 *>(p), *reinterpret_cast<const bf16x4 *>(p + 16));
+// Tile order inside every 32-element block: stored position 8g + 4t + e holds element
+// 16t + 4g + e.  K and Q rows (over d) and K^T rows (over tokens) are kept in LDS in
+// this order, so the 8 tile-order operand values of lane group g = lane/16 are one
+// contiguous 16-byte read (ld_std at k0 = 32 * block).  Gram products read both
+// operands in the same permuted order, which leaves them unchanged.
+__device__ __forceinline__ int tile_pos(int x) {
+    const int r = x & 31;
+    return (x & ~31) + 8 * ((r >> 2) & 3) + 4 * (r >> 4) + (r & 3);
 }
+// K^T bank swizzle: 8-element groups are permuted per 8-row band of K^T so that the
+// 16 lanes writing one token hit 16 different banks; groups of 8 stay contiguous.
+__device__ __forceinline__ int kt_col(int d, int pos) { return pos ^ (8 * ((d >> 3) & 7)); }
 
-// K^T token swizzle: 8-token groups are permuted per 8-row band of K^T so that the
-// 16 lanes writing one token row hit 16 different banks.  Groups of 4 stay contiguous.
-__device__ __forceinline__ int kt_col(int d, int tok) { return tok ^ (8 * ((d >> 3) & 7)); }
+// 2^x on the hardware exponential unit (flushes very negative x to zero).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Sum over each row of 16 lanes, result in every lane of the row (DPP, no LDS traffic).
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+    return x;
+}
 
 // A copy of x the compiler cannot see through: lane-dependent addresses derived from
 // it are recomputed inside the chunk loop instead of being hoisted out and spilled.
@@ -121,9 +138,6 @@ __device__ __forceinline__ int opaque(int x) {
     asm volatile("" : "+v"(x));
     return x;
 }
-
-// Keeps the scheduler from hoisting loads of later iterations (bounds live registers).
-__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // Orders LDS writes before later LDS reads of the same wave (no workgroup barrier).
 __device__ __forceinline__ void wave_lds_sync() {
@@ -140,16 +154,20 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
     __bf16 *sK = reinterpret_cast<__bf16 *>(lds + OFF_K);
     __bf16 *sQ = reinterpret_cast<__bf16 *>(lds + OFF_Q);
-    __bf16 *sKt = reinterpret_cast<__bf16 *>(lds + OFF_KT);
+    __bf16 *const sKt0 = reinterpret_cast<__bf16 *>(lds + OFF_KT);
     bf16x8 *opT = reinterpret_cast<bf16x8 *>(lds + OFF_OPT);  // [((b*2 + rt)*2 + hl)*64 + lane]
     bf16x8 *opA = reinterpret_cast<bf16x8 *>(lds + OFF_OPA);  // [(rt*2 + hl)*64 + lane]
     bf16x8 *opP = reinterpret_cast<bf16x8 *>(lds + OFF_OPP);  // [idx*64 + lane]
-    float *sG = reinterpret_cast<float *>(lds + OFF_SC);      // cumulative log-decay
-    float *sGam = sG + C;                                     // exp(G_i)
-    float *sRk = sGam + C;                                    // 1 / |k_i|
-    float *sRq = sRk + C;                                     // scale / |q_i|
-    float *sB = sRq + C;                                      // beta_i
-    float *sDn = sB + C;                                      // r_k,i exp(G_n - G_i)
+    float *const sc0 = reinterpret_cast<float *>(lds + OFF_SC);
+    // Per-token scalars of chunk c live in buffer c % 2 (the next chunk's are written
+    // while the current one is still being read):  G (cumulative log-decay times log2 e),
+    // gamma = exp(G), r_k = 1/|k|, r_q = scale/|q|, beta, r_k exp(G_n - G).
+#define GDN_SCALARS(c)                                         \
+    float *sc_ = sc0 + ((c) & 1) * SC_SZ;                      \
+    float *sG = sc_, *sGam = sc_ + C, *sRk = sc_ + 2 * C;      \
+    float *sRq = sc_ + 3 * C, *sB = sc_ + 4 * C, *sDn = sc_ + 5 * C; \
+    __bf16 *sKt = sKt0 + ((c) & 1) * DK * LT;                  \
+    (void)sG; (void)sGam; (void)sRk; (void)sRq; (void)sB; (void)sDn; (void)sKt;
 
     const int unit = blockIdx.x;  // n * HV + h
     const int h = unit % HV;
@@ -182,6 +200,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         f32x4 S[8];
         const size_t tab = (size_t)unit * DK * DV;
         const int mycol = col0 + 16 * w + lr;
+        uint16_t *ost = reinterpret_cast<uint16_t *>(lds + OFF_OST) + w * 256;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
@@ -201,21 +220,23 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                     vreg[rt][e] = (i < nn) ? v[((size_t)(cs + i) * HV + h) * DV + mycol] : (uint16_t)0;
                 }
         };
-        if (nchunks > 0) prefetch_v(0);
+        if (nchunks > 0) {
+            prefetch_v(0);
+            __syncthreads();  // (0) chunk 0's K, Q, K^T and scalars are in LDS
+        }
 
         for (int c = 0; c < nchunks; ++c) {
             const int ln = opaque(lane);
             const int lrr = ln & 15, lqq = ln >> 4;
             const int64_t c0 = t0 + (int64_t)c * C;
             const int n = chunk_len(c);
-            __syncthreads();  // (1) previous chunk done with LDS
+            GDN_SCALARS(c)
             float vcur[4][4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) vcur[rt][e] = bf16_to_f32(vreg[rt][e]);
             if (c + 1 < nchunks) prefetch_v(c + 1);
-            __syncthreads();  // (2) K, Q, K^T and the scalars are in LDS
 
             // ---- Y = K S (hi + lo), Oacc = Q S (hi), Z = beta (v - gamma r_k Y)
             f32x4 Z[4], Oacc[4];
@@ -228,22 +249,22 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                     f32x4 y = {0.f, 0.f, 0.f, 0.f}, oa = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < 4; ++ks) {
-                        const bf16x8 kk = ld_tile(sK, LK, 16 * rt, 32 * ks, ln);
-                        const bf16x8 qq = ld_tile(sQ, LK, 16 * rt, 32 * ks, ln);
+                        const bf16x8 kk = ld_std(sK, LK, 16 * rt, 32 * ks, ln);
+                        const bf16x8 qq = ld_std(sQ, LK, 16 * rt, 32 * ks, ln);
                         y = mfma32(kk, Sh[ks], y);
                         y = mfma32(kk, Sl[ks], y);
                         oa = mfma32(qq, Sh[ks], oa);
                     }
+                    const int i0 = 16 * rt + 4 * lqq;
+                    const f32x4 b4 = *reinterpret_cast<const f32x4 *>(sB + i0);
+                    const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sGam + i0);
+                    const f32x4 k4 = *reinterpret_cast<const f32x4 *>(sRk + i0);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = 16 * rt + 4 * lqq + e;
-                        Z[rt][e] = sB[i] * (vcur[rt][e] - sGam[i] * sRk[i] * y[e]);
-                    }
+                    for (int e = 0; e < 4; ++e) Z[rt][e] = b4[e] * (vcur[rt][e] - g4[e] * k4[e] * y[e]);
                     Oacc[rt] = oa;
-                    sched_fence();
                 }
             }
-            __syncthreads();  // (3) P, -A_10, T_0, T_1 and r_k exp(G_n - G) are in LDS
+            __syncthreads();  // (A) P, -A_10, T_0, T_1 and r_k exp(G_n - G) of chunk c are in LDS
 
             // ---- Delta_0 = T_0 Z_0;  Delta_1 = T_1 (Z_1 - A_10 Delta_0)
             f32x4 Dl[4];
@@ -281,15 +302,21 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                     const int base = rt == 0 ? 0 : (rt == 1 ? 1 : (rt == 2 ? 2 : 4));
 #pragma unroll
                     for (int ks = 0; ks <= (rt >> 1); ++ks) pd = mfma32(opP[(base + ks) * 64 + ln], Dsg[ks], pd);
+                    const int i0 = 16 * rt + 4 * lqq;
+                    const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sGam + i0);
+                    const f32x4 q4 = *reinterpret_cast<const f32x4 *>(sRq + i0);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = 16 * rt + 4 * lqq + e;
-                        if (i < n) {
-                            const float ov = sGam[i] * sRq[i] * Oacc[rt][e] + pd[e];
-                            o[((size_t)(c0 + i) * HV + h) * DV + mycol] = __builtin_bit_cast(uint16_t, (__bf16)ov);
-                        }
+                    for (int e = 0; e < 4; ++e)
+                        ost[(4 * lqq + e) * 16 + lrr] = __builtin_bit_cast(uint16_t, (__bf16)(g4[e] * q4[e] * Oacc[rt][e] + pd[e]));
+                    wave_lds_sync();
+                    {
+                        const int r = ln >> 2, cq = ln & 3;
+                        const uint2 val = *reinterpret_cast<const uint2 *>(ost + r * 16 + 4 * cq);
+                        if (16 * rt + r < n)
+                            *reinterpret_cast<uint2 *>(o + ((size_t)(c0 + 16 * rt + r) * HV + h) * DV + col0 + 16 * w +
+                                                       4 * cq) = val;
                     }
-                    sched_fence();
+                    wave_lds_sync();
                 }
             }
             // ---- S <- gamma_n S + K^T D,  D = diag(r_k exp(G_n - G)) Delta
@@ -299,9 +326,11 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                 for (int ks = 0; ks < 2; ++ks) {
                     f32x8 x = cat(Dl[2 * ks], Dl[2 * ks + 1]);
 #pragma unroll
-                    for (int t = 0; t < 2; ++t)
+                    for (int t = 0; t < 2; ++t) {
+                        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sDn + 32 * ks + 16 * t + 4 * lqq);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) x[4 * t + e] *= sDn[32 * ks + 16 * t + 4 * lqq + e];
+                        for (int e = 0; e < 4; ++e) x[4 * t + e] *= d4[e];
+                    }
                     split(x, Dh[ks], Dlo[ks]);
                 }
                 const float gam_n = sGam[C - 1];
@@ -312,16 +341,14 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                     const __bf16 *rowp = sKt + d * LT;
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks) {
-                        const int tk = 32 * ks + 4 * lqq;
-                        const bf16x8 kt = cat(*reinterpret_cast<const bf16x4 *>(rowp + kt_col(d, tk)),
-                                              *reinterpret_cast<const bf16x4 *>(rowp + kt_col(d, tk + 16)));
+                        const bf16x8 kt = *reinterpret_cast<const bf16x8 *>(rowp + kt_col(d, 32 * ks + 8 * lqq));
                         acc = mfma32(kt, Dh[ks], acc);
                         acc = mfma32(kt, Dlo[ks], acc);
                     }
                     S[dt] = acc;
-                    sched_fence();
                 }
             }
+            __syncthreads();  // (B) chunk c+1's K, Q, K^T and scalars are in LDS
         }
         if (S_T) {
 #pragma unroll
@@ -361,18 +388,24 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     };
     if (nchunks > 0) prefetch_qk(0);
 
-    for (int c = 0; c < nchunks; ++c) {
+    // chunk c's q, k, g, beta (already in registers) -> LDS, norms, cumulative decay
+    auto stage_chunk = [&](int c) {
+        GDN_SCALARS(c)
         const int ln = opaque(lane);
-        const int lrr = ln & 15, lqq = ln >> 4;
         const int gtt = opaque(gt);
         const int sgs = gtt & 15;
-        __syncthreads();  // (1) previous chunk done with LDS
         // ---- registers -> LDS (K, Q row-major, K^T swizzled), norms, cumulative decay
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const int r = (gtt >> 4) + 16 * p;
-            *reinterpret_cast<uint4 *>(sK + r * LK + 8 * sgs) = kreg[p];
-            *reinterpret_cast<uint4 *>(sQ + r * LK + 8 * sgs) = qreg[p];
+            {
+                // segment sgs holds d = 8 sgs .. 8 sgs + 7: two runs of 4 in tile order
+                const int p0 = 32 * (sgs >> 2) + 16 * (sgs & 1) + 4 * ((sgs >> 1) & 1);
+                *reinterpret_cast<uint2 *>(sK + r * LK + p0) = make_uint2(kreg[p].x, kreg[p].y);
+                *reinterpret_cast<uint2 *>(sK + r * LK + p0 + 8) = make_uint2(kreg[p].z, kreg[p].w);
+                *reinterpret_cast<uint2 *>(sQ + r * LK + p0) = make_uint2(qreg[p].x, qreg[p].y);
+                *reinterpret_cast<uint2 *>(sQ + r * LK + p0 + 8) = make_uint2(qreg[p].z, qreg[p].w);
+            }
             const uint32_t kw[4] = {kreg[p].x, kreg[p].y, kreg[p].z, kreg[p].w};
             const uint32_t qw[4] = {qreg[p].x, qreg[p].y, qreg[p].z, qreg[p].w};
             float sk = 0.f, sq = 0.f;
@@ -381,35 +414,40 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                 const uint16_t kb = (uint16_t)(kw[e >> 1] >> (16 * (e & 1)));
                 const uint16_t qb = (uint16_t)(qw[e >> 1] >> (16 * (e & 1)));
                 const int d = 8 * sgs + e;
-                reinterpret_cast<uint16_t *>(sKt)[d * LT + kt_col(d, r)] = kb;
+                reinterpret_cast<uint16_t *>(sKt)[d * LT + kt_col(d, tile_pos(r))] = kb;
                 const float kx = bf16_to_f32(kb), qx = bf16_to_f32(qb);
                 sk += kx * kx;
                 sq += qx * qx;
             }
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) {
-                sk += __shfl_xor(sk, off, 64);
-                sq += __shfl_xor(sq, off, 64);
-            }
+            sk = row16_sum(sk);
+            sq = row16_sum(sq);
             if (sgs == 0) {
                 sRk[r] = inv_norm(sk);
                 sRq[r] = inv_norm(sq) * scale;
             }
-            sched_fence();
         }
         if (gw == 3) {
-            float x = greg;
+            float x = greg * 1.44269504088896341f;  // log2(e)
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float y = __shfl_up(x, off, 64);
                 if (ln >= off) x += y;
             }
             sG[ln] = x;
-            sGam[ln] = expf(x);
+            sGam[ln] = exp2_hw(x);
             sB[ln] = breg;
         }
-        if (c + 1 < nchunks) prefetch_qk(c + 1);
-        __syncthreads();  // (2)
+    };
+
+    if (nchunks > 0) {
+        stage_chunk(0);
+        if (nchunks > 1) prefetch_qk(1);
+        __syncthreads();  // (0)
+    }
+    for (int c = 0; c < nchunks; ++c) {
+        const int ln = opaque(lane);
+        const int lrr = ln & 15, lqq = ln >> 4;
+        GDN_SCALARS(c)
 
         if (gw < 2) {
             // ---- T_b = (I + A_bb)^{-1} for the 32-token block b = gw
@@ -430,10 +468,9 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = 16 * ti + 4 * lqq + e;
-                    const float a = (j < i) ? sB[i] * sRk[i] * rkj * acc[e] * expf(sG[i] - Gj) : 0.f;
+                    const float a = (j < i) ? sB[i] * sRk[i] * rkj * acc[e] * exp2_hw(sG[i] - Gj) : 0.f;
                     Af[(i - 32 * b) * LW + (j - 32 * b)] = a;
                 }
-                sched_fence();
             }
             wave_lds_sync();
             // 16x16 diagonal inverses by forward substitution, one column per ln
@@ -450,7 +487,6 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                     x[j] = (j == cc) ? 1.f : (j > cc ? -acc[j] : 0.f);
 #pragma unroll
                     for (int i = j + 1; i < 16; ++i) acc[i] += Ab[i * LW + j] * x[j];
-                    sched_fence();
                 }
                 if (ln < 32) {
 #pragma unroll
@@ -494,37 +530,10 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                 opT[((2 * b + rt) * 2 + 0) * 64 + ln] = hi;
                 opT[((2 * b + rt) * 2 + 1) * 64 + ln] = lo;
             }
-        } else if (gw == 2) {
-            // ---- -A_10 (rows 32..63, columns 0..31) in tile order, from role-swapped Gram tiles
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                f32x8 x;
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < DK / 32; ++ks)
-                        acc = mfma32(ld_std(sK, LK, 16 * t, 32 * ks, ln),
-                                     ld_std(sK, LK, 32 + 16 * rt, 32 * ks, ln), acc);
-                    const int i = 32 + 16 * rt + lrr;
-                    const float ci = sB[i] * sRk[i], Gi = sG[i];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int j = 16 * t + 4 * lqq + e;
-                        x[4 * t + e] = -ci * sRk[j] * acc[e] * expf(Gi - sG[j]);
-                    }
-                    sched_fence();
-                }
-                bf16x8 hi, lo;
-                split(x, hi, lo);
-                opA[(rt * 2 + 0) * 64 + ln] = hi;
-                opA[(rt * 2 + 1) * 64 + ln] = lo;
-            }
-            sDn[ln] = sRk[ln] * expf(sG[C - 1] - sG[ln]);
         } else {
-            // ---- P in tile order, operand (rt, ks) for ks <= rt / 2
-#pragma unroll
-            for (int idx = 0; idx < 6; ++idx) {
+            // P in tile order: operand idx = (rt, ks) for ks <= rt / 2, i.e.
+            // idx 0 (0,0), 1 (1,0), 2 (2,0), 3 (2,1), 4 (3,0), 5 (3,1).
+            auto p_operand = [&](int idx) {
                 const int rt = idx == 0 ? 0 : (idx == 1 ? 1 : (idx < 4 ? 2 : 3));
                 const int ks = (idx == 3 || idx == 5) ? 1 : 0;
                 f32x8 x;
@@ -539,22 +548,58 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kq = 0; kq < DK / 32; ++kq)
-                        acc = mfma32(ld_std(sK, LK, 16 * kt, 32 * kq, ln), ld_std(sQ, LK, 16 * rt, 32 * kq, ln),
-                                     acc);
+                        acc = mfma32(ld_std(sK, LK, 16 * kt, 32 * kq, ln), ld_std(sQ, LK, 16 * rt, 32 * kq, ln), acc);
                     const int i = 16 * rt + lrr;
                     const float ci = sRq[i], Gi = sG[i];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int j = 16 * kt + 4 * lqq + e;
-                        x[4 * t + e] = (j <= i) ? ci * sRk[j] * acc[e] * expf(Gi - sG[j]) : 0.f;
+                        x[4 * t + e] = (j <= i) ? ci * sRk[j] * acc[e] * exp2_hw(Gi - sG[j]) : 0.f;
                     }
-                    sched_fence();
                 }
                 opP[idx * 64 + ln] = to_bf16(x);
-                sched_fence();
+            };
+            if (gw == 2) {
+                // -A_10 (rows 32..63, columns 0..31) in tile order, from role-swapped Gram tiles
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    f32x8 x;
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int ks = 0; ks < DK / 32; ++ks)
+                            acc = mfma32(ld_std(sK, LK, 16 * t, 32 * ks, ln),
+                                         ld_std(sK, LK, 32 + 16 * rt, 32 * ks, ln), acc);
+                        const int i = 32 + 16 * rt + lrr;
+                        const float ci = sB[i] * sRk[i], Gi = sG[i];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int j = 16 * t + 4 * lqq + e;
+                            x[4 * t + e] = -ci * sRk[j] * acc[e] * exp2_hw(Gi - sG[j]);
+                        }
+                    }
+                    bf16x8 hi, lo;
+                    split(x, hi, lo);
+                    opA[(rt * 2 + 0) * 64 + ln] = hi;
+                    opA[(rt * 2 + 1) * 64 + ln] = lo;
+                }
+                sDn[ln] = sRk[ln] * exp2_hw(sG[C - 1] - sG[ln]);
+                p_operand(0);
+                p_operand(1);
+            } else {
+                p_operand(2);
+                p_operand(3);
+                p_operand(4);
+                p_operand(5);
             }
         }
-        __syncthreads();  // (3)
+        __syncthreads();  // (A)
+        if (c + 1 < nchunks) {
+            stage_chunk(c + 1);
+            if (c + 2 < nchunks) prefetch_qk(c + 2);
+        }
+        __syncthreads();  // (B)
     }
 }
 
