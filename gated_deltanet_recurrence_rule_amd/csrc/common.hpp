@@ -39,10 +39,11 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-// 1 / max(sqrt(ss), eps): the L2-normalisation factor x / max(|x|, eps).
+// 1 / max(sqrt(ss), eps) with eps = 1e-12: the L2-normalisation factor x / max(|x|, eps).
+// Uses the hardware reciprocal square root (about 1 ulp); ss <= eps^2 (zero included)
+// gives 1 / eps.
 __device__ __forceinline__ float inv_norm(float ss) {
-    const float n = sqrtf(ss);
-    return 1.0f / fmaxf(n, 1e-12f);
+    return ss > 1e-24f ? __builtin_amdgcn_rsqf(ss) : 1e12f;
 }
 
 // ------------------------------------------------------------------ streaming access

@@ -61,7 +61,7 @@ constexpr int NT = 512;     // threads (8 waves)
 
 constexpr int LK = DK + 8;  // row stride (bf16) of K and Q in LDS
 constexpr int LT = C + 8;   // row stride (bf16) of K^T in LDS
-constexpr int LW = 33;      // row stride (fp32) of the Gram waves' private 32x32 blocks
+constexpr int LW = 36;      // row stride (fp32) of the Gram waves' private 32x32 blocks (16-byte rows)
 
 // LDS layout (bytes)
 constexpr int OFF_K = 0;                                   // K  [C][LK] bf16, rows = tokens
@@ -209,17 +209,26 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
 
         // v[16 rt + 4 lq + e][mycol] of the next chunk, fetched one chunk ahead
         uint16_t vreg[4][4];
+        const size_t vrs = (size_t)HV * DV;  // token stride of v and o
+        const uint16_t *vthr = v + (size_t)h * DV + mycol + (size_t)(4 * lq) * vrs;
         auto prefetch_v = [&](int c) {
             const int nn = chunk_len(c);
-            const int64_t cs = t0 + (int64_t)c * C;
+            const uint16_t *vc = vthr + (size_t)(t0 + (int64_t)c * C) * vrs;
+            if (nn == C) {
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
+                for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 16 * rt + 4 * lq + e;
-                    vreg[rt][e] = (i < nn) ? v[((size_t)(cs + i) * HV + h) * DV + mycol] : (uint16_t)0;
-                }
+                    for (int e = 0; e < 4; ++e) vreg[rt][e] = vc[(size_t)(16 * rt + e) * vrs];
+            } else {
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        vreg[rt][e] = (16 * rt + 4 * lq + e < nn) ? vc[(size_t)(16 * rt + e) * vrs] : (uint16_t)0;
+            }
         };
+        // output stores: lane writes row lane/4 of a 16-row tile, columns 4 (lane % 4) .. +3
+        uint16_t *othr = o + (size_t)h * DV + col0 + 16 * w + 4 * (lane & 3) + (size_t)(lane >> 2) * vrs;
         if (nchunks > 0) {
             prefetch_v(0);
             __syncthreads();  // (0) chunk 0's K, Q, K^T and scalars are in LDS
@@ -313,8 +322,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                         const int r = ln >> 2, cq = ln & 3;
                         const uint2 val = *reinterpret_cast<const uint2 *>(ost + r * 16 + 4 * cq);
                         if (16 * rt + r < n)
-                            *reinterpret_cast<uint2 *>(o + ((size_t)(c0 + 16 * rt + r) * HV + h) * DV + col0 + 16 * w +
-                                                       4 * cq) = val;
+                            *reinterpret_cast<uint2 *>(othr + (size_t)(c0 + 16 * rt) * vrs) = val;
                     }
                     wave_lds_sync();
                 }
@@ -359,26 +367,44 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         return;
     }
 
-    // ====================== Gram waves: chunk loads, norms, decay, P, A, T ===========
+    // ====================== Gram waves: chunk staging, norms, decay, P, A, T =====
     const int gt = tid - 256;  // 0..255
     const int gw = w - 4;      // 0..3
-    // q, k of the next chunk: rows r = gt/16 + 16 p (p = 0..3), 16-byte segment s = gt % 16
+    // Staging: item gt + 256 p (p = 0, 1) is the token pair (2 pr, 2 pr + 1), pr = gt/16 + 16 p,
+    // times the 16-byte segment s = gt % 16 of their q and k rows (d = 8 s .. 8 s + 7).
     const int seg_s = gt & 15;
-    uint4 kreg[4], qreg[4];
-    float greg = 0.f, breg = 0.f;  // Gram wave 3 (w == 7): token = lane
+    uint4 kreg[2][2], qreg[2][2];  // [p][token of the pair]
+    float greg = 0.f, breg = 0.f;  // Gram wave 3: token = lane
+    const size_t rs = (size_t)HQK * DK;  // token stride of q and k
+    const size_t thr_off = (size_t)hq * DK + 8 * seg_s + (size_t)(2 * (gt >> 4)) * rs;
+    const uint16_t *kthr = k + thr_off;
+    const uint16_t *qthr = q + thr_off;
     auto prefetch_qk = [&](int c) {
         const int nn = chunk_len(c);
         const int64_t cs = t0 + (int64_t)c * C;
+        const uint16_t *kc = kthr + (size_t)cs * rs;
+        const uint16_t *qc = qthr + (size_t)cs * rs;
+        if (nn == C) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int r = (gt >> 4) + 16 * p;
-            kreg[p] = make_uint4(0, 0, 0, 0);
-            qreg[p] = make_uint4(0, 0, 0, 0);
-            if (r < nn) {
-                const size_t off = ((size_t)(cs + r) * HQK + hq) * DK + 8 * seg_s;
-                kreg[p] = *reinterpret_cast<const uint4 *>(k + off);
-                qreg[p] = *reinterpret_cast<const uint4 *>(q + off);
-            }
+            for (int p = 0; p < 2; ++p)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    kreg[p][u] = *reinterpret_cast<const uint4 *>(kc + (size_t)(32 * p + u) * rs);
+                    qreg[p][u] = *reinterpret_cast<const uint4 *>(qc + (size_t)(32 * p + u) * rs);
+                }
+        } else {
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int r = 2 * ((gt >> 4) + 16 * p) + u;
+                    kreg[p][u] = make_uint4(0, 0, 0, 0);
+                    qreg[p][u] = make_uint4(0, 0, 0, 0);
+                    if (r < nn) {
+                        kreg[p][u] = *reinterpret_cast<const uint4 *>(kc + (size_t)(32 * p + u) * rs);
+                        qreg[p][u] = *reinterpret_cast<const uint4 *>(qc + (size_t)(32 * p + u) * rs);
+                    }
+                }
         }
         if (gw == 3) {
             const bool ok = lane < nn;
@@ -394,36 +420,54 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         const int ln = opaque(lane);
         const int gtt = opaque(gt);
         const int sgs = gtt & 15;
-        // ---- registers -> LDS (K, Q row-major, K^T swizzled), norms, cumulative decay
+        // segment sgs (d = 8 sgs .. +7) sits at two runs of 4 in tile order
+        const int p0 = 32 * (sgs >> 2) + 16 * (sgs & 1) + 4 * ((sgs >> 1) & 1);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int r = (gtt >> 4) + 16 * p;
-            {
-                // segment sgs holds d = 8 sgs .. 8 sgs + 7: two runs of 4 in tile order
-                const int p0 = 32 * (sgs >> 2) + 16 * (sgs & 1) + 4 * ((sgs >> 1) & 1);
-                *reinterpret_cast<uint2 *>(sK + r * LK + p0) = make_uint2(kreg[p].x, kreg[p].y);
-                *reinterpret_cast<uint2 *>(sK + r * LK + p0 + 8) = make_uint2(kreg[p].z, kreg[p].w);
-                *reinterpret_cast<uint2 *>(sQ + r * LK + p0) = make_uint2(qreg[p].x, qreg[p].y);
-                *reinterpret_cast<uint2 *>(sQ + r * LK + p0 + 8) = make_uint2(qreg[p].z, qreg[p].w);
+        for (int p = 0; p < 2; ++p) {
+            const int pr = (gtt >> 4) + 16 * p;
+            float sk[2], sq[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int r = 2 * pr + u;
+                const uint4 kv = kreg[p][u], qv = qreg[p][u];
+                *reinterpret_cast<uint2 *>(sK + r * LK + p0) = make_uint2(kv.x, kv.y);
+                *reinterpret_cast<uint2 *>(sK + r * LK + p0 + 8) = make_uint2(kv.z, kv.w);
+                *reinterpret_cast<uint2 *>(sQ + r * LK + p0) = make_uint2(qv.x, qv.y);
+                *reinterpret_cast<uint2 *>(sQ + r * LK + p0 + 8) = make_uint2(qv.z, qv.w);
+                const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+                const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+                float a = 0.f, bq = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float k0 = __uint_as_float(kw[e] << 16), k1 = __uint_as_float(kw[e] & 0xffff0000u);
+                    const float q0 = __uint_as_float(qw[e] << 16), q1 = __uint_as_float(qw[e] & 0xffff0000u);
+                    a += k0 * k0 + k1 * k1;
+                    bq += q0 * q0 + q1 * q1;
+                }
+                sk[u] = a;
+                sq[u] = bq;
             }
-            const uint32_t kw[4] = {kreg[p].x, kreg[p].y, kreg[p].z, kreg[p].w};
-            const uint32_t qw[4] = {qreg[p].x, qreg[p].y, qreg[p].z, qreg[p].w};
-            float sk = 0.f, sq = 0.f;
+            // K^T: both tokens of the pair are adjacent in tile order -> one 4-byte write per d
+            const int tp = tile_pos(2 * pr);
+            const uint32_t k0w[4] = {kreg[p][0].x, kreg[p][0].y, kreg[p][0].z, kreg[p][0].w};
+            const uint32_t k1w[4] = {kreg[p][1].x, kreg[p][1].y, kreg[p][1].z, kreg[p][1].w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const uint16_t kb = (uint16_t)(kw[e >> 1] >> (16 * (e & 1)));
-                const uint16_t qb = (uint16_t)(qw[e >> 1] >> (16 * (e & 1)));
                 const int d = 8 * sgs + e;
-                reinterpret_cast<uint16_t *>(sKt)[d * LT + kt_col(d, tile_pos(r))] = kb;
-                const float kx = bf16_to_f32(kb), qx = bf16_to_f32(qb);
-                sk += kx * kx;
-                sq += qx * qx;
+                const uint32_t lo = (e & 1) ? (k0w[e >> 1] >> 16) : (k0w[e >> 1] & 0xffffu);
+                const uint32_t hi = (e & 1) ? (k1w[e >> 1] & 0xffff0000u) : (k1w[e >> 1] << 16);
+                *reinterpret_cast<uint32_t *>(sKt + d * LT + kt_col(d, tp)) = lo | hi;
             }
-            sk = row16_sum(sk);
-            sq = row16_sum(sq);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                sk[u] = row16_sum(sk[u]);
+                sq[u] = row16_sum(sq[u]);
+            }
             if (sgs == 0) {
-                sRk[r] = inv_norm(sk);
-                sRq[r] = inv_norm(sq) * scale;
+                sRk[2 * pr] = inv_norm(sk[0]);
+                sRk[2 * pr + 1] = inv_norm(sk[1]);
+                sRq[2 * pr] = inv_norm(sq[0]) * scale;
+                sRq[2 * pr + 1] = inv_norm(sq[1]) * scale;
             }
         }
         if (gw == 3) {
@@ -455,38 +499,59 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             float *Af = reinterpret_cast<float *>(lds + OFF_WP + b * WP_SZ);
             float *Tf = Af + 32 * LW;
             float *Rf = Tf + 32 * LW;
+            bf16x8 ka[4], kb[4];
 #pragma unroll
-            for (int job = 0; job < 3; ++job) {
-                const int li = job == 0 ? 0 : 1, lj = job == 2 ? 1 : 0;
-                const int ti = 2 * b + li, tj = 2 * b + lj;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int ks = 0; ks < 4; ++ks) {
+                ka[ks] = ld_std(sK, LK, 32 * b, 32 * ks, ln);
+                kb[ks] = ld_std(sK, LK, 32 * b + 16, 32 * ks, ln);
+            }
+            f32x4 g00 = {0.f, 0.f, 0.f, 0.f}, g10 = g00, g11 = g00;
 #pragma unroll
-                for (int ks = 0; ks < DK / 32; ++ks)
-                    acc = mfma32(ld_std(sK, LK, 16 * ti, 32 * ks, ln), ld_std(sK, LK, 16 * tj, 32 * ks, ln), acc);
-                const int j = 16 * tj + lrr;
+            for (int ks = 0; ks < 4; ++ks) {
+                g00 = mfma32(ka[ks], ka[ks], g00);
+                g10 = mfma32(kb[ks], ka[ks], g10);
+                g11 = mfma32(kb[ks], kb[ks], g11);
+            }
+            // A values of local tile (li, lj): element e at local (16 li + 4 lq + e, 16 lj + lr)
+            auto put_a = [&](const f32x4 &acc, int li, int lj) {
+                const int j = 32 * b + 16 * lj + lrr;
                 const float Gj = sG[j], rkj = sRk[j];
+                const int i0 = 32 * b + 16 * li + 4 * lqq;
+                const f32x4 G4 = *reinterpret_cast<const f32x4 *>(sG + i0);
+                const f32x4 B4 = *reinterpret_cast<const f32x4 *>(sB + i0);
+                const f32x4 R4 = *reinterpret_cast<const f32x4 *>(sRk + i0);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int i = 16 * ti + 4 * lqq + e;
-                    const float a = (j < i) ? sB[i] * sRk[i] * rkj * acc[e] * exp2_hw(sG[i] - Gj) : 0.f;
-                    Af[(i - 32 * b) * LW + (j - 32 * b)] = a;
+                    const float a = (j < i0 + e) ? B4[e] * R4[e] * rkj * acc[e] * exp2_hw(G4[e] - Gj) : 0.f;
+                    Af[(16 * li + 4 * lqq + e) * LW + 16 * lj + lrr] = a;
                 }
-            }
+            };
+            put_a(g00, 0, 0);
+            put_a(g10, 1, 0);
+            put_a(g11, 1, 1);
             wave_lds_sync();
-            // 16x16 diagonal inverses by forward substitution, one column per ln
-            // (ln = (block, column c)), swept by columns of A so that only one
-            // column of A is live at a time.
+            // 16x16 diagonal inverses by forward substitution, one column per lane
+            // (lane = (block, column cc)); row i of A is read as four 16-byte broadcasts.
             {
                 const int blk = (ln >> 4) & 1, cc = ln & 15;
                 const float *Ab = Af + (16 * blk) * LW + 16 * blk;
-                float x[16], acc[16];
+                float x[16];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+                for (int i = 0; i < 16; ++i) x[i] = (i == cc) ? 1.f : 0.f;
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    x[j] = (j == cc) ? 1.f : (j > cc ? -acc[j] : 0.f);
+                for (int i = 1; i < 16; ++i) {
+                    const f32x4 *row = reinterpret_cast<const f32x4 *>(Ab + i * LW);
+                    float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int i = j + 1; i < 16; ++i) acc[i] += Ab[i * LW + j] * x[j];
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        if (4 * q4 >= i) break;
+                        const f32x4 a4 = row[q4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (4 * q4 + e < i) part[e] += a4[e] * x[4 * q4 + e];
+                    }
+                    const float sum = (part[0] + part[1]) + (part[2] + part[3]);
+                    if (i > cc) x[i] = -sum;
                 }
                 if (ln < 32) {
 #pragma unroll
@@ -518,24 +583,28 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             // T_b -> tile-order operands (hi, lo) for row tiles rt = 0, 1
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
-                const float *row = Tf + (16 * rt + lrr) * LW + 4 * lqq;
-                f32x8 x;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x[e] = row[e];
-                    x[4 + e] = row[16 + e];
-                }
+                const f32x4 *row = reinterpret_cast<const f32x4 *>(Tf + (16 * rt + lrr) * LW + 4 * lqq);
+                const f32x4 x0 = row[0], x1 = row[4];
                 bf16x8 hi, lo;
-                split(x, hi, lo);
+                split(cat(x0, x1), hi, lo);
                 opT[((2 * b + rt) * 2 + 0) * 64 + ln] = hi;
                 opT[((2 * b + rt) * 2 + 1) * 64 + ln] = lo;
             }
         } else {
-            // P in tile order: operand idx = (rt, ks) for ks <= rt / 2, i.e.
-            // idx 0 (0,0), 1 (1,0), 2 (2,0), 3 (2,1), 4 (3,0), 5 (3,1).
-            auto p_operand = [&](int idx) {
+            // K blocks as the first (role-swapped) operand of every tile below
+            bf16x8 kk[4][4];
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) kk[blk][ks] = ld_std(sK, LK, 16 * blk, 32 * ks, ln);
+            // P operand idx = (rt, ks), ks <= rt / 2:  0 (0,0) 1 (1,0) 2 (2,0) 3 (2,1) 4 (3,0) 5 (3,1).
+            // Tile (rt, kt) from MFMA(K block kt, Q block rt): element e at lane is
+            // (Q K^T)[16 rt + lr][16 kt + 4 lq + e], the tile-order operand slot.
+            auto p_operand = [&](int idx, const bf16x8 *qq) {
                 const int rt = idx == 0 ? 0 : (idx == 1 ? 1 : (idx < 4 ? 2 : 3));
                 const int ks = (idx == 3 || idx == 5) ? 1 : 0;
+                const int i = 16 * rt + lrr;
+                const float ci = sRq[i], Gi = sG[i];
                 f32x8 x;
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
@@ -547,37 +616,38 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                     }
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int kq = 0; kq < DK / 32; ++kq)
-                        acc = mfma32(ld_std(sK, LK, 16 * kt, 32 * kq, ln), ld_std(sQ, LK, 16 * rt, 32 * kq, ln), acc);
-                    const int i = 16 * rt + lrr;
-                    const float ci = sRq[i], Gi = sG[i];
+                    for (int kq = 0; kq < 4; ++kq) acc = mfma32(kk[kt][kq], qq[kq], acc);
+                    const int j0 = 16 * kt + 4 * lqq;
+                    const f32x4 G4 = *reinterpret_cast<const f32x4 *>(sG + j0);
+                    const f32x4 R4 = *reinterpret_cast<const f32x4 *>(sRk + j0);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int j = 16 * kt + 4 * lqq + e;
-                        x[4 * t + e] = (j <= i) ? ci * sRk[j] * acc[e] * exp2_hw(Gi - sG[j]) : 0.f;
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        x[4 * t + e] = (j0 + e <= i) ? ci * R4[e] * acc[e] * exp2_hw(Gi - G4[e]) : 0.f;
                 }
                 opP[idx * 64 + ln] = to_bf16(x);
+            };
+            bf16x8 qq[4];
+            auto load_q = [&](int rt) {
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) qq[ks] = ld_std(sQ, LK, 16 * rt, 32 * ks, ln);
             };
             if (gw == 2) {
                 // -A_10 (rows 32..63, columns 0..31) in tile order, from role-swapped Gram tiles
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt) {
+                    const int i = 32 + 16 * rt + lrr;
+                    const float ci = sB[i] * sRk[i], Gi = sG[i];
                     f32x8 x;
 #pragma unroll
                     for (int t = 0; t < 2; ++t) {
                         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int ks = 0; ks < DK / 32; ++ks)
-                            acc = mfma32(ld_std(sK, LK, 16 * t, 32 * ks, ln),
-                                         ld_std(sK, LK, 32 + 16 * rt, 32 * ks, ln), acc);
-                        const int i = 32 + 16 * rt + lrr;
-                        const float ci = sB[i] * sRk[i], Gi = sG[i];
+                        for (int ks = 0; ks < 4; ++ks) acc = mfma32(kk[t][ks], kk[2 + rt][ks], acc);
+                        const int j0 = 16 * t + 4 * lqq;
+                        const f32x4 G4 = *reinterpret_cast<const f32x4 *>(sG + j0);
+                        const f32x4 R4 = *reinterpret_cast<const f32x4 *>(sRk + j0);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int j = 16 * t + 4 * lqq + e;
-                            x[4 * t + e] = -ci * sRk[j] * acc[e] * exp2_hw(Gi - sG[j]);
-                        }
+                        for (int e = 0; e < 4; ++e) x[4 * t + e] = -ci * R4[e] * acc[e] * exp2_hw(Gi - G4[e]);
                     }
                     bf16x8 hi, lo;
                     split(x, hi, lo);
@@ -585,13 +655,18 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                     opA[(rt * 2 + 1) * 64 + ln] = lo;
                 }
                 sDn[ln] = sRk[ln] * exp2_hw(sG[C - 1] - sG[ln]);
-                p_operand(0);
-                p_operand(1);
+                load_q(0);
+                p_operand(0, qq);
+                load_q(1);
+                p_operand(1, qq);
+                load_q(2);
+                p_operand(2, qq);
             } else {
-                p_operand(2);
-                p_operand(3);
-                p_operand(4);
-                p_operand(5);
+                load_q(2);
+                p_operand(3, qq);
+                load_q(3);
+                p_operand(4, qq);
+                p_operand(5, qq);
             }
         }
         __syncthreads();  // (A)
