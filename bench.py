@@ -50,6 +50,22 @@ def decode_alg(N, HQK, HV, dk, dv, e):
     return int(bytes_), int(N * HV * 7 * dk * dv), int(N * HV * 2 * dk * dv * 4)
 
 
+def recorded_traffic(kernel: str):
+    """HBM bytes per dispatch measured with rocprofv3 counters (profiles/traffic.json),
+    or None when the kernel's source has changed since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))["kernels"][kernel]
+        src = os.path.join(ROOT, "gated_deltanet_recurrence_rule_amd", "csrc", rec["source"])
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["sha256"]:
+            return None
+        return float(rec["bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,11 +164,11 @@ def main():
         pre_roof = {"bound": "alu", "achieved": pf_rec / (pre_avg * 1e-3) / 1e12,
                     "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s"}
     pre_roof["frac"] = pre_roof["achieved"] / pre_roof["peak"]
-    pre_roof["traffic"] = None
+    pre_roof["traffic"] = recorded_traffic("prefill_chunked") if "chunk" in kname else None
     pre_roof["kernel"] = kname
     dec_gbps = db / (dec_avg * 1e-3) / 1e9
     dec_roof = {"bound": "hbm", "achieved": dec_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": dec_gbps / PEAK_HBM_GBPS, "traffic": None, "kernel": "decode"}
+                "frac": dec_gbps / PEAK_HBM_GBPS, "traffic": recorded_traffic("decode"), "kernel": "decode"}
     pre_hbm_frac = pb / (pre_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS
     value = N * T / (pre_avg * 1e-3) / 1e6
     state_gbps = dstate / (dec_avg * 1e-3) / 1e9
