@@ -19,7 +19,12 @@
 // Only exp(G_i - G_j) <= 1 and exp(G_n - G_i) <= 1 are formed, never 1/gamma.
 // The triangular system is split into two 32-token blocks:
 //   Delta_0 = T_0 Z_0,   Delta_1 = T_1 (Z_1 - A_10 Delta_0),   T_b = (I + A_bb)^{-1},
-// with T_b built in fp32 from 16x16 forward substitutions and one 16-block merge.
+// with T_b built on MFMA by blocked recursion.  If T holds the inverses of the diagonal
+// s x s blocks of a unit lower triangular I + A, and A_s is the part of A coupling the two
+// s-halves of each 2s-block, the inverses of the 2s x 2s blocks are
+//   T - T A_s T   (for two blocks: [[T_a, 0], [-T_b A_ba T_a, T_b]]),
+// applied for s = 1, 2, 4, 8 inside a 16-block (all factors stay as small as T itself);
+// the last step, s = 16, merges the two 16-blocks of a 32-block through W = A_10 T_00.
 //
 // Precision.  MFMA operands are bf16; a value that is not exactly bf16 is either
 // rounded once or carried as hi + lo (hi = bf16(x), lo = bf16(x - hi); two or
@@ -52,6 +57,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int C = 64;       // chunk length
@@ -61,28 +67,28 @@ constexpr int NT = 512;     // threads (8 waves)
 
 constexpr int LK = DK + 8;  // row stride (bf16) of K and Q in LDS
 constexpr int LT = C + 8;   // row stride (bf16) of K^T in LDS
-constexpr int LW = 36;      // row stride (fp32) of the Gram waves' private 32x32 blocks (16-byte rows)
 
-// LDS layout (bytes)
-constexpr int OFF_K = 0;                                   // K  [C][LK] bf16, rows = tokens
-constexpr int OFF_Q = OFF_K + C * LK * 2;                  // Q  [C][LK]
-constexpr int OFF_KT = OFF_Q + C * LK * 2;                 // K^T [2 chunk parity][DK][LT], swizzled
-constexpr int OFF_OPT = OFF_KT + 2 * DK * LT * 2;          // T_b operands [2 b][2 rt][2 hi/lo][64][8]
-constexpr int OFF_OPA = OFF_OPT + 2 * 2 * 2 * 64 * 16;     // -A_10 operands [2 rt][2 hi/lo][64][8]
-constexpr int OFF_OPP = OFF_OPA + 2 * 2 * 64 * 16;         // P operands [6 (rt, ks)][64][8]
-constexpr int OFF_WP = OFF_OPP + 6 * 64 * 16;              // per Gram wave 4,5: Af, Tf [32][LW], Rf [16][17]
-constexpr int WP_SZ = (2 * 32 * LW + 16 * 17) * 4;
+// LDS layout (bytes).  Buffers tagged [2] are selected by chunk parity.
+constexpr int KQ_SZ = 2 * C * LK * 2;                      // K then Q, [C][LK] bf16 each, rows = tokens
+constexpr int OFF_KQ = 0;                                  // [2]
+constexpr int KT_SZ = DK * LT * 2;                         // K^T [DK][LT], swizzled
+constexpr int OFF_KT = OFF_KQ + 2 * KQ_SZ;                 // [2]
+constexpr int OPT_SZ = 2 * 2 * 2 * 64 * 16;                // T_b operands [2 b][2 rt][2 hi/lo][64][8]
+constexpr int OPA_SZ = 2 * 2 * 64 * 16;                    // -A_10 operands [2 rt][2 hi/lo][64][8]
+constexpr int OPP_SZ = 6 * 64 * 16;                        // P operands [6 (rt, ks)][64][8]
+constexpr int OP_SZ = OPT_SZ + OPA_SZ + OPP_SZ;
+constexpr int OFF_OP = OFF_KT + 2 * KT_SZ;                 // [2]
 constexpr int SC_SZ = 6 * C;                               // fp32 per-token scalars of one chunk
-constexpr int OFF_SC = OFF_WP + 2 * WP_SZ;                 // scalars [2 chunk parity][SC_SZ]
-constexpr int OFF_OST = OFF_SC + 2 * SC_SZ * 4;            // per column wave: one 16x16 bf16 output tile
-constexpr int LDS_BYTES = OFF_OST + 4 * 16 * 16 * 2;
+constexpr int OFF_SC = OFF_OP + 2 * OP_SZ;                 // [2]
+constexpr int OFF_FLAG = OFF_SC + 2 * SC_SZ * 4;           // two int hand-over counters
+constexpr int LDS_BYTES = OFF_FLAG + 16;
+// The 16x16 tiles W_b = A_10 T_00 of the two 32-token blocks are handed from one Gram wave
+// to another through the K/Q buffer of the other parity, which nobody reads meanwhile.
+static_assert(2 * 64 * 16 <= KQ_SZ, "hand-over tiles fit in one K/Q buffer");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ bf16x8 to_bf16(f32x8 x) { return __builtin_convertvector(x, bf16x8); }
 __device__ __forceinline__ f32x8 to_f32(bf16x8 x) { return __builtin_convertvector(x, f32x8); }
@@ -92,9 +98,43 @@ __device__ __forceinline__ f32x8 cat(f32x4 a, f32x4 b) {
 __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
+// bf16 pair dot product a.x b.x + a.y b.y + c in one instruction (products are exact in fp32)
+__device__ __forceinline__ float dot2(bf16x2 a, bf16x2 b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+// A packed bf16 pair constant held in a scalar register.  (Written as a vector literal,
+// (-1, 0) is emitted as the inline constant -1.0, which packed bf16 operands read as (0, -1).)
+__device__ __forceinline__ bf16x2 pair_const(uint32_t bits) {
+    uint32_t r;
+    asm volatile("s_mov_b32 %0, %1" : "=s"(r) : "i"(bits));
+    return __builtin_bit_cast(bf16x2, r);
+}
+// hi = bf16(x), lo = bf16(x - hi).  x - hi is exact in fp32; it is formed by a dot product
+// of the packed hi pair with (-1, 0) or (0, -1), which also does the widening of hi.
 __device__ __forceinline__ void split(f32x8 x, bf16x8 &hi, bf16x8 &lo) {
     hi = to_bf16(x);
-    lo = to_bf16(x - to_f32(hi));
+    const bf16x2 m0 = pair_const(0x0000bf80u), m1 = pair_const(0xbf800000u);
+    const bf16x2 hp[4] = {__builtin_shufflevector(hi, hi, 0, 1), __builtin_shufflevector(hi, hi, 2, 3),
+                          __builtin_shufflevector(hi, hi, 4, 5), __builtin_shufflevector(hi, hi, 6, 7)};
+    f32x8 r;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        r[2 * p] = dot2(hp[p], m0, x[2 * p]);
+        r[2 * p + 1] = dot2(hp[p], m1, x[2 * p + 1]);
+    }
+    lo = to_bf16(r);
+}
+__device__ __forceinline__ void split4(f32x4 x, bf16x4 &hi, bf16x4 &lo) {
+    hi = __builtin_convertvector(x, bf16x4);
+    const bf16x2 m0 = pair_const(0x0000bf80u), m1 = pair_const(0xbf800000u);
+    const bf16x2 hp[2] = {__builtin_shufflevector(hi, hi, 0, 1), __builtin_shufflevector(hi, hi, 2, 3)};
+    f32x4 r;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        r[2 * p] = dot2(hp[p], m0, x[2 * p]);
+        r[2 * p + 1] = dot2(hp[p], m1, x[2 * p + 1]);
+    }
+    lo = __builtin_convertvector(r, bf16x4);
 }
 // hi*hi + hi*lo + lo*hi
 __device__ __forceinline__ f32x4 mfma32_x3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, f32x4 c) {
@@ -139,6 +179,18 @@ __device__ __forceinline__ int opaque(int x) {
     return x;
 }
 
+// Global traffic goes through raw buffer accesses: a descriptor over a wave-uniform base
+// (re-based every chunk, so 32-bit offsets suffice), a per-lane byte offset in a VGPR and a
+// per-access uniform byte offset in an SGPR.  The 64-bit address arithmetic then stays out
+// of the vector ALU.  The descriptor's byte range is the chunk's valid rows: accesses past
+// it read zero and write nothing (the kernel predicates them as well).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 // Orders LDS writes before later LDS reads of the same wave (no workgroup barrier).
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -152,22 +204,24 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     const int32_t *__restrict__ cu_seqlens, int64_t eq_len, const float *__restrict__ S0,
     uint16_t *__restrict__ o, float *__restrict__ S_T, int HV, int DV, int rep, float scale) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
-    __bf16 *sK = reinterpret_cast<__bf16 *>(lds + OFF_K);
-    __bf16 *sQ = reinterpret_cast<__bf16 *>(lds + OFF_Q);
-    __bf16 *const sKt0 = reinterpret_cast<__bf16 *>(lds + OFF_KT);
-    bf16x8 *opT = reinterpret_cast<bf16x8 *>(lds + OFF_OPT);  // [((b*2 + rt)*2 + hl)*64 + lane]
-    bf16x8 *opA = reinterpret_cast<bf16x8 *>(lds + OFF_OPA);  // [(rt*2 + hl)*64 + lane]
-    bf16x8 *opP = reinterpret_cast<bf16x8 *>(lds + OFF_OPP);  // [idx*64 + lane]
-    float *const sc0 = reinterpret_cast<float *>(lds + OFF_SC);
-    // Per-token scalars of chunk c live in buffer c % 2 (the next chunk's are written
-    // while the current one is still being read):  G (cumulative log-decay times log2 e),
-    // gamma = exp(G), r_k = 1/|k|, r_q = scale/|q|, beta, r_k exp(G_n - G).
-#define GDN_SCALARS(c)                                         \
-    float *sc_ = sc0 + ((c) & 1) * SC_SZ;                      \
-    float *sG = sc_, *sGam = sc_ + C, *sRk = sc_ + 2 * C;      \
-    float *sRq = sc_ + 3 * C, *sB = sc_ + 4 * C, *sDn = sc_ + 5 * C; \
-    __bf16 *sKt = sKt0 + ((c) & 1) * DK * LT;                  \
-    (void)sG; (void)sGam; (void)sRk; (void)sRq; (void)sB; (void)sDn; (void)sKt;
+    // Everything belonging to chunk c lives in the buffers of parity c % 2: K and Q rows, K^T,
+    // the per-token scalars, and the solve / read operands built from them.  Scalars:
+    // G (cumulative log-decay times log2 e), gamma = exp(G), r_k = 1/|k|, r_q = scale/|q|,
+    // beta, r_k exp(G_n - G).
+#define GDN_CHUNK(c)                                                                        \
+    const int par_ = (c) & 1;                                                               \
+    __bf16 *sK = reinterpret_cast<__bf16 *>(lds + OFF_KQ + par_ * KQ_SZ);                   \
+    __bf16 *sQ = sK + C * LK;                                                               \
+    __bf16 *sKt = reinterpret_cast<__bf16 *>(lds + OFF_KT + par_ * KT_SZ);                  \
+    bf16x8 *opT = reinterpret_cast<bf16x8 *>(lds + OFF_OP + par_ * OP_SZ);                  \
+    bf16x8 *opA = opT + OPT_SZ / 16;                                                        \
+    bf16x8 *opP = opA + OPA_SZ / 16;                                                        \
+    float *sc_ = reinterpret_cast<float *>(lds + OFF_SC) + par_ * SC_SZ;                    \
+    float *sG = sc_, *sGam = sc_ + C, *sRk = sc_ + 2 * C;                                   \
+    float *sRq = sc_ + 3 * C, *sB = sc_ + 4 * C, *sDn = sc_ + 5 * C;                        \
+    (void)sK; (void)sQ; (void)sKt; (void)opT; (void)opA; (void)opP;                         \
+    (void)sG; (void)sGam; (void)sRk; (void)sRq; (void)sB; (void)sDn;
+    // opT [((b*2 + rt)*2 + hl)*64 + lane], opA [(rt*2 + hl)*64 + lane], opP [idx*64 + lane]
 
     const int unit = blockIdx.x;  // n * HV + h
     const int h = unit % HV;
@@ -180,6 +234,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     const int w = tid >> 6;
     const int lr = lane & 15;
     const int lq = lane >> 4;
+    const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index, known to be uniform
     const bool colwave = w < 4;
 
     int64_t t0, t1;
@@ -194,88 +249,107 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     const int nchunks = (int)((t1 - t0 + C - 1) / C);
     auto chunk_len = [&](int c) { return (int)((t1 - t0 - (int64_t)c * C) < C ? (t1 - t0 - (int64_t)c * C) : C); };
 
+    // Schedule.  Phase "a" of chunk c: column waves form K S, Q S and Z of chunk c while
+    // the Gram waves stage chunk c+1 into LDS.  Phase "b" of chunk c: column waves solve,
+    // write the reads and update the table while the Gram waves build T, -A_10 and P of
+    // chunk c+1.  One workgroup barrier closes every phase; a prologue stages chunk 0,
+    // builds its operands (beside the column waves' phase a of chunk 0) and stages chunk 1.
     if (colwave) {
         // ====================== column waves: the table and the per-chunk chain ======
         // Element e of S[dt] is S[16 dt + 4 lq + e][col0 + 16 w + lr].
         f32x4 S[8];
         const size_t tab = (size_t)unit * DK * DV;
         const int mycol = col0 + 16 * w + lr;
-        uint16_t *ost = reinterpret_cast<uint16_t *>(lds + OFF_OST) + w * 256;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 S[dt][e] = S0 ? S0[tab + (size_t)(16 * dt + 4 * lq + e) * DV + mycol] : 0.f;
+        if (nchunks == 0) {
+            if (S_T) {
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) S_T[tab + (size_t)(16 * dt + 4 * lq + e) * DV + mycol] = S[dt][e];
+            }
+            return;
+        }
 
         // v[16 rt + 4 lq + e][mycol] of the next chunk, fetched one chunk ahead
         uint16_t vreg[4][4];
         const size_t vrs = (size_t)HV * DV;  // token stride of v and o
-        const uint16_t *vthr = v + (size_t)h * DV + mycol + (size_t)(4 * lq) * vrs;
+        const uint32_t rowb = 2u * (uint32_t)vrs;  // bytes per token row of v and o
+        const uint16_t *vwave = v + (size_t)h * DV + col0 + 16 * wu;
+        uint16_t *owave = o + (size_t)h * DV + col0 + 16 * wu;
         auto prefetch_v = [&](int c) {
             const int nn = chunk_len(c);
-            const uint16_t *vc = vthr + (size_t)(t0 + (int64_t)c * C) * vrs;
+            const rsrc_t vr = make_rsrc(vwave + (size_t)(t0 + (int64_t)c * C) * vrs, (uint32_t)nn * rowb);
+            const uint32_t off = 2u * (uint32_t)lr + (uint32_t)(4 * lq) * rowb;
             if (nn == C) {
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) vreg[rt][e] = vc[(size_t)(16 * rt + e) * vrs];
+                    for (int e = 0; e < 4; ++e)
+                        vreg[rt][e] = __builtin_amdgcn_raw_buffer_load_b16(vr, off, (uint32_t)(16 * rt + e) * rowb, 0);
             } else {
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        vreg[rt][e] = (16 * rt + 4 * lq + e < nn) ? vc[(size_t)(16 * rt + e) * vrs] : (uint16_t)0;
+                        vreg[rt][e] = (16 * rt + 4 * lq + e < nn)
+                                          ? __builtin_amdgcn_raw_buffer_load_b16(vr, off, (uint32_t)(16 * rt + e) * rowb, 0)
+                                          : (uint16_t)0;
             }
         };
-        // output stores: lane writes row lane/4 of a 16-row tile, columns 4 (lane % 4) .. +3
-        uint16_t *othr = o + (size_t)h * DV + col0 + 16 * w + 4 * (lane & 3) + (size_t)(lane >> 2) * vrs;
-        if (nchunks > 0) {
-            prefetch_v(0);
-            __syncthreads();  // (0) chunk 0's K, Q, K^T and scalars are in LDS
-        }
 
-        for (int c = 0; c < nchunks; ++c) {
+        // Carried from phase a to phase b of a chunk.  Swapping the operands of a product
+        // transposes its accumulator tile: element e of Ot[rt] at this lane is
+        // (Q S)[16 rt + lr][16 w + 4 lq + e].
+        f32x4 Z[4], Ot[4];
+
+        // ---- phase a: Y = K S (hi + lo), Z = beta (v - gamma r_k Y), O^T = S^T Q^T (hi)
+        auto phase_a = [&](int c) {
             const int ln = opaque(lane);
-            const int lrr = ln & 15, lqq = ln >> 4;
-            const int64_t c0 = t0 + (int64_t)c * C;
-            const int n = chunk_len(c);
-            GDN_SCALARS(c)
+            const int lqq = ln >> 4;
+            GDN_CHUNK(c)
             float vcur[4][4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) vcur[rt][e] = bf16_to_f32(vreg[rt][e]);
             if (c + 1 < nchunks) prefetch_v(c + 1);
-
-            // ---- Y = K S (hi + lo), Oacc = Q S (hi), Z = beta (v - gamma r_k Y)
-            f32x4 Z[4], Oacc[4];
-            {
-                bf16x8 Sh[4], Sl[4];
+            bf16x8 Sh[4], Sl[4];
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) split(cat(S[2 * ks], S[2 * ks + 1]), Sh[ks], Sl[ks]);
+            for (int ks = 0; ks < 4; ++ks) split(cat(S[2 * ks], S[2 * ks + 1]), Sh[ks], Sl[ks]);
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    f32x4 y = {0.f, 0.f, 0.f, 0.f}, oa = {0.f, 0.f, 0.f, 0.f};
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4 y = {0.f, 0.f, 0.f, 0.f}, oa = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
-                        const bf16x8 kk = ld_std(sK, LK, 16 * rt, 32 * ks, ln);
-                        const bf16x8 qq = ld_std(sQ, LK, 16 * rt, 32 * ks, ln);
-                        y = mfma32(kk, Sh[ks], y);
-                        y = mfma32(kk, Sl[ks], y);
-                        oa = mfma32(qq, Sh[ks], oa);
-                    }
-                    const int i0 = 16 * rt + 4 * lqq;
-                    const f32x4 b4 = *reinterpret_cast<const f32x4 *>(sB + i0);
-                    const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sGam + i0);
-                    const f32x4 k4 = *reinterpret_cast<const f32x4 *>(sRk + i0);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) Z[rt][e] = b4[e] * (vcur[rt][e] - g4[e] * k4[e] * y[e]);
-                    Oacc[rt] = oa;
+                for (int ks = 0; ks < 4; ++ks) {
+                    const bf16x8 kk = ld_std(sK, LK, 16 * rt, 32 * ks, ln);
+                    const bf16x8 qq = ld_std(sQ, LK, 16 * rt, 32 * ks, ln);
+                    y = mfma32(kk, Sh[ks], y);
+                    y = mfma32(kk, Sl[ks], y);
+                    oa = mfma32(Sh[ks], qq, oa);
                 }
+                const int i0 = 16 * rt + 4 * lqq;
+                const f32x4 b4 = *reinterpret_cast<const f32x4 *>(sB + i0);
+                const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sGam + i0);
+                const f32x4 k4 = *reinterpret_cast<const f32x4 *>(sRk + i0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Z[rt][e] = b4[e] * (vcur[rt][e] - g4[e] * k4[e] * y[e]);
+                Ot[rt] = oa;
             }
-            __syncthreads();  // (A) P, -A_10, T_0, T_1 and r_k exp(G_n - G) of chunk c are in LDS
+        };
 
-            // ---- Delta_0 = T_0 Z_0;  Delta_1 = T_1 (Z_1 - A_10 Delta_0)
+        // ---- phase b: solve, reads, table update
+        auto phase_b = [&](int c) {
+            const int ln = opaque(lane);
+            const int lrr = ln & 15, lqq = ln >> 4;
+            const int64_t c0 = t0 + (int64_t)c * C;
+            const int n = chunk_len(c);
+            GDN_CHUNK(c)
+            // Delta_0 = T_0 Z_0;  Delta_1 = T_1 (Z_1 - A_10 Delta_0)
             f32x4 Dl[4];
             {
                 bf16x8 zh, zl;
@@ -300,34 +374,28 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                                            rh, rl, zero);
                 }
             }
-            // ---- O = gamma r_q (Q S) + P Delta
+            // O^T = gamma r_q (Q S)^T + (P Delta)^T: token 16 rt + lr, 4 adjacent columns per lane
             {
                 bf16x8 Dsg[2];
                 Dsg[0] = to_bf16(cat(Dl[0], Dl[1]));
                 Dsg[1] = to_bf16(cat(Dl[2], Dl[3]));
+                const rsrc_t orr = make_rsrc(owave + (size_t)c0 * vrs, (uint32_t)n * rowb);
+                const uint32_t ooff = (uint32_t)lrr * rowb + 8u * (uint32_t)lqq;
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
                     f32x4 pd = {0.f, 0.f, 0.f, 0.f};
                     const int base = rt == 0 ? 0 : (rt == 1 ? 1 : (rt == 2 ? 2 : 4));
 #pragma unroll
-                    for (int ks = 0; ks <= (rt >> 1); ++ks) pd = mfma32(opP[(base + ks) * 64 + ln], Dsg[ks], pd);
-                    const int i0 = 16 * rt + 4 * lqq;
-                    const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sGam + i0);
-                    const f32x4 q4 = *reinterpret_cast<const f32x4 *>(sRq + i0);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        ost[(4 * lqq + e) * 16 + lrr] = __builtin_bit_cast(uint16_t, (__bf16)(g4[e] * q4[e] * Oacc[rt][e] + pd[e]));
-                    wave_lds_sync();
-                    {
-                        const int r = ln >> 2, cq = ln & 3;
-                        const uint2 val = *reinterpret_cast<const uint2 *>(ost + r * 16 + 4 * cq);
-                        if (16 * rt + r < n)
-                            *reinterpret_cast<uint2 *>(othr + (size_t)(c0 + 16 * rt) * vrs) = val;
-                    }
-                    wave_lds_sync();
+                    for (int ks = 0; ks <= (rt >> 1); ++ks) pd = mfma32(Dsg[ks], opP[(base + ks) * 64 + ln], pd);
+                    const int i = 16 * rt + lrr;
+                    const float gq = sGam[i] * sRq[i];
+                    const bf16x4 ob = __builtin_convertvector(gq * Ot[rt] + pd, bf16x4);
+                    if (i < n)
+                        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob), orr, ooff,
+                                                              (uint32_t)(16 * rt) * rowb, 0);
                 }
             }
-            // ---- S <- gamma_n S + K^T D,  D = diag(r_k exp(G_n - G)) Delta
+            // S <- gamma_n S + K^T D,  D = diag(r_k exp(G_n - G)) Delta
             {
                 bf16x8 Dh[2], Dlo[2];
 #pragma unroll
@@ -356,7 +424,18 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                     S[dt] = acc;
                 }
             }
-            __syncthreads();  // (B) chunk c+1's K, Q, K^T and scalars are in LDS
+        };
+
+        prefetch_v(0);
+        __syncthreads();  // chunk 0 staged
+        phase_a(0);
+        __syncthreads();  // operands of chunk 0 built
+        __syncthreads();  // chunk 1 staged
+        for (int c = 0; c < nchunks; ++c) {
+            phase_b(c);
+            __syncthreads();
+            if (c + 1 < nchunks) phase_a(c + 1);
+            __syncthreads();
         }
         if (S_T) {
 #pragma unroll
@@ -366,31 +445,36 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         }
         return;
     }
+    if (nchunks == 0) return;
 
     // ====================== Gram waves: chunk staging, norms, decay, P, A, T =====
     const int gt = tid - 256;  // 0..255
     const int gw = w - 4;      // 0..3
     // Staging: item gt + 256 p (p = 0, 1) is the token pair (2 pr, 2 pr + 1), pr = gt/16 + 16 p,
     // times the 16-byte segment s = gt % 16 of their q and k rows (d = 8 s .. 8 s + 7).
-    const int seg_s = gt & 15;
     uint4 kreg[2][2], qreg[2][2];  // [p][token of the pair]
     float greg = 0.f, breg = 0.f;  // Gram wave 3: token = lane
     const size_t rs = (size_t)HQK * DK;  // token stride of q and k
-    const size_t thr_off = (size_t)hq * DK + 8 * seg_s + (size_t)(2 * (gt >> 4)) * rs;
-    const uint16_t *kthr = k + thr_off;
-    const uint16_t *qthr = q + thr_off;
+    // token row of item (p, u) = 8 gw + 32 p + u (uniform) + 2 lq (lane)
+    const int gwu = wu - 4;
+    const uint32_t qkrow = 2u * (uint32_t)rs;  // bytes per token row of q and k
     auto prefetch_qk = [&](int c) {
         const int nn = chunk_len(c);
         const int64_t cs = t0 + (int64_t)c * C;
-        const uint16_t *kc = kthr + (size_t)cs * rs;
-        const uint16_t *qc = qthr + (size_t)cs * rs;
+        const rsrc_t kr = make_rsrc(k + (size_t)cs * rs + (size_t)hq * DK, (uint32_t)nn * qkrow);
+        const rsrc_t qr = make_rsrc(q + (size_t)cs * rs + (size_t)hq * DK, (uint32_t)nn * qkrow);
+        const uint32_t off = (uint32_t)(2 * lq) * qkrow + 16u * (uint32_t)lr;
+        auto ld = [&](const rsrc_t &r, int p, int u) {
+            return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 r, off, (uint32_t)(8 * gwu + 32 * p + u) * qkrow, 0));
+        };
         if (nn == C) {
 #pragma unroll
             for (int p = 0; p < 2; ++p)
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    kreg[p][u] = *reinterpret_cast<const uint4 *>(kc + (size_t)(32 * p + u) * rs);
-                    qreg[p][u] = *reinterpret_cast<const uint4 *>(qc + (size_t)(32 * p + u) * rs);
+                    kreg[p][u] = ld(kr, p, u);
+                    qreg[p][u] = ld(qr, p, u);
                 }
         } else {
 #pragma unroll
@@ -401,22 +485,25 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                     kreg[p][u] = make_uint4(0, 0, 0, 0);
                     qreg[p][u] = make_uint4(0, 0, 0, 0);
                     if (r < nn) {
-                        kreg[p][u] = *reinterpret_cast<const uint4 *>(kc + (size_t)(32 * p + u) * rs);
-                        qreg[p][u] = *reinterpret_cast<const uint4 *>(qc + (size_t)(32 * p + u) * rs);
+                        kreg[p][u] = ld(kr, p, u);
+                        qreg[p][u] = ld(qr, p, u);
                     }
                 }
         }
-        if (gw == 3) {
+        if (gwu == 3) {
             const bool ok = lane < nn;
-            greg = ok ? g[(size_t)(cs + lane) * HV + h] : 0.f;
-            breg = ok ? beta[(size_t)(cs + lane) * HV + h] : 0.f;
+            const uint32_t goff = 4u * (uint32_t)lane * (uint32_t)HV;
+            const uint32_t gbytes = 4u * (uint32_t)nn * (uint32_t)HV;
+            const rsrc_t gr = make_rsrc(g + (size_t)cs * HV + h, gbytes);
+            const rsrc_t br = make_rsrc(beta + (size_t)cs * HV + h, gbytes);
+            greg = ok ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gr, goff, 0, 0)) : 0.f;
+            breg = ok ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(br, goff, 0, 0)) : 0.f;
         }
     };
-    if (nchunks > 0) prefetch_qk(0);
 
     // chunk c's q, k, g, beta (already in registers) -> LDS, norms, cumulative decay
     auto stage_chunk = [&](int c) {
-        GDN_SCALARS(c)
+        GDN_CHUNK(c)
         const int ln = opaque(lane);
         const int gtt = opaque(gt);
         const int sgs = gtt & 15;
@@ -439,10 +526,9 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                 float a = 0.f, bq = 0.f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float k0 = __uint_as_float(kw[e] << 16), k1 = __uint_as_float(kw[e] & 0xffff0000u);
-                    const float q0 = __uint_as_float(qw[e] << 16), q1 = __uint_as_float(qw[e] & 0xffff0000u);
-                    a += k0 * k0 + k1 * k1;
-                    bq += q0 * q0 + q1 * q1;
+                    const bf16x2 k2 = __builtin_bit_cast(bf16x2, kw[e]), q2 = __builtin_bit_cast(bf16x2, qw[e]);
+                    a = dot2(k2, k2, a);
+                    bq = dot2(q2, q2, bq);
                 }
                 sk[u] = a;
                 sq[u] = bq;
@@ -454,9 +540,9 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int d = 8 * sgs + e;
-                const uint32_t lo = (e & 1) ? (k0w[e >> 1] >> 16) : (k0w[e >> 1] & 0xffffu);
-                const uint32_t hi = (e & 1) ? (k1w[e >> 1] & 0xffff0000u) : (k1w[e >> 1] << 16);
-                *reinterpret_cast<uint32_t *>(sKt + d * LT + kt_col(d, tp)) = lo | hi;
+                // low half: element e of token 2 pr, high half: element e of token 2 pr + 1
+                const uint32_t pair = __builtin_amdgcn_perm(k1w[e >> 1], k0w[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+                *reinterpret_cast<uint32_t *>(sKt + d * LT + kt_col(d, tp)) = pair;
             }
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -471,211 +557,257 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             }
         }
         if (gw == 3) {
+            // inclusive prefix sum over the 64 lanes: within rows of 16 by row shifts, then
+            // across rows by the row-15 and row-31 broadcasts (DPP, no LDS traffic)
             float x = greg * 1.44269504088896341f;  // log2(e)
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off, 64);
-                if (ln >= off) x += y;
-            }
+#define GDN_DPP_ADD(ctrl, row_mask) \
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, row_mask, 0xF, true))
+            GDN_DPP_ADD(0x111, 0xF);  // row_shr:1
+            GDN_DPP_ADD(0x112, 0xF);  // row_shr:2
+            GDN_DPP_ADD(0x114, 0xF);  // row_shr:4
+            GDN_DPP_ADD(0x118, 0xF);  // row_shr:8
+            GDN_DPP_ADD(0x142, 0xA);  // row_bcast:15 into rows 1 and 3
+            GDN_DPP_ADD(0x143, 0xC);  // row_bcast:31 into rows 2 and 3
+#undef GDN_DPP_ADD
             sG[ln] = x;
             sGam[ln] = exp2_hw(x);
             sB[ln] = breg;
         }
     };
 
-    if (nchunks > 0) {
-        stage_chunk(0);
-        if (nchunks > 1) prefetch_qk(1);
-        __syncthreads();  // (0)
-    }
-    for (int c = 0; c < nchunks; ++c) {
+    // T_0, T_1, -A_10, P and r_k exp(G_n - G) of chunk c, from its staged K, Q and scalars.
+    //
+    // Gram wave gw owns diagonal 16-block gw.  Its matrices live in MFMA accumulator form:
+    // element e at lane (g = lane/16, j = lane%16) is M[4 g + e][j].  With Y and X in that
+    // form, Y^T X needs no data movement (lane group g and element e enumerate the contracted
+    // index on both sides), so every product below keeps a matrix and its transpose.
+    // Waves 0 and 2 also form W = A_10 T_00 of their 32-block and hand it to waves 1 and 3,
+    // which finish the block.  The hand-over counter holds the last chunk whose W is in LDS.
+    int *flag = reinterpret_cast<int *>(lds + OFF_FLAG);
+    auto build_operands = [&](int c) {
         const int ln = opaque(lane);
         const int lrr = ln & 15, lqq = ln >> 4;
-        GDN_SCALARS(c)
-
-        if (gw < 2) {
-            // ---- T_b = (I + A_bb)^{-1} for the 32-token block b = gw
-            const int b = gw;
-            float *Af = reinterpret_cast<float *>(lds + OFF_WP + b * WP_SZ);
-            float *Tf = Af + 32 * LW;
-            float *Rf = Tf + 32 * LW;
-            bf16x8 ka[4], kb[4];
+        GDN_CHUNK(c)
+        f32x4 *Wbuf = reinterpret_cast<f32x4 *>(lds + OFF_KQ + (par_ ^ 1) * KQ_SZ);  // [2 b][64]
+        const int blk = gwu;
+        const int b = gwu >> 1;
+        const bool first = (gwu & 1) == 0;
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        auto load_blk = [&](const __bf16 *base, int kb, bf16x8 *dst) {
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                ka[ks] = ld_std(sK, LK, 32 * b, 32 * ks, ln);
-                kb[ks] = ld_std(sK, LK, 32 * b + 16, 32 * ks, ln);
-            }
-            f32x4 g00 = {0.f, 0.f, 0.f, 0.f}, g10 = g00, g11 = g00;
+            for (int ks = 0; ks < 4; ++ks) dst[ks] = ld_std(base, LK, 16 * kb, 32 * ks, ln);
+        };
+        // P operand idx = (rt, ks), ks <= rt / 2:  0 (0,0) 1 (1,0) 2 (2,0) 3 (2,1) 4 (3,0) 5 (3,1).
+        // Tile (rt, kt) from MFMA(K block kt, Q block rt): element e at lane is
+        // (Q K^T)[16 rt + lr][16 kt + 4 lq + e], the tile-order operand slot.
+        auto p_operand = [&](int idx) {
+            const int rt = idx == 0 ? 0 : (idx == 1 ? 1 : (idx < 4 ? 2 : 3));
+            const int ks = (idx == 3 || idx == 5) ? 1 : 0;
+            const int i = 16 * rt + lrr;
+            const float ci = sRq[i], Gi = sG[i];
+            bf16x8 qq[4];
+            load_blk(sQ, rt, qq);
+            f32x8 x;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                g00 = mfma32(ka[ks], ka[ks], g00);
-                g10 = mfma32(kb[ks], ka[ks], g10);
-                g11 = mfma32(kb[ks], kb[ks], g11);
+            for (int t = 0; t < 2; ++t) {
+                const int kt = 2 * ks + t;
+                if (kt > rt) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[4 * t + e] = 0.f;
+                    continue;
+                }
+                bf16x8 kk[4];
+                load_blk(sK, kt, kk);
+                f32x4 acc = zero;
+#pragma unroll
+                for (int kq = 0; kq < 4; ++kq) acc = mfma32(kk[kq], qq[kq], acc);
+                const int j0 = 16 * kt + 4 * lqq;
+                const f32x4 G4 = *reinterpret_cast<const f32x4 *>(sG + j0);
+                const f32x4 R4 = *reinterpret_cast<const f32x4 *>(sRk + j0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    x[4 * t + e] = (j0 + e <= i) ? ci * R4[e] * acc[e] * exp2_hw(Gi - G4[e]) : 0.f;
             }
-            // A values of local tile (li, lj): element e at local (16 li + 4 lq + e, 16 lj + lr)
-            auto put_a = [&](const f32x4 &acc, int li, int lj) {
-                const int j = 32 * b + 16 * lj + lrr;
-                const float Gj = sG[j], rkj = sRk[j];
-                const int i0 = 32 * b + 16 * li + 4 * lqq;
-                const f32x4 G4 = *reinterpret_cast<const f32x4 *>(sG + i0);
-                const f32x4 B4 = *reinterpret_cast<const f32x4 *>(sB + i0);
-                const f32x4 R4 = *reinterpret_cast<const f32x4 *>(sRk + i0);
+            opP[idx * 64 + ln] = to_bf16(x);
+        };
+        // -A_10 (rows 32 + 16 rt .., columns 0..31) in tile order, from role-swapped Gram tiles
+        auto a_operand = [&](int rt) {
+            const int i = 32 + 16 * rt + lrr;
+            const float ci = sB[i] * sRk[i], Gi = sG[i];
+            bf16x8 kr[4];
+            load_blk(sK, 2 + rt, kr);
+            f32x8 x;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                bf16x8 kk[4];
+                load_blk(sK, t, kk);
+                f32x4 acc = zero;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) acc = mfma32(kk[ks], kr[ks], acc);
+                const int j0 = 16 * t + 4 * lqq;
+                const f32x4 G4 = *reinterpret_cast<const f32x4 *>(sG + j0);
+                const f32x4 R4 = *reinterpret_cast<const f32x4 *>(sRk + j0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[4 * t + e] = -ci * R4[e] * acc[e] * exp2_hw(Gi - G4[e]);
+            }
+            bf16x8 hi, lo;
+            split(x, hi, lo);
+            opA[(rt * 2 + 0) * 64 + ln] = hi;
+            opA[(rt * 2 + 1) * 64 + ln] = lo;
+        };
+        // Products on bf16 MFMA with hi/lo operands.  Y and X in accumulator form split into
+        // bf16 (hi, lo); one 16x16x32 MFMA with A = (Yh, Yh) and B = (Xh, Xl) gives
+        // Yh^T Xh + Yh^T Xl, a second with A = (Yl, 0) adds Yl^T Xh.
+        auto hl = [&](const f32x4 &x, bf16x4 &h, bf16x4 &l) { split4(x, h, l); };
+        auto prod3 = [&](const bf16x4 &yh, const bf16x4 &yl, const bf16x4 &xh, const bf16x4 &xl, f32x4 acc) {
+            const bf16x4 z4 = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+            const bf16x8 bx = cat(xh, xl);
+            acc = mfma32(cat(yh, yh), bx, acc);
+            return mfma32(cat(yl, z4), bx, acc);
+        };
+        // Inverse T of the diagonal 16-block and its transpose, as accumulator tiles.
+        auto invert_block = [&](f32x4 &T, f32x4 &Tt, bf16x8 *kd) {
+            load_blk(sK, blk, kd);
+            f32x4 gd = zero;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) gd = mfma32(kd[ks], kd[ks], gd);
+            // A and A^T from the symmetric Gram tile: element e is local row i = 4 lq + e,
+            // column j = lr; exactly one of A[i][j], A[j][i] is nonzero off the diagonal.
+            const int i0 = 16 * blk + 4 * lqq;
+            const int jj = 16 * blk + lrr;
+            const f32x4 G4 = *reinterpret_cast<const f32x4 *>(sG + i0);
+            const f32x4 B4 = *reinterpret_cast<const f32x4 *>(sB + i0);
+            const f32x4 R4 = *reinterpret_cast<const f32x4 *>(sRk + i0);
+            const float Gj = sG[jj], Bj = sB[jj], Rj = sRk[jj];
+            f32x4 Am;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * lqq + e, j = lrr;
+                const float d = G4[e] - Gj;
+                const float f = R4[e] * Rj * gd[e] * exp2_hw(j < i ? d : -d);
+                Am[e] = j < i ? B4[e] * f : 0.f;
+                const float amt = j > i ? Bj * f : 0.f;  // A[j][i]
+                // s = 1: 2x2 blocks [[1, 0], [-a, 1]]
+                T[e] = (i == j) ? 1.f : (((i ^ j) == 1) ? -Am[e] : 0.f);
+                Tt[e] = (i == j) ? 1.f : (((i ^ j) == 1) ? -amt : 0.f);
+            }
+#pragma unroll
+            for (int sl = 2; sl <= 8; sl <<= 1) {
+                f32x4 Ao;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float a = (j < i0 + e) ? B4[e] * R4[e] * rkj * acc[e] * exp2_hw(G4[e] - Gj) : 0.f;
-                    Af[(16 * li + 4 * lqq + e) * LW + 16 * lj + lrr] = a;
+                    const int x = (4 * lqq + e) ^ lrr;
+                    Ao[e] = (x >= sl && x < 2 * sl) ? Am[e] : 0.f;
                 }
-            };
-            put_a(g00, 0, 0);
-            put_a(g10, 1, 0);
-            put_a(g11, 1, 1);
-            wave_lds_sync();
-            // 16x16 diagonal inverses by forward substitution, one column per lane
-            // (lane = (block, column cc)); row i of A is read as four 16-byte broadcasts.
-            {
-                const int blk = (ln >> 4) & 1, cc = ln & 15;
-                const float *Ab = Af + (16 * blk) * LW + 16 * blk;
-                float x[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) x[i] = (i == cc) ? 1.f : 0.f;
-#pragma unroll
-                for (int i = 1; i < 16; ++i) {
-                    const f32x4 *row = reinterpret_cast<const f32x4 *>(Ab + i * LW);
-                    float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        if (4 * q4 >= i) break;
-                        const f32x4 a4 = row[q4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (4 * q4 + e < i) part[e] += a4[e] * x[4 * q4 + e];
-                    }
-                    const float sum = (part[0] + part[1]) + (part[2] + part[3]);
-                    if (i > cc) x[i] = -sum;
-                }
-                if (ln < 32) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) Tf[(16 * blk + i) * LW + 16 * blk + cc] = x[i];
-                } else {
-                    // the upper 16x16 block of T_b is zero
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) Tf[(8 * ((ln - 32) >> 4) + i) * LW + 16 + (ln & 15)] = 0.f;
-                }
+                bf16x4 aoh, aol, tth, ttl, th, tl, uh, ul;
+                hl(Ao, aoh, aol);
+                hl(Tt, tth, ttl);
+                hl(T, th, tl);
+                const f32x4 Ut = prod3(aoh, aol, tth, ttl, zero);  // (T A_s)^T
+                hl(Ut, uh, ul);
+                T = T - prod3(uh, ul, th, tl, zero);    // T - (T A_s) T
+                Tt = Tt - prod3(th, tl, uh, ul, zero);  // its transpose
             }
-            wave_lds_sync();
-            // merge: T_10 = -T_11 (A_10 T_00), fp32 MFMA
+        };
+        // Row tile rt of T_b as a tile-order (hi, lo) operand: 8 values at lane (g, i) are
+        // T_b[16 rt + i][4 g + e] (first 16 columns) and T_b[16 rt + i][16 + 4 g + e].
+        auto put_t = [&](int rt, const f32x4 &left_t, const f32x4 &right_t) {
+            bf16x8 hi, lo;
+            split(cat(left_t, right_t), hi, lo);
+            opT[((2 * b + rt) * 2 + 0) * 64 + ln] = hi;
+            opT[((2 * b + rt) * 2 + 1) * 64 + ln] = lo;
+        };
+
+        if (first) {
+            __builtin_amdgcn_s_setprio(2);
+            f32x4 T, Tt;
+            bf16x8 kd[4];
+            invert_block(T, Tt, kd);
+            put_t(0, Tt, zero);
+            // W = A_10 T_00 = (A_10^T)^T T_00.  A_10^T from the role-swapped Gram tile of
+            // blocks (blk, blk + 1): element e is A[16 (blk+1) + lr][16 blk + 4 lq + e].
             {
-                f32x4 r = {0.f, 0.f, 0.f, 0.f};
+                bf16x8 kn[4];
+                load_blk(sK, blk + 1, kn);
+                f32x4 gx = zero;
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    r = mfma_f32(Af[(16 + lrr) * LW + 4 * kk + lqq], Tf[(4 * kk + lqq) * LW + lrr], r);
+                for (int ks = 0; ks < 4; ++ks) gx = mfma32(kd[ks], kn[ks], gx);
+                const int i0 = 16 * blk + 4 * lqq;
+                const int r = 16 * (blk + 1) + lrr;
+                const f32x4 G4 = *reinterpret_cast<const f32x4 *>(sG + i0);
+                const f32x4 R4 = *reinterpret_cast<const f32x4 *>(sRk + i0);
+                const float cr = sB[r] * sRk[r], Gr = sG[r];
+                f32x4 At;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) Rf[(4 * lqq + e) * 17 + lrr] = r[e];
-                wave_lds_sync();
-                f32x4 t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    t = mfma_f32(Tf[(16 + lrr) * LW + 16 + 4 * kk + lqq], Rf[(4 * kk + lqq) * 17 + lrr], t);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) Tf[(16 + 4 * lqq + e) * LW + lrr] = -t[e];
+                for (int e = 0; e < 4; ++e) At[e] = cr * R4[e] * gx[e] * exp2_hw(Gr - G4[e]);
+                bf16x4 ah, al, th, tl;
+                hl(At, ah, al);
+                hl(T, th, tl);
+                Wbuf[b * 64 + ln] = prod3(ah, al, th, tl, zero);
+                __hip_atomic_store(flag + b, c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
-            wave_lds_sync();
-            // T_b -> tile-order operands (hi, lo) for row tiles rt = 0, 1
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const f32x4 *row = reinterpret_cast<const f32x4 *>(Tf + (16 * rt + lrr) * LW + 4 * lqq);
-                const f32x4 x0 = row[0], x1 = row[4];
-                bf16x8 hi, lo;
-                split(cat(x0, x1), hi, lo);
-                opT[((2 * b + rt) * 2 + 0) * 64 + ln] = hi;
-                opT[((2 * b + rt) * 2 + 1) * 64 + ln] = lo;
+            __builtin_amdgcn_s_setprio(0);
+            if (b == 0) {
+                p_operand(0);
+                p_operand(1);
+            } else {
+                p_operand(3);
+                p_operand(4);
             }
         } else {
-            // K blocks as the first (role-swapped) operand of every tile below
-            bf16x8 kk[4][4];
-#pragma unroll
-            for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) kk[blk][ks] = ld_std(sK, LK, 16 * blk, 32 * ks, ln);
-            // P operand idx = (rt, ks), ks <= rt / 2:  0 (0,0) 1 (1,0) 2 (2,0) 3 (2,1) 4 (3,0) 5 (3,1).
-            // Tile (rt, kt) from MFMA(K block kt, Q block rt): element e at lane is
-            // (Q K^T)[16 rt + lr][16 kt + 4 lq + e], the tile-order operand slot.
-            auto p_operand = [&](int idx, const bf16x8 *qq) {
-                const int rt = idx == 0 ? 0 : (idx == 1 ? 1 : (idx < 4 ? 2 : 3));
-                const int ks = (idx == 3 || idx == 5) ? 1 : 0;
-                const int i = 16 * rt + lrr;
-                const float ci = sRq[i], Gi = sG[i];
-                f32x8 x;
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int kt = 2 * ks + t;
-                    if (kt > rt) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) x[4 * t + e] = 0.f;
-                        continue;
-                    }
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kq = 0; kq < 4; ++kq) acc = mfma32(kk[kt][kq], qq[kq], acc);
-                    const int j0 = 16 * kt + 4 * lqq;
-                    const f32x4 G4 = *reinterpret_cast<const f32x4 *>(sG + j0);
-                    const f32x4 R4 = *reinterpret_cast<const f32x4 *>(sRk + j0);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        x[4 * t + e] = (j0 + e <= i) ? ci * R4[e] * acc[e] * exp2_hw(Gi - G4[e]) : 0.f;
-                }
-                opP[idx * 64 + ln] = to_bf16(x);
-            };
-            bf16x8 qq[4];
-            auto load_q = [&](int rt) {
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) qq[ks] = ld_std(sQ, LK, 16 * rt, 32 * ks, ln);
-            };
-            if (gw == 2) {
-                // -A_10 (rows 32..63, columns 0..31) in tile order, from role-swapped Gram tiles
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
-                    const int i = 32 + 16 * rt + lrr;
-                    const float ci = sB[i] * sRk[i], Gi = sG[i];
-                    f32x8 x;
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int ks = 0; ks < 4; ++ks) acc = mfma32(kk[t][ks], kk[2 + rt][ks], acc);
-                        const int j0 = 16 * t + 4 * lqq;
-                        const f32x4 G4 = *reinterpret_cast<const f32x4 *>(sG + j0);
-                        const f32x4 R4 = *reinterpret_cast<const f32x4 *>(sRk + j0);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) x[4 * t + e] = -ci * R4[e] * acc[e] * exp2_hw(Gi - G4[e]);
-                    }
-                    bf16x8 hi, lo;
-                    split(x, hi, lo);
-                    opA[(rt * 2 + 0) * 64 + ln] = hi;
-                    opA[(rt * 2 + 1) * 64 + ln] = lo;
-                }
+            if (b == 0) {
+                p_operand(2);
+                a_operand(0);
                 sDn[ln] = sRk[ln] * exp2_hw(sG[C - 1] - sG[ln]);
-                load_q(0);
-                p_operand(0, qq);
-                load_q(1);
-                p_operand(1, qq);
-                load_q(2);
-                p_operand(2, qq);
             } else {
-                load_q(2);
-                p_operand(3, qq);
-                load_q(3);
-                p_operand(4, qq);
-                p_operand(5, qq);
+                p_operand(5);
+                a_operand(1);
             }
+            __builtin_amdgcn_s_setprio(2);
+            f32x4 T, Tt;
+            bf16x8 kd[4];
+            invert_block(T, Tt, kd);
+            // wait for W of this chunk (bounded: the partner wave writes it unconditionally)
+            for (int spin = 0; spin < (1 << 22); ++spin) {
+                if (__hip_atomic_load(flag + b, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) > c) break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+            const f32x4 W = Wbuf[b * 64 + ln];
+            // T_10^T = -(T_11 W)^T = -W^T T_11^T
+            bf16x4 wh, wl, th, tl;
+            hl(W, wh, wl);
+            hl(Tt, th, tl);
+            const f32x4 T10t = -prod3(wh, wl, th, tl, zero);
+            put_t(1, T10t, Tt);
+            __builtin_amdgcn_s_setprio(0);
         }
-        __syncthreads();  // (A)
-        if (c + 1 < nchunks) {
-            stage_chunk(c + 1);
-            if (c + 2 < nchunks) prefetch_qk(c + 2);
-        }
-        __syncthreads();  // (B)
+    };
+
+    if (gt == 0) {
+        flag[0] = 0;
+        flag[1] = 0;
     }
+    prefetch_qk(0);
+    stage_chunk(0);
+    if (nchunks > 1) prefetch_qk(1);
+    __syncthreads();  // chunk 0 staged
+    build_operands(0);
+    __syncthreads();  // operands of chunk 0 built
+    if (nchunks > 1) {
+        stage_chunk(1);
+        if (nchunks > 2) prefetch_qk(2);
+    }
+    __syncthreads();  // chunk 1 staged
+    for (int c = 0; c < nchunks; ++c) {
+        if (c + 1 < nchunks) build_operands(c + 1);
+        __syncthreads();
+        if (c + 2 < nchunks) {
+            stage_chunk(c + 2);
+            if (c + 3 < nchunks) prefetch_qk(c + 3);
+        }
+        __syncthreads();
+    }
+#undef GDN_CHUNK
 }
 
 }  // namespace
