@@ -115,7 +115,7 @@ def main():
     torch.cuda.synchronize()
 
     def prefill():
-        binding.prefill(P["q"], P["k"], P["v"], P["g"], P["beta"], cu_seqlens=P["cu"],
+        binding.prefill(P["q"], P["k"], P["v"], P["g"], P["beta"], cu_seqlens=P["cu"], cu_seqlens_host=pf.cu_seqlens,
                         S0=P["S0"], o=o_p, S_T=S_T, workspace=ws)
 
     def decode():

@@ -89,8 +89,10 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const fl
 
 size_t gdn_prefill_workspace_size(int32_t N, int64_t total_T, int32_t HQK, int32_t HV,
                                   int32_t dk, int32_t dv, gdn_dtype dtype) {
-    (void)N; (void)total_T; (void)HQK; (void)HV; (void)dk; (void)dv; (void)dtype;
-    return 0;
+    (void)total_T; (void)HQK; (void)HV; (void)dk; (void)dv; (void)dtype;
+    // the longest-first launch order: one int32 per sequence, rounded to 256 bytes
+    if (N <= 1 || N > gdn::kMaxOrderedSequences) return 0;
+    return ((size_t)N * 4 + 255) / 256 * 256;
 }
 
 gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float *g,
@@ -136,7 +138,24 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
     if (workspace && !aligned(workspace, 16)) return fail(GDN_ERR_ALIGN, "workspace must be 16-byte aligned");
     if (N == 0) return GDN_OK;
 
-    gdn::PrefillArgs a{q, k, v, g, beta, cu_seqlens, eq_len, N, total_T, S0, o, S_T,
+    // Launch order: longest sequences first.  Equal lengths (cu_seqlens NULL) and host
+    // lengths that are already non-increasing keep the given order.
+    const int32_t *order = nullptr;
+    if (cu_seqlens && need > 0) {
+        bool sorted = false;
+        if (cu_seqlens_host) {
+            sorted = true;
+            for (int32_t i = 1; i < N && sorted; ++i)
+                sorted = cu_seqlens_host[i + 1] - cu_seqlens_host[i] <= cu_seqlens_host[i] - cu_seqlens_host[i - 1];
+        }
+        if (!sorted) {
+            int32_t *ord = static_cast<int32_t *>(workspace);
+            gdn_status s2 = hip_status(gdn::launch_longest_first(cu_seqlens, N, ord, stream), "order launch");
+            if (s2 != GDN_OK) return s2;
+            order = ord;
+        }
+    }
+    gdn::PrefillArgs a{q, k, v, g, beta, cu_seqlens, order, eq_len, N, total_T, S0, o, S_T,
                        HQK, HV, dk, dv, scale, workspace, workspace_bytes};
     const bool bf16 = dtype == GDN_BF16;
     if (gdn::prefill_chunked_supported(dk, dv, bf16))

@@ -20,6 +20,7 @@ struct PrefillArgs {
     const void *q, *k, *v;
     const float *g, *beta;
     const int32_t *cu_seqlens;  // device, or nullptr => equal lengths eq_len
+    const int32_t *order;       // device: sequence of each launch rank, or nullptr => identity
     int64_t eq_len;
     int32_t N;
     int64_t total_T;
@@ -35,6 +36,11 @@ struct PrefillArgs {
 // Each returns hipSuccess or the launch error.  `bf16` selects the I/O type.
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t stream);
 hipError_t launch_prefill_recurrent(const PrefillArgs &a, bool bf16, hipStream_t stream);
+
+// Longest-first order of the N sequences of cu_seqlens (device) into order[N] (device).
+hipError_t launch_longest_first(const int32_t *cu_seqlens, int32_t N, int32_t *order, hipStream_t stream);
+// Sequences whose order costs O(N^2) work at most this large are reordered.
+constexpr int32_t kMaxOrderedSequences = 16384;
 
 // Chunked MFMA prefill: bf16 I/O, dk = 128, dv a multiple of 64.
 bool prefill_chunked_supported(int dk, int dv, bool bf16);

@@ -201,8 +201,9 @@ __device__ __forceinline__ void wave_lds_sync() {
 __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
-    const int32_t *__restrict__ cu_seqlens, int64_t eq_len, const float *__restrict__ S0,
-    uint16_t *__restrict__ o, float *__restrict__ S_T, int HV, int DV, int rep, float scale) {
+    const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ order, int64_t eq_len,
+    const float *__restrict__ S0, uint16_t *__restrict__ o, float *__restrict__ S_T, int HV, int DV,
+    int rep, int NG, int M, float scale) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
     // Everything belonging to chunk c lives in the buffers of parity c % 2: K and Q rows, K^T,
     // the per-token scalars, and the solve / read operands built from them.  Scalars:
@@ -223,12 +224,22 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     (void)sG; (void)sGam; (void)sRk; (void)sRq; (void)sB; (void)sDn;
     // opT [((b*2 + rt)*2 + hl)*64 + lane], opA [(rt*2 + hl)*64 + lane], opP [idx*64 + lane]
 
-    const int unit = blockIdx.x;  // n * HV + h
-    const int h = unit % HV;
-    const int nseq = unit / HV;
-    const int hq = h / rep;
+    // Workgroup -> (sequence, V head, column slice).  The M = rep * (DV / 64) workgroups
+    // that read the same q and k rows (one sequence, one QK head: group G) get linear ids
+    // L = 8 (M (G / 8) + m) + G % 8, i.e. the same L mod 8, so round-robin dispatch over the
+    // eight XCDs places them on one XCD and one L2, launched one after another.  Groups are
+    // numbered in launch order (sequence rank, then QK head); ids past the last group exit.
     const int HQK = HV / rep;
-    const int col0 = blockIdx.y * DVS;
+    const int Lid = blockIdx.x;
+    const int G = 8 * ((Lid >> 3) / M) + (Lid & 7);
+    if (G >= NG) return;
+    const int mem = (Lid >> 3) % M;
+    const int rank = G / HQK;
+    const int hq = G % HQK;
+    const int nseq = order ? order[rank] : rank;
+    const int h = hq * rep + mem / (DV / DVS);
+    const int col0 = (mem % (DV / DVS)) * DVS;
+    const int unit = nseq * HV + h;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
@@ -318,27 +329,39 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) vcur[rt][e] = bf16_to_f32(vreg[rt][e]);
             if (c + 1 < nchunks) prefetch_v(c + 1);
-            bf16x8 Sh[4], Sl[4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) split(cat(S[2 * ks], S[2 * ks + 1]), Sh[ks], Sl[ks]);
+            // contraction block ks outermost: eight independent accumulator chains in flight
+            f32x4 y[4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                f32x4 y = {0.f, 0.f, 0.f, 0.f}, oa = {0.f, 0.f, 0.f, 0.f};
+                y[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                Ot[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const bf16x8 kk = ld_std(sK, LK, 16 * rt, 32 * ks, ln);
-                    const bf16x8 qq = ld_std(sQ, LK, 16 * rt, 32 * ks, ln);
-                    y = mfma32(kk, Sh[ks], y);
-                    y = mfma32(kk, Sl[ks], y);
-                    oa = mfma32(Sh[ks], qq, oa);
+            for (int ks = 0; ks < 4; ++ks) {
+                bf16x8 Sh, Sl;
+                split(cat(S[2 * ks], S[2 * ks + 1]), Sh, Sl);
+                bf16x8 kk[4], qq[4];
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    kk[rt] = ld_std(sK, LK, 16 * rt, 32 * ks, ln);
+                    qq[rt] = ld_std(sQ, LK, 16 * rt, 32 * ks, ln);
                 }
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    y[rt] = mfma32(kk[rt], Sh, y[rt]);
+                    Ot[rt] = mfma32(Sh, qq[rt], Ot[rt]);
+                }
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) y[rt] = mfma32(kk[rt], Sl, y[rt]);
+            }
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
                 const int i0 = 16 * rt + 4 * lqq;
                 const f32x4 b4 = *reinterpret_cast<const f32x4 *>(sB + i0);
                 const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sGam + i0);
                 const f32x4 k4 = *reinterpret_cast<const f32x4 *>(sRk + i0);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) Z[rt][e] = b4[e] * (vcur[rt][e] - g4[e] * k4[e] * y[e]);
-                Ot[rt] = oa;
+                for (int e = 0; e < 4; ++e) Z[rt][e] = b4[e] * (vcur[rt][e] - g4[e] * k4[e] * y[rt][e]);
             }
         };
 
@@ -817,11 +840,14 @@ bool prefill_chunked_supported(int dk, int dv, bool bf16) { return bf16 && dk ==
 hipError_t launch_prefill_chunked(const PrefillArgs &a, hipStream_t stream) {
     if (a.N == 0) return hipSuccess;
     const int rep = a.HV / a.HQK;
-    dim3 grid((unsigned)((int64_t)a.N * a.HV), (unsigned)(a.dv / DVS));
-    hipLaunchKernelGGL(prefill_chunked_kernel, grid, dim3(NT), 0, stream, static_cast<const uint16_t *>(a.q),
-                       static_cast<const uint16_t *>(a.k), static_cast<const uint16_t *>(a.v), a.g, a.beta,
-                       a.cu_seqlens, a.eq_len, a.S0, static_cast<uint16_t *>(a.o), a.S_T, a.HV, a.dv, rep,
-                       a.scale);
+    const int64_t NG = (int64_t)a.N * a.HQK;            // (sequence, QK head) groups
+    const int64_t M = (int64_t)rep * (a.dv / DVS);      // workgroups per group
+    const int64_t nwg = 8 * M * ((NG + 7) / 8);
+    if (nwg > 0x7fffffffLL || NG > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(prefill_chunked_kernel, dim3((unsigned)nwg), dim3(NT), 0, stream,
+                       static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
+                       static_cast<const uint16_t *>(a.v), a.g, a.beta, a.cu_seqlens, a.order, a.eq_len,
+                       a.S0, static_cast<uint16_t *>(a.o), a.S_T, a.HV, a.dv, rep, (int)NG, (int)M, a.scale);
     return hipGetLastError();
 }
 

@@ -25,15 +25,18 @@ template <int DK, typename T>
 __global__ __launch_bounds__(64) void prefill_recurrent_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
-    const int32_t *__restrict__ cu_seqlens, int64_t eq_len, const float *__restrict__ S0,
-    T *__restrict__ o, float *__restrict__ S_T, int HV, int DV, int rep, float scale) {
+    const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ order, int64_t eq_len,
+    const float *__restrict__ S0, T *__restrict__ o, float *__restrict__ S_T, int HV, int DV, int rep,
+    float scale) {
     constexpr int EPL = (DK + 63) / 64;  // q/k elements per lane
     __shared__ float kh_s[DK];
     __shared__ float qh_s[DK];
 
-    const int unit = blockIdx.x;  // n * HV + h
-    const int h = unit % HV;
-    const int n = unit / HV;
+    // launch rank * HV + h; rank -> sequence through the longest-first order
+    const int h = blockIdx.x % HV;
+    const int rank = blockIdx.x / HV;
+    const int n = order ? order[rank] : rank;
+    const int unit = n * HV + h;
     const int hq = h / rep;
     const int HQK = HV / rep;
     const int lane = threadIdx.x;
@@ -114,7 +117,7 @@ hipError_t launch(const PrefillArgs &a, hipStream_t stream) {
     dim3 grid((unsigned)((int64_t)a.N * a.HV), (unsigned)((a.dv + 63) / 64));
     hipLaunchKernelGGL((prefill_recurrent_kernel<DK, T>), grid, dim3(64), 0, stream,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
-                       static_cast<const T *>(a.v), a.g, a.beta, a.cu_seqlens, a.eq_len, a.S0,
+                       static_cast<const T *>(a.v), a.g, a.beta, a.cu_seqlens, a.order, a.eq_len, a.S0,
                        static_cast<T *>(a.o), a.S_T, a.HV, a.dv, rep, a.scale);
     return hipGetLastError();
 }

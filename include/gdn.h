@@ -91,7 +91,9 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const fl
 
 /*
  * gdn_prefill_workspace_size -- bytes of device workspace gdn_prefill needs for
- * these sizes (0 means the workspace pointer may be NULL).
+ * these sizes (0 means the workspace pointer may be NULL).  The workspace holds
+ * the launch order of the sequences (one int32 each); it is 0 for N <= 1 and
+ * for N above 16384 (such batches run in the given order).
  */
 size_t gdn_prefill_workspace_size(int32_t N, int64_t total_T, int32_t HQK, int32_t HV,
                                   int32_t dk, int32_t dv, gdn_dtype dtype);
@@ -108,8 +110,13 @@ size_t gdn_prefill_workspace_size(int32_t N, int64_t total_T, int32_t HQK, int32
  *               cu[N] = total_T.  Empty sequences are allowed.  NULL means N
  *               equal sequences of total_T / N tokens (N must divide total_T).
  *   cu_seqlens_host  optional host copy of the same array.  When given it is
- *               validated (GDN_ERR_SEQLENS) and used to schedule long sequences
- *               first; when NULL the device array is trusted as is.
+ *               validated (GDN_ERR_SEQLENS); when NULL the device array is
+ *               trusted as is.
+ *               Sequences are launched longest first: unless the host copy shows
+ *               lengths that never increase, a small ranking kernel writes the
+ *               order into the workspace ahead of the scan (same stream).  A HIP
+ *               error at the scan's launch is then reported as GDN_ERR_HIP after
+ *               the ranking kernel (which writes only the workspace) is enqueued.
  *   S0          [N, HV, dk, dv] fp32 start tables, or NULL for empty tables
  *   o           [total_T, HV, dv] dtype, out: per-token reads
  *   S_T         [N, HV, dk, dv] fp32, out: final tables, or NULL to skip.

@@ -128,6 +128,30 @@ def test_prefill_state_in_place_alias():
     assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), "bf16", "alias")
 
 
+@pytest.mark.parametrize("host_lengths", [True, False])
+def test_prefill_longest_first_order(host_lengths):
+    """Unsorted lengths: the workspace receives the longest-first launch order (a stable
+    sort by length, descending), and every sequence still matches the oracle."""
+    rng = np.random.default_rng(7)
+    lens = [int(x) for x in rng.integers(0, 200, size=37)]
+    lens[5] = lens[11] = 150  # ties keep index order
+    _say(f"prefill order host={host_lengths} lens={lens}")
+    inp = W.random_small(47, lens, 2, 4, 128, 64)
+    d = to_device(inp)
+    need = binding.prefill_workspace_size(len(lens), inp.total_T, 2, 4, 128, 64, torch.bfloat16)
+    assert need >= 4 * len(lens)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    o, S = binding.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu"],
+                           cu_seqlens_host=inp.cu_seqlens if host_lengths else None, S0=d["S0"],
+                           scale=inp.scale, workspace=ws)
+    torch.cuda.synchronize()
+    order = ws[:4 * len(lens)].cpu().numpy().view(np.int32)
+    expect = sorted(range(len(lens)), key=lambda i: (-lens[i], i))
+    assert list(order) == expect
+    o_ref, S_ref = oracle.run_inputs(inp)
+    assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), "bf16", "order")
+
+
 def test_prefill_equal_lengths_without_cu_seqlens():
     inp = W.random_small(44, [33, 33, 33], 2, 4, 64, 64)
     d = to_device(inp)
