@@ -413,9 +413,10 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                     const int i = 16 * rt + lrr;
                     const float gq = sGam[i] * sRq[i];
                     const bf16x4 ob = __builtin_convertvector(gq * Ot[rt] + pd, bf16x4);
-                    if (i < n)
-                        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob), orr, ooff,
-                                                              (uint32_t)(16 * rt) * rowb, 0);
+                    // rows past the chunk get an offset beyond the descriptor's range, which the
+                    // hardware drops (no branch, so the memory counters stay exact)
+                    const uint32_t off = (i < n) ? ooff + (uint32_t)(16 * rt) * rowb : 0xFFFFFFF0u;
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob), orr, off, 0, 0);
                 }
             }
             // S <- gamma_n S + K^T D,  D = diag(r_k exp(G_n - G)) Delta
