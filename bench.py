@@ -71,8 +71,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--cpu-sample-seqs", type=int, default=2,
-                    help="prefill sequences (all V heads) the CPU oracle baseline runs on")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=4,
+                    help="prefill sequences (all V heads) the CPU oracle baseline runs on (default: all 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run one 1 GiB device copy (counter calibration)")
