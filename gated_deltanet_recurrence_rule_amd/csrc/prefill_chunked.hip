@@ -78,7 +78,7 @@ constexpr int OPA_SZ = 2 * 2 * 64 * 16;                    // -A_10 operands [2 
 constexpr int OPP_SZ = 6 * 64 * 16;                        // P operands [6 (rt, ks)][64][8]
 constexpr int OP_SZ = OPT_SZ + OPA_SZ + OPP_SZ;
 constexpr int OFF_OP = OFF_KT + 2 * KT_SZ;                 // [2]
-constexpr int SC_SZ = 6 * C;                               // fp32 per-token scalars of one chunk
+constexpr int SC_SZ = 10 * C;                              // fp32 per-token scalars of one chunk
 constexpr int OFF_SC = OFF_OP + 2 * OP_SZ;                 // [2]
 constexpr int OFF_FLAG = OFF_SC + 2 * SC_SZ * 4;           // two int hand-over counters
 constexpr int LDS_BYTES = OFF_FLAG + 16;
@@ -208,7 +208,10 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     // Everything belonging to chunk c lives in the buffers of parity c % 2: K and Q rows, K^T,
     // the per-token scalars, and the solve / read operands built from them.  Scalars:
     // G (cumulative log-decay times log2 e), gamma = exp(G), r_k = 1/|k|, r_q = scale/|q|,
-    // beta, r_k exp(G_n - G).
+    // beta, r_k exp(G_n - G), and split decays.  With E_b = G at token 16 b + 15 (the end of
+    // 16-token tile b): CF[t] = exp(E_{t/16} - G_t) and RF[b][t] = exp(G_t - E_b) for t past
+    // tile b, so a tile with rows i after its columns j (tile b) has exp(G_i - G_j) =
+    // RF[b][i] CF[j], both factors <= 1.
 #define GDN_CHUNK(c)                                                                        \
     const int par_ = (c) & 1;                                                               \
     __bf16 *sK = reinterpret_cast<__bf16 *>(lds + OFF_KQ + par_ * KQ_SZ);                   \
@@ -220,8 +223,9 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     float *sc_ = reinterpret_cast<float *>(lds + OFF_SC) + par_ * SC_SZ;                    \
     float *sG = sc_, *sGam = sc_ + C, *sRk = sc_ + 2 * C;                                   \
     float *sRq = sc_ + 3 * C, *sB = sc_ + 4 * C, *sDn = sc_ + 5 * C;                        \
+    float *sCF = sc_ + 6 * C, *sRF = sc_ + 7 * C;                                           \
     (void)sK; (void)sQ; (void)sKt; (void)opT; (void)opA; (void)opP;                         \
-    (void)sG; (void)sGam; (void)sRk; (void)sRq; (void)sB; (void)sDn;
+    (void)sG; (void)sGam; (void)sRk; (void)sRq; (void)sB; (void)sDn; (void)sCF; (void)sRF;
     // opT [((b*2 + rt)*2 + hl)*64 + lane], opA [(rt*2 + hl)*64 + lane], opP [idx*64 + lane]
 
     // Workgroup -> (sequence, V head, column slice).  The M = rep * (DV / 64) workgroups
@@ -596,6 +600,15 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             sG[ln] = x;
             sGam[ln] = exp2_hw(x);
             sB[ln] = breg;
+            const float E0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 15));
+            const float E1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 31));
+            const float E2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 47));
+            const float E3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+            const int tb = ln >> 4;
+            sCF[ln] = exp2_hw((tb == 0 ? E0 : tb == 1 ? E1 : tb == 2 ? E2 : E3) - x);
+            sRF[ln] = tb > 0 ? exp2_hw(x - E0) : 0.f;
+            sRF[C + ln] = tb > 1 ? exp2_hw(x - E1) : 0.f;
+            sRF[2 * C + ln] = tb > 2 ? exp2_hw(x - E2) : 0.f;
         }
     };
 
@@ -646,18 +659,25 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
 #pragma unroll
                 for (int kq = 0; kq < 4; ++kq) acc = mfma32(kk[kq], qq[kq], acc);
                 const int j0 = 16 * kt + 4 * lqq;
-                const f32x4 G4 = *reinterpret_cast<const f32x4 *>(sG + j0);
                 const f32x4 R4 = *reinterpret_cast<const f32x4 *>(sRk + j0);
+                if (kt < rt) {  // every row after every column: split decays, no mask
+                    const float cr = ci * sRF[kt * C + i];
+                    const f32x4 CF4 = *reinterpret_cast<const f32x4 *>(sCF + j0);
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    x[4 * t + e] = (j0 + e <= i) ? ci * R4[e] * acc[e] * exp2_hw(Gi - G4[e]) : 0.f;
+                    for (int e = 0; e < 4; ++e) x[4 * t + e] = cr * (R4[e] * CF4[e]) * acc[e];
+                } else {
+                    const f32x4 G4 = *reinterpret_cast<const f32x4 *>(sG + j0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        x[4 * t + e] = (j0 + e <= i) ? ci * R4[e] * acc[e] * exp2_hw(Gi - G4[e]) : 0.f;
+                }
             }
             opP[idx * 64 + ln] = to_bf16(x);
         };
         // -A_10 (rows 32 + 16 rt .., columns 0..31) in tile order, from role-swapped Gram tiles
         auto a_operand = [&](int rt) {
             const int i = 32 + 16 * rt + lrr;
-            const float ci = sB[i] * sRk[i], Gi = sG[i];
+            const float ci = sB[i] * sRk[i];
             bf16x8 kr[4];
             load_blk(sK, 2 + rt, kr);
             f32x8 x;
@@ -669,10 +689,11 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) acc = mfma32(kk[ks], kr[ks], acc);
                 const int j0 = 16 * t + 4 * lqq;
-                const f32x4 G4 = *reinterpret_cast<const f32x4 *>(sG + j0);
                 const f32x4 R4 = *reinterpret_cast<const f32x4 *>(sRk + j0);
+                const f32x4 CF4 = *reinterpret_cast<const f32x4 *>(sCF + j0);
+                const float cr = -ci * sRF[t * C + i];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[4 * t + e] = -ci * R4[e] * acc[e] * exp2_hw(Gi - G4[e]);
+                for (int e = 0; e < 4; ++e) x[4 * t + e] = cr * (R4[e] * CF4[e]) * acc[e];
             }
             bf16x8 hi, lo;
             split(x, hi, lo);
@@ -758,12 +779,12 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                 for (int ks = 0; ks < 4; ++ks) gx = mfma32(kd[ks], kn[ks], gx);
                 const int i0 = 16 * blk + 4 * lqq;
                 const int r = 16 * (blk + 1) + lrr;
-                const f32x4 G4 = *reinterpret_cast<const f32x4 *>(sG + i0);
                 const f32x4 R4 = *reinterpret_cast<const f32x4 *>(sRk + i0);
-                const float cr = sB[r] * sRk[r], Gr = sG[r];
+                const f32x4 CF4 = *reinterpret_cast<const f32x4 *>(sCF + i0);
+                const float cr = sB[r] * sRk[r] * sRF[blk * C + r];
                 f32x4 At;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) At[e] = cr * R4[e] * gx[e] * exp2_hw(Gr - G4[e]);
+                for (int e = 0; e < 4; ++e) At[e] = cr * (R4[e] * CF4[e]) * gx[e];
                 bf16x4 ah, al, th, tl;
                 hl(At, ah, al);
                 hl(T, th, tl);
