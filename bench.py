@@ -74,6 +74,9 @@ def main():
     ap.add_argument("--cpu-sample-seqs", type=int, default=4,
                     help="prefill sequences (all V heads) the CPU oracle baseline runs on (default: all 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="before the warm-up steps, run steps for at least this long so the GPU "
+                         "reaches its sustained clock (untimed; 0 disables)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run one 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -121,6 +124,13 @@ def main():
     def decode():
         binding.decode_step(D["q"], D["k"], D["v"], D["g"], D["beta"], D["S"], o=o_d)
 
+    # Clock settle (untimed): the first ~10 ms of load run ~20% slower than sustained.
+    if args.settle_ms > 0:
+        t_set = time.perf_counter()
+        while (time.perf_counter() - t_set) * 1e3 < args.settle_ms:
+            prefill()
+            decode()
+            torch.cuda.synchronize()
     for _ in range(args.warmup):
         prefill()
         decode()

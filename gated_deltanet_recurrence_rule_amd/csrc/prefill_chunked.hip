@@ -376,8 +376,12 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             const int64_t c0 = t0 + (int64_t)c * C;
             const int n = chunk_len(c);
             GDN_CHUNK(c)
-            // Delta_0 = T_0 Z_0;  Delta_1 = T_1 (Z_1 - A_10 Delta_0)
+            // Delta_0 = T_0 Z_0;  Delta_1 = T_1 (Z_1 - A_10 Delta_0);  D = diag(r_k exp(G_n - G)) Delta.
+            // D and the bf16 read operands are taken from each Delta half before its hi/lo split,
+            // so the split can overwrite it.
             f32x4 Dl[4];
+            f32x8 Dx[2];
+            bf16x8 Dsg[2];
             {
                 bf16x8 zh, zl;
                 split(cat(Z[0], Z[1]), zh, zl);
@@ -386,8 +390,15 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
                     Dl[rt] = mfma32_x3(opT[(rt * 2 + 0) * 64 + ln], opT[(rt * 2 + 1) * 64 + ln], zh, zl, zero);
                 }
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sDn + 16 * t + 4 * lqq);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Dx[0][4 * t + e] = Dl[t][e] * d4[e];
+                }
                 bf16x8 dh, dl;
                 split(cat(Dl[0], Dl[1]), dh, dl);
+                Dsg[0] = dh;
                 f32x4 r1[2];
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
@@ -400,12 +411,16 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                     Dl[2 + rt] = mfma32_x3(opT[((2 + rt) * 2 + 0) * 64 + ln], opT[((2 + rt) * 2 + 1) * 64 + ln],
                                            rh, rl, zero);
                 }
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sDn + 32 + 16 * t + 4 * lqq);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Dx[1][4 * t + e] = Dl[2 + t][e] * d4[e];
+                }
+                Dsg[1] = to_bf16(cat(Dl[2], Dl[3]));
             }
             // O^T = gamma r_q (Q S)^T + (P Delta)^T: token 16 rt + lr, 4 adjacent columns per lane
             {
-                bf16x8 Dsg[2];
-                Dsg[0] = to_bf16(cat(Dl[0], Dl[1]));
-                Dsg[1] = to_bf16(cat(Dl[2], Dl[3]));
                 const rsrc_t orr = make_rsrc(owave + (size_t)c0 * vrs, (uint32_t)n * rowb);
                 const uint32_t ooff = (uint32_t)lrr * rowb + 8u * (uint32_t)lqq;
 #pragma unroll
@@ -423,20 +438,11 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob), orr, off, 0, 0);
                 }
             }
-            // S <- gamma_n S + K^T D,  D = diag(r_k exp(G_n - G)) Delta
+            // S <- gamma_n S + K^T D
             {
                 bf16x8 Dh[2], Dlo[2];
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    f32x8 x = cat(Dl[2 * ks], Dl[2 * ks + 1]);
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sDn + 32 * ks + 16 * t + 4 * lqq);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) x[4 * t + e] *= d4[e];
-                    }
-                    split(x, Dh[ks], Dlo[ks]);
-                }
+                for (int ks = 0; ks < 2; ++ks) split(Dx[ks], Dh[ks], Dlo[ks]);
                 const float gam_n = sGam[C - 1];
 #pragma unroll
                 for (int dt = 0; dt < 8; ++dt) {
@@ -459,12 +465,15 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         phase_a(0);
         __syncthreads();  // operands of chunk 0 built
         __syncthreads();  // chunk 1 staged
-        for (int c = 0; c < nchunks; ++c) {
+        for (int c = 0; c + 1 < nchunks; ++c) {
             phase_b(c);
             __syncthreads();
-            if (c + 1 < nchunks) phase_a(c + 1);
+            phase_a(c + 1);
             __syncthreads();
         }
+        phase_b(nchunks - 1);
+        __syncthreads();
+        __syncthreads();
         if (S_T) {
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt)

@@ -5,9 +5,9 @@ Three runs feed it (each writes CSV files into its own directory):
   kernel times   rocprofv3 --kernel-trace --stats --output-format csv -d <KT> -o bench -- \
                      python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline
   HBM reads      timeout -s KILL 180 rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH> -o bench -- \
-                     python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-probe
+                     python3 bench.py --steps 2 --warmup 1 --settle-ms 0 --no-cpu-baseline --copy-probe
   HBM writes     timeout -s KILL 180 rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE> -o bench -- \
-                     python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-probe
+                     python3 bench.py --steps 2 --warmup 1 --settle-ms 0 --no-cpu-baseline --copy-probe
 
 then
 
@@ -44,7 +44,7 @@ KERNELS = {
 CMD_KT = ("rocprofv3 --kernel-trace --stats --output-format csv -d {kt} -o bench -- "
           "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline")
 CMD_PMC = ("timeout -s KILL 180 rocprofv3 --pmc {ctr} --output-format csv -d {d} -o bench -- "
-           "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-probe")
+           "python3 bench.py --steps 2 --warmup 1 --settle-ms 0 --no-cpu-baseline --copy-probe")
 CMD_SUM = "python3 -m gated_deltanet_recurrence_rule_amd.profsummary {kt} {fetch} {write} --out profiles"
 
 
