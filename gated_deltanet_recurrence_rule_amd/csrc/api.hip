@@ -27,9 +27,17 @@ bool dim_ok(int32_t d) { return d == 32 || d == 64 || d == 128; }
 
 // `tokens` is the number of tokens the call touches; with none, the token
 // arrays may be NULL (an empty tensor has no storage).
+// Which inputs a variant reads: the gated ones read g; the look-up ones need beta
+// (the linear variants may pass NULL for b = 1).
+bool variant_ok(gdn_variant x) { return x == GDN_GATED_DELTA || x == GDN_DELTA || x == GDN_GATED_LINEAR || x == GDN_LINEAR; }
+bool variant_gated(gdn_variant x) { return x == GDN_GATED_DELTA || x == GDN_GATED_LINEAR; }
+bool variant_delta(gdn_variant x) { return x == GDN_GATED_DELTA || x == GDN_DELTA; }
+
 gdn_status check_common(const void *q, const void *k, const void *v, const float *g,
                         const float *beta, const void *o, int32_t N, int32_t HQK, int32_t HV,
-                        int32_t dk, int32_t dv, gdn_dtype dtype, int64_t tokens) {
+                        int32_t dk, int32_t dv, gdn_dtype dtype, int64_t tokens,
+                        gdn_variant variant = GDN_GATED_DELTA) {
+    if (!variant_ok(variant)) return fail(GDN_ERR_UNSUPPORTED, "unknown variant %d", (int)variant);
     if (dtype != GDN_BF16 && dtype != GDN_F32) return fail(GDN_ERR_DTYPE, "unknown dtype %d", (int)dtype);
     if (N < 0) return fail(GDN_ERR_SHAPE, "N = %d is negative", N);
     if (HQK <= 0 || HV <= 0) return fail(GDN_ERR_SHAPE, "head counts must be positive (HQK=%d, HV=%d)", HQK, HV);
@@ -37,7 +45,9 @@ gdn_status check_common(const void *q, const void *k, const void *v, const float
     if (!dim_ok(dk) || !dim_ok(dv))
         return fail(GDN_ERR_UNSUPPORTED, "dk=%d, dv=%d: each must be 32, 64 or 128", dk, dv);
     if (tokens == 0) return GDN_OK;
-    if (!q || !k || !v || !g || !beta || !o) return fail(GDN_ERR_NULL, "q, k, v, g, beta and o must be non-NULL");
+    if (!q || !k || !v || !o) return fail(GDN_ERR_NULL, "q, k, v and o must be non-NULL");
+    if (variant_gated(variant) && !g) return fail(GDN_ERR_NULL, "g must be non-NULL for a gated variant");
+    if (variant_delta(variant) && !beta) return fail(GDN_ERR_NULL, "beta must be non-NULL for a delta variant");
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
         return fail(GDN_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
     if (!aligned(g, 4) || !aligned(beta, 4)) return fail(GDN_ERR_ALIGN, "g and beta must be 4-byte aligned");
@@ -76,14 +86,23 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const fl
                            const float *beta, float *S, void *o, int32_t N, int32_t HQK,
                            int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype, float scale,
                            hipStream_t stream) {
+    return gdn_decode_step_v(q, k, v, g, beta, S, o, N, HQK, HV, dk, dv, dtype, scale, GDN_GATED_DELTA,
+                             stream);
+}
+
+gdn_status gdn_decode_step_v(const void *q, const void *k, const void *v, const float *g,
+                             const float *beta, float *S, void *o, int32_t N, int32_t HQK,
+                             int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype, float scale,
+                             gdn_variant variant, hipStream_t stream) {
     g_last_error[0] = 0;
-    gdn_status st = check_common(q, k, v, g, beta, o, N, HQK, HV, dk, dv, dtype, N);
+    gdn_status st = check_common(q, k, v, g, beta, o, N, HQK, HV, dk, dv, dtype, N, variant);
     if (st != GDN_OK) return st;
     if (N == 0) return GDN_OK;
     if (!S) return fail(GDN_ERR_NULL, "S must be non-NULL");
     if (!aligned(S, 16)) return fail(GDN_ERR_ALIGN, "S must be 16-byte aligned");
     if ((int64_t)N * HV > 0x7fffffffLL) return fail(GDN_ERR_SHAPE, "N * HV exceeds the grid limit");
-    gdn::DecodeArgs a{q, k, v, g, beta, S, o, N, HQK, HV, dk, dv, scale};
+    gdn::DecodeArgs a{q, k, v, variant_gated(variant) ? g : nullptr, beta, S, o, N, HQK, HV, dk, dv, scale,
+                      variant_delta(variant) ? 1 : 0};
     return hip_status(gdn::launch_decode(a, dtype == GDN_BF16, stream), "decode launch");
 }
 
@@ -101,9 +120,19 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
                        const float *S0, void *o, float *S_T, int32_t HQK, int32_t HV, int32_t dk,
                        int32_t dv, gdn_dtype dtype, float scale, void *workspace,
                        size_t workspace_bytes, hipStream_t stream) {
+    return gdn_prefill_v(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, N, total_T, S0, o, S_T, HQK, HV, dk,
+                         dv, dtype, scale, GDN_GATED_DELTA, workspace, workspace_bytes, stream);
+}
+
+gdn_status gdn_prefill_v(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const int32_t *cu_seqlens,
+                         const int32_t *cu_seqlens_host, int32_t N, int64_t total_T,
+                         const float *S0, void *o, float *S_T, int32_t HQK, int32_t HV, int32_t dk,
+                         int32_t dv, gdn_dtype dtype, float scale, gdn_variant variant, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
     g_last_error[0] = 0;
     if (total_T < 0) return fail(GDN_ERR_SHAPE, "total_T = %lld is negative", (long long)total_T);
-    gdn_status st = check_common(q, k, v, g, beta, o, N, HQK, HV, dk, dv, dtype, total_T);
+    gdn_status st = check_common(q, k, v, g, beta, o, N, HQK, HV, dk, dv, dtype, total_T, variant);
     if (st != GDN_OK) return st;
     if (S0 && !aligned(S0, 16)) return fail(GDN_ERR_ALIGN, "S0 must be 16-byte aligned");
     if (S_T && !aligned(S_T, 16)) return fail(GDN_ERR_ALIGN, "S_T must be 16-byte aligned");
@@ -155,8 +184,9 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
             order = ord;
         }
     }
-    gdn::PrefillArgs a{q, k, v, g, beta, cu_seqlens, order, eq_len, N, total_T, S0, o, S_T,
-                       HQK, HV, dk, dv, scale, workspace, workspace_bytes};
+    gdn::PrefillArgs a{q, k, v, variant_gated(variant) ? g : nullptr, beta, cu_seqlens, order, eq_len, N,
+                       total_T, S0, o, S_T, HQK, HV, dk, dv, scale, workspace, workspace_bytes,
+                       variant_delta(variant) ? 1 : 0};
     const bool bf16 = dtype == GDN_BF16;
     if (gdn::prefill_chunked_supported(dk, dv, bf16))
         return hip_status(gdn::launch_prefill_chunked(a, stream), "chunked prefill launch");

@@ -32,7 +32,7 @@ template <int DK, int DV, typename T>
 __global__ __launch_bounds__(4 * DV) void decode_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float *__restrict__ S,
-    T *__restrict__ o, int HV, int rep, float scale) {
+    T *__restrict__ o, int HV, int rep, float scale, int delta) {
     constexpr int NQ = DV / 4;          // column quads
     constexpr int NT = NQ * kRowGroups; // threads
     constexpr int RPT = DK / kRowGroups;
@@ -62,8 +62,8 @@ __global__ __launch_bounds__(4 * DV) void decode_kernel(
 #pragma unroll
     for (int m = 0; m < RPT; ++m) s[m] = ld_stream(Sp + (size_t)(rg + kRowGroups * m) * DV + 4 * cq);
 
-    const float a = expf(g[unit]);
-    const float b = beta[unit];
+    const float a = g ? expf(g[unit]) : 1.f;
+    const float b = beta ? beta[unit] : 1.f;
 
     // Wave 0: normalise this token's q and k (shared by the `rep` V heads of QK head hq).
     if (wave == 0) {
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(4 * DV) void decode_kernel(
             aq += part_s[w][1][j];
         }
         const size_t vo = (size_t)unit * DV + j;
-        const float d = b * (elem<T>::ld(v + vo) - a * ak);
+        const float d = b * (elem<T>::ld(v + vo) - (delta ? a * ak : 0.f));
         d_s[j] = d;
         elem<T>::st(o + vo, a * aq + qk_s * d);
     }
@@ -153,7 +153,7 @@ hipError_t launch(const DecodeArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((decode_kernel<DK, DV, T>), grid, dim3(4 * DV), 0, stream,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), a.g, a.beta, a.S, static_cast<T *>(a.o), a.HV,
-                       rep, a.scale);
+                       rep, a.scale, a.delta);
     return hipGetLastError();
 }
 

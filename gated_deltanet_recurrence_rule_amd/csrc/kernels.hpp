@@ -7,6 +7,8 @@
 namespace gdn {
 
 // Arguments shared by the launchers, already validated by the C-ABI layer.
+// g == nullptr means a = 1 (no decay); beta == nullptr means b = 1; delta == 0 drops the
+// look-up (the write is b v instead of b (v - a S^T k)).
 struct DecodeArgs {
     const void *q, *k, *v;
     const float *g, *beta;
@@ -14,6 +16,7 @@ struct DecodeArgs {
     void *o;
     int32_t N, HQK, HV, dk, dv;
     float scale;
+    int32_t delta;
 };
 
 struct PrefillArgs {
@@ -31,6 +34,7 @@ struct PrefillArgs {
     float scale;
     void *workspace;
     size_t workspace_bytes;
+    int32_t delta;
 };
 
 // Each returns hipSuccess or the launch error.  `bf16` selects the I/O type.

@@ -198,6 +198,9 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// DELTA = false drops the look-up (A = 0, so T = I and Delta = Z = diag(b) V): the decayed
+// linear-attention rule of the learn-llm page's update-rule table.
+template <bool DELTA>
 __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
@@ -352,11 +355,13 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                 }
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
-                    y[rt] = mfma32(kk[rt], Sh, y[rt]);
+                    if constexpr (DELTA) y[rt] = mfma32(kk[rt], Sh, y[rt]);
                     Ot[rt] = mfma32(Sh, qq[rt], Ot[rt]);
                 }
+                if constexpr (DELTA) {
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt) y[rt] = mfma32(kk[rt], Sl, y[rt]);
+                    for (int rt = 0; rt < 4; ++rt) y[rt] = mfma32(kk[rt], Sl, y[rt]);
+                }
             }
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
@@ -365,7 +370,8 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                 const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sGam + i0);
                 const f32x4 k4 = *reinterpret_cast<const f32x4 *>(sRk + i0);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) Z[rt][e] = b4[e] * (vcur[rt][e] - g4[e] * k4[e] * y[rt][e]);
+                for (int e = 0; e < 4; ++e)
+                    Z[rt][e] = DELTA ? b4[e] * (vcur[rt][e] - g4[e] * k4[e] * y[rt][e]) : b4[e] * vcur[rt][e];
             }
         };
 
@@ -382,7 +388,19 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             f32x4 Dl[4];
             f32x8 Dx[2];
             bf16x8 Dsg[2];
-            {
+            if constexpr (!DELTA) {
+                // no look-up: Delta = Z
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sDn + 32 * ks + 16 * t + 4 * lqq);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) Dx[ks][4 * t + e] = Z[2 * ks + t][e] * d4[e];
+                    }
+                    Dsg[ks] = to_bf16(cat(Z[2 * ks], Z[2 * ks + 1]));
+                }
+            } else {
                 bf16x8 zh, zl;
                 split(cat(Z[0], Z[1]), zh, zl);
 #pragma unroll
@@ -531,10 +549,17 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             const bool ok = lane < nn;
             const uint32_t goff = 4u * (uint32_t)lane * (uint32_t)HV;
             const uint32_t gbytes = 4u * (uint32_t)nn * (uint32_t)HV;
-            const rsrc_t gr = make_rsrc(g + (size_t)cs * HV + h, gbytes);
-            const rsrc_t br = make_rsrc(beta + (size_t)cs * HV + h, gbytes);
-            greg = ok ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gr, goff, 0, 0)) : 0.f;
-            breg = ok ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(br, goff, 0, 0)) : 0.f;
+            // no g: a = 1 (G = 0); no beta: b = 1 (padding tokens keep b = 0)
+            greg = 0.f;
+            breg = ok ? 1.f : 0.f;
+            if (g) {
+                const rsrc_t gr = make_rsrc(g + (size_t)cs * HV + h, gbytes);
+                greg = ok ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gr, goff, 0, 0)) : 0.f;
+            }
+            if (beta) {
+                const rsrc_t br = make_rsrc(beta + (size_t)cs * HV + h, gbytes);
+                breg = ok ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(br, goff, 0, 0)) : 0.f;
+            }
         }
     };
 
@@ -772,7 +797,17 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             opT[((2 * b + rt) * 2 + 1) * 64 + ln] = lo;
         };
 
-        if (first) {
+        if constexpr (!DELTA) {
+            // no look-up: only P and r_k exp(G_n - G) are needed
+            if (b == 0) {
+                p_operand(first ? 0 : 2);
+                if (first) p_operand(1);
+                else sDn[ln] = sRk[ln] * exp2_hw(sG[C - 1] - sG[ln]);
+            } else {
+                p_operand(first ? 3 : 5);
+                if (first) p_operand(4);
+            }
+        } else if (first) {
             __builtin_amdgcn_s_setprio(2);
             f32x4 T, Tt;
             bf16x8 kd[4];
@@ -875,7 +910,8 @@ hipError_t launch_prefill_chunked(const PrefillArgs &a, hipStream_t stream) {
     const int64_t M = (int64_t)rep * (a.dv / DVS);      // workgroups per group
     const int64_t nwg = 8 * M * ((NG + 7) / 8);
     if (nwg > 0x7fffffffLL || NG > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(prefill_chunked_kernel, dim3((unsigned)nwg), dim3(NT), 0, stream,
+    hipLaunchKernelGGL(a.delta ? prefill_chunked_kernel<true> : prefill_chunked_kernel<false>, dim3((unsigned)nwg),
+                       dim3(NT), 0, stream,
                        static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
                        static_cast<const uint16_t *>(a.v), a.g, a.beta, a.cu_seqlens, a.order, a.eq_len,
                        a.S0, static_cast<uint16_t *>(a.o), a.S_T, a.HV, a.dv, rep, (int)NG, (int)M, a.scale);

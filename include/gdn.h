@@ -58,7 +58,7 @@ typedef enum {
     GDN_ERR_NULL = -1,        /* a required pointer is NULL                           */
     GDN_ERR_SHAPE = -2,       /* negative size, HV % HQK != 0, mismatched lengths      */
     GDN_ERR_DTYPE = -3,       /* unknown gdn_dtype                                     */
-    GDN_ERR_UNSUPPORTED = -4, /* dk or dv not in {32, 64, 128}                         */
+    GDN_ERR_UNSUPPORTED = -4, /* dk or dv not in {32, 64, 128}, or an unknown variant   */
     GDN_ERR_ALIGN = -5,       /* a pointer breaks the alignment rule above             */
     GDN_ERR_SEQLENS = -6,     /* cu_seqlens_host malformed, or N does not divide T     */
     GDN_ERR_WORKSPACE = -7,   /* workspace smaller than gdn_prefill_workspace_size()   */
@@ -69,6 +69,29 @@ typedef enum {
     GDN_BF16 = 0, /* q, k, v, o are bfloat16; o is rounded to nearest even */
     GDN_F32 = 1   /* q, k, v, o are float32                                */
 } gdn_dtype;
+
+/*
+ * gdn_variant -- the update rules of the learn-llm page 13_linear_attention_viz
+ * (its update-rule table), stated here in the handbook's orientation (S is
+ * [dk, dv], o = S^T q).  The library's q, k normalisation and `scale` apply to
+ * every variant.
+ *
+ *   GDN_GATED_DELTA   S <- a S + b k (v - a S^T k)^T   Gated DeltaNet (the default)
+ *   GDN_DELTA         S <- S + b k (v - S^T k)^T       DeltaNet: a = 1; g is ignored
+ *                                                      and may be NULL
+ *   GDN_GATED_LINEAR  S <- a S + b k v^T               Mamba2-style decayed linear
+ *                                                      attention: no look-up
+ *   GDN_LINEAR        S <- S + b k v^T                 linear attention: a = 1, no look-up
+ *
+ * The two linear rules of that table carry no write strength: they accept
+ * beta == NULL, meaning b = 1.
+ */
+typedef enum {
+    GDN_GATED_DELTA = 0,
+    GDN_DELTA = 1,
+    GDN_GATED_LINEAR = 2,
+    GDN_LINEAR = 3
+} gdn_variant;
 
 /*
  * gdn_decode_step -- advance every sequence and V head by one token, in place.
@@ -88,6 +111,13 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const fl
                            const float *beta, float *S, void *o, int32_t N, int32_t HQK,
                            int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype, float scale,
                            hipStream_t stream);
+
+/* gdn_decode_step with an update rule other than the default (see gdn_variant);
+ * g may be NULL for GDN_DELTA and GDN_LINEAR, beta for GDN_GATED_LINEAR and GDN_LINEAR. */
+gdn_status gdn_decode_step_v(const void *q, const void *k, const void *v, const float *g,
+                             const float *beta, float *S, void *o, int32_t N, int32_t HQK,
+                             int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype, float scale,
+                             gdn_variant variant, hipStream_t stream);
 
 /*
  * gdn_prefill_workspace_size -- bytes of device workspace gdn_prefill needs for
@@ -133,6 +163,16 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
                        const float *S0, void *o, float *S_T, int32_t HQK, int32_t HV, int32_t dk,
                        int32_t dv, gdn_dtype dtype, float scale, void *workspace,
                        size_t workspace_bytes, hipStream_t stream);
+
+/* gdn_prefill with an update rule other than the default (see gdn_variant);
+ * g may be NULL for GDN_DELTA and GDN_LINEAR, beta for GDN_GATED_LINEAR and GDN_LINEAR.
+ * Without the look-up (the linear rules) the chunked kernel skips the triangular solve. */
+gdn_status gdn_prefill_v(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const int32_t *cu_seqlens,
+                         const int32_t *cu_seqlens_host, int32_t N, int64_t total_T,
+                         const float *S0, void *o, float *S_T, int32_t HQK, int32_t HV, int32_t dk,
+                         int32_t dv, gdn_dtype dtype, float scale, gdn_variant variant, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream);
 
 /*
  * gdn_prefill_kernel_name -- which kernel gdn_prefill runs for these sizes

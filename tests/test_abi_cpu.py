@@ -40,6 +40,10 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def test_exports_variant_entry_points(lib):
+    assert {"gdn_decode_step_v", "gdn_prefill_v"} <= set(declared_functions())
+
+
 def test_status_strings(lib):
     for s in (OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_ALIGN, E_SEQ, E_WS, E_HIP):
         assert lib.gdn_status_str(s)
@@ -158,4 +162,52 @@ def test_prefill_zero_sequences_is_a_noop(lib):
     z = np.zeros(1, np.int32)
     assert _prefill(lib, B, N=0, T=0, cu=B.p(z), cu_host=B.p(z), q=None, k=None, v=None,
                     g=None, b=None, o=None, S0=None, ST=None) == OK
+    assert B.untouched()
+
+
+def _decode_v(lib, B, variant, **kw):
+    a = dict(q=B.p(B.q), k=B.p(B.k), v=B.p(B.v), g=B.p(B.g), b=B.p(B.b), S=B.p(B.S), o=B.p(B.o),
+             N=B.N, HQK=B.HQK, HV=B.HV, dk=B.dk, dv=B.dv, dtype=1, scale=1.0)
+    a.update(kw)
+    return lib.gdn_decode_step_v(a["q"], a["k"], a["v"], a["g"], a["b"], a["S"], a["o"], a["N"],
+                                 a["HQK"], a["HV"], a["dk"], a["dv"], a["dtype"], a["scale"], variant,
+                                 None)
+
+
+def _prefill_v(lib, B, variant, **kw):
+    a = dict(q=B.p(B.q), k=B.p(B.k), v=B.p(B.v), g=B.p(B.g), b=B.p(B.b), cu=B.p(B.cu),
+             cu_host=B.p(B.cu), N=B.N, T=B.T, S0=B.p(B.S), o=B.p(B.o), ST=B.p(B.ST), HQK=B.HQK,
+             HV=B.HV, dk=B.dk, dv=B.dv, dtype=1, scale=1.0, ws=None, ws_bytes=0)
+    a.update(kw)
+    return lib.gdn_prefill_v(a["q"], a["k"], a["v"], a["g"], a["b"], a["cu"], a["cu_host"], a["N"],
+                             a["T"], a["S0"], a["o"], a["ST"], a["HQK"], a["HV"], a["dk"], a["dv"],
+                             a["dtype"], a["scale"], variant, a["ws"], a["ws_bytes"], None)
+
+
+GATED_DELTA, DELTA, GATED_LINEAR, LINEAR = 0, 1, 2, 3
+
+
+@pytest.mark.parametrize("call", [_decode_v, _prefill_v])
+@pytest.mark.parametrize("variant,kw,status", [
+    (7, {}, E_UNSUP), (-1, {}, E_UNSUP),
+    (GATED_DELTA, dict(g=None), E_NULL), (GATED_DELTA, dict(b=None), E_NULL),
+    (DELTA, dict(b=None), E_NULL), (GATED_LINEAR, dict(g=None), E_NULL),
+    (DELTA, dict(g=None, HQK=3), E_SHAPE), (LINEAR, dict(g=None, b=None, dk=48), E_UNSUP),
+    (GATED_LINEAR, dict(b=None, g=None), E_NULL),
+])
+def test_variant_rejects(lib, call, variant, kw, status):
+    B = Bufs()
+    assert call(lib, B, variant, **kw) == status
+    assert lib.gdn_last_error()
+    assert B.untouched()
+
+
+@pytest.mark.parametrize("variant", [DELTA, GATED_LINEAR, LINEAR])
+def test_variant_zero_sequences_is_a_noop(lib, variant):
+    B = Bufs()
+    z = np.zeros(1, np.int32)
+    assert _decode_v(lib, B, variant, N=0, q=None, k=None, v=None, g=None, b=None, o=None,
+                     S=None) == OK
+    assert _prefill_v(lib, B, variant, N=0, T=0, cu=B.p(z), cu_host=B.p(z), q=None, k=None, v=None,
+                      g=None, b=None, o=None, S0=None, ST=None) == OK
     assert B.untouched()
