@@ -19,6 +19,10 @@ Three statements of the method live here, all float64:
   mathematically equivalent to the loop; it gives no formulas, so they are
   derived in that function's docstring).
 
+``oracle/shell.py`` states, in float64 as well, the parts of the GatedDeltaNet
+block that touch only the scan's inputs or output (the gates from raw
+projections, the short causal convolution + SiLU, the gated RMS norm).
+
 Sources: [HB7] handbook page "7. Gated DeltaNet: the token-by-token recurrence"
 (anrans.github.io/ai-infra-handbooks/en/transformer/deltanet/, and its Chinese
 twin); [LLV] learn-llm page 13_linear_attention_viz (learn-llm.fim.ai).
