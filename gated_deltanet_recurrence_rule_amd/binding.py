@@ -29,6 +29,12 @@ VARIANTS = {"gated_delta": GDN_GATED_DELTA, "delta": GDN_DELTA, "gated_linear": 
 _lib = None
 
 
+class BlockOps(ctypes.Structure):
+    """gdn_block_ops: gates from raw projections and the gated RMS norm (include/gdn.h)."""
+    _fields_ = [("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p), ("beta_logits", ctypes.c_int32),
+                ("z", ctypes.c_void_p), ("norm_w", ctypes.c_void_p), ("norm_eps", ctypes.c_float)]
+
+
 class GdnError(RuntimeError):
     """A libgdn call returned a non-zero status."""
 
@@ -54,6 +60,10 @@ def load() -> ctypes.CDLL:
     lib.gdn_decode_step_v.argtypes = [vp, vp, vp, fp, fp, fp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
                                       ctypes.c_float, ctypes.c_int, vp]
     lib.gdn_decode_step_v.restype = ctypes.c_int
+    ops_p = ctypes.POINTER(BlockOps)
+    lib.gdn_decode_step_ex.argtypes = [vp, vp, vp, fp, fp, fp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
+                                       ctypes.c_float, ctypes.c_int, ops_p, vp]
+    lib.gdn_decode_step_ex.restype = ctypes.c_int
     lib.gdn_prefill_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, ctypes.c_int]
     lib.gdn_prefill_workspace_size.restype = sz
     lib.gdn_prefill.argtypes = [vp, vp, vp, fp, fp, vp, vp, i32, i64, fp, vp, fp, i32, i32, i32, i32,
@@ -62,6 +72,14 @@ def load() -> ctypes.CDLL:
     lib.gdn_prefill_v.argtypes = [vp, vp, vp, fp, fp, vp, vp, i32, i64, fp, vp, fp, i32, i32, i32, i32,
                                   ctypes.c_int, ctypes.c_float, ctypes.c_int, vp, sz, vp]
     lib.gdn_prefill_v.restype = ctypes.c_int
+    lib.gdn_prefill_ex.argtypes = [vp, vp, vp, fp, fp, vp, vp, i32, i64, fp, vp, fp, i32, i32, i32, i32,
+                                   ctypes.c_int, ctypes.c_float, ctypes.c_int, ops_p, vp, sz, vp]
+    lib.gdn_prefill_ex.restype = ctypes.c_int
+    lib.gdn_conv_silu.argtypes = [vp, vp, vp, vp, i32, i64, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                  ctypes.c_int, vp]
+    lib.gdn_conv_silu.restype = ctypes.c_int
+    lib.gdn_gated_rmsnorm.argtypes = [vp, vp, vp, ctypes.c_float, vp, i64, i32, ctypes.c_int, vp]
+    lib.gdn_gated_rmsnorm.restype = ctypes.c_int
     lib.gdn_status_str.argtypes = [ctypes.c_int]
     lib.gdn_status_str.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
@@ -109,6 +127,22 @@ def _need_opt(t: Optional[torch.Tensor], name: str, dtype):
         _need(t, name, dtype)
 
 
+def _block_ops(A_log, dt_bias, beta_logits, z, norm_w, norm_eps, io_dtype):
+    """A BlockOps for the given parts, or None when none is asked for."""
+    if A_log is None and dt_bias is None and not beta_logits and z is None:
+        return None
+    _need_opt(A_log, "A_log", torch.float32)
+    _need_opt(dt_bias, "dt_bias", torch.float32)
+    _need_opt(z, "z", io_dtype)
+    _need_opt(norm_w, "norm_w", torch.float32)
+    if dt_bias is not None and A_log is None:
+        raise ValueError("dt_bias is only used with A_log")
+    return BlockOps(None if A_log is None else A_log.data_ptr(),
+                    None if dt_bias is None else dt_bias.data_ptr(), 1 if beta_logits else 0,
+                    None if z is None else z.data_ptr(), None if norm_w is None else norm_w.data_ptr(),
+                    float(norm_eps))
+
+
 def _need(t: torch.Tensor, name: str, dtype=None):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
@@ -120,13 +154,16 @@ def _need(t: torch.Tensor, name: str, dtype=None):
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch.Tensor],
                 beta: Optional[torch.Tensor], S: torch.Tensor, *, scale: float = 1.0,
-                o: Optional[torch.Tensor] = None, variant="gated_delta") -> torch.Tensor:
+                o: Optional[torch.Tensor] = None, variant="gated_delta", A_log=None, dt_bias=None,
+                beta_logits: bool = False, z=None, norm_w=None, norm_eps: float = 1e-6) -> torch.Tensor:
     """One token for every sequence and V head; S [N, HV, dk, dv] fp32 is updated in place.
 
     q, k [N, HQK, dk]; v [N, HV, dv] (bf16 or fp32, one type); g, beta [N, HV] fp32.
     Returns o [N, HV, dv] in v's dtype.  variant: "gated_delta" (default), "delta",
     "gated_linear" or "linear" (gdn_variant); the library decides which of g / beta
-    may be None for it.
+    may be None for it.  Block parts (gdn_block_ops): A_log, dt_bias [HV] fp32 make g the
+    raw decay projection; beta_logits makes beta the raw projection b; z [N, HV, dv] with
+    norm_w [dv] and norm_eps applies the gated RMS norm to o.
     """
     N, HQK, dk = q.shape
     HV, dv = v.shape[1], v.shape[2]
@@ -140,9 +177,12 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[t
     _need(o, "o", v.dtype)
     var = _variant_code(variant)
     lib = load()
+    ops = _block_ops(A_log, dt_bias, beta_logits, z, norm_w, norm_eps, v.dtype)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(o), N, HQK, HV, dk, dv,
             _dtype_code(q), float(scale))
-    if var == GDN_GATED_DELTA:
+    if ops is not None:
+        _check(lib.gdn_decode_step_ex(*args, var, ctypes.byref(ops), _stream(q.device)))
+    elif var == GDN_GATED_DELTA:
         _check(lib.gdn_decode_step(*args, _stream(q.device)))
     else:
         _check(lib.gdn_decode_step_v(*args, var, _stream(q.device)))
@@ -161,14 +201,15 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch
             scale: float = 1.0, o: Optional[torch.Tensor] = None,
             S_T: Optional[torch.Tensor] = None, output_state: bool = True,
             workspace: Optional[torch.Tensor] = None,
-            variant="gated_delta") -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+            variant="gated_delta", A_log=None, dt_bias=None, beta_logits: bool = False, z=None,
+            norm_w=None, norm_eps: float = 1e-6) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Whole sequences of a packed batch.
 
     q, k [total_T, HQK, dk]; v [total_T, HV, dv]; g, beta [total_T, HV] fp32.
     cu_seqlens: int32 device tensor [N + 1] (or None with N given: equal lengths).
     cu_seqlens_host: optional host copy (list / numpy / CPU tensor) for validation.
     S0 [N, HV, dk, dv] fp32 or None.  Returns (o [total_T, HV, dv], S_T or None).
-    variant: as for decode_step.
+    variant and the block parts: as for decode_step (z is [total_T, HV, dv]).
     """
     total_T, HQK, dk = q.shape
     HV, dv = v.shape[1], v.shape[2]
@@ -208,11 +249,80 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch
     var = _variant_code(variant)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), host_ptr, n_seq, total_T,
             _ptr(S0), _ptr(o), _ptr(S_T), HQK, HV, dk, dv, code, float(scale))
-    if var == GDN_GATED_DELTA:
+    ops = _block_ops(A_log, dt_bias, beta_logits, z, norm_w, norm_eps, v.dtype)
+    if ops is not None:
+        _check(lib.gdn_prefill_ex(*args, var, ctypes.byref(ops), _ptr(workspace), ws_bytes,
+                                  _stream(q.device)))
+    elif var == GDN_GATED_DELTA:
         _check(lib.gdn_prefill(*args, _ptr(workspace), ws_bytes, _stream(q.device)))
     else:
         _check(lib.gdn_prefill_v(*args, var, _ptr(workspace), ws_bytes, _stream(q.device)))
     return o, S_T
+
+
+def _host_seqlens(cu_seqlens_host, n_seq):
+    if cu_seqlens_host is None:
+        return None, None
+    import numpy as np
+    host = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
+    if host.shape[0] != n_seq + 1:
+        raise ValueError("cu_seqlens_host must have N + 1 entries")
+    return host, host.ctypes.data_as(ctypes.c_void_p)
+
+
+def conv_silu(x: torch.Tensor, w: torch.Tensor, *, HQK: int, HV: int, dk: int, dv: int,
+              cu_seqlens: Optional[torch.Tensor] = None, cu_seqlens_host=None, N: Optional[int] = None,
+              state_in: Optional[torch.Tensor] = None, state_out: Optional[torch.Tensor] = None,
+              q: Optional[torch.Tensor] = None, k: Optional[torch.Tensor] = None,
+              v: Optional[torch.Tensor] = None):
+    """Causal depthwise convolution (width 4) + SiLU of the concatenated q | k | v channels.
+
+    x [total_T, 2 HQK dk + HV dv] (bf16 or fp32); w [Ctot, 4] fp32; state_in / state_out
+    [N, 3, Ctot] in x's dtype (None: zeros / not written; they may be the same tensor).
+    Returns (q [total_T, HQK, dk], k, v [total_T, HV, dv]) in x's dtype.
+    """
+    total_T, Ct = x.shape
+    if Ct != 2 * HQK * dk + HV * dv:
+        raise ValueError("x's width must be 2 HQK dk + HV dv")
+    _need(x, "x")
+    code = _dtype_code(x)
+    _need(w, "w", torch.float32)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32)
+        n_seq = int(cu_seqlens.shape[0] - 1)
+    else:
+        if N is None:
+            raise ValueError("give cu_seqlens or N")
+        n_seq = int(N)
+    _need_opt(state_in, "state_in", x.dtype)
+    _need_opt(state_out, "state_out", x.dtype)
+    dev = x.device
+    q = torch.empty((total_T, HQK, dk), dtype=x.dtype, device=dev) if q is None else q
+    k = torch.empty((total_T, HQK, dk), dtype=x.dtype, device=dev) if k is None else k
+    v = torch.empty((total_T, HV, dv), dtype=x.dtype, device=dev) if v is None else v
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, x.dtype)
+    host, host_ptr = _host_seqlens(cu_seqlens_host, n_seq)
+    _check(load().gdn_conv_silu(_ptr(x), _ptr(w), _ptr(cu_seqlens), host_ptr, n_seq, total_T, _ptr(state_in),
+                                _ptr(state_out), _ptr(q), _ptr(k), _ptr(v), HQK, HV, dk, dv, code,
+                                _stream(dev)))
+    return q, k, v
+
+
+def gated_rmsnorm(x: torch.Tensor, z: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
+                  y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = w * x / sqrt(mean(x^2) + eps) * silu(z) over the last dimension (dv); y may be x."""
+    _need(x, "x")
+    _need(z, "z", x.dtype)
+    _need(w, "w", torch.float32)
+    if z.shape != x.shape:
+        raise ValueError("z must have x's shape")
+    dv = x.shape[-1]
+    y = torch.empty_like(x) if y is None else y
+    _need(y, "y", x.dtype)
+    _check(load().gdn_gated_rmsnorm(_ptr(x), _ptr(z), _ptr(w), float(eps), _ptr(y), x.numel() // max(dv, 1), dv,
+                                    _dtype_code(x), _stream(x.device)))
+    return y
 
 
 def prefill_kernel_name(N: int, total_T: int, HQK: int, HV: int, dk: int, dv: int,

@@ -54,6 +54,66 @@ gdn_status check_common(const void *q, const void *k, const void *v, const float
     return GDN_OK;
 }
 
+// cu_seqlens rules shared by prefill and the convolution; sets eq_len when cu_seqlens is NULL.
+gdn_status check_seqlens(const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int32_t N,
+                         int64_t total_T, int64_t *eq_len) {
+    *eq_len = 0;
+    if (cu_seqlens && !aligned(cu_seqlens, 4)) return fail(GDN_ERR_ALIGN, "cu_seqlens must be 4-byte aligned");
+    if (total_T > 0x7fffffffLL) return fail(GDN_ERR_SHAPE, "total_T must fit in int32");
+    if (cu_seqlens_host) {
+        if (N > 0 && cu_seqlens_host[0] != 0) return fail(GDN_ERR_SEQLENS, "cu_seqlens[0] must be 0");
+        for (int32_t i = 0; i < N; ++i)
+            if (cu_seqlens_host[i + 1] < cu_seqlens_host[i])
+                return fail(GDN_ERR_SEQLENS, "cu_seqlens decreases at %d", i);
+        if (N > 0 && (int64_t)cu_seqlens_host[N] != total_T)
+            return fail(GDN_ERR_SEQLENS, "cu_seqlens[N] = %d but total_T = %lld", cu_seqlens_host[N],
+                        (long long)total_T);
+    }
+    if (!cu_seqlens) {
+        if (N == 0) {
+            if (total_T != 0) return fail(GDN_ERR_SEQLENS, "N = 0 with total_T = %lld", (long long)total_T);
+        } else {
+            if (total_T % N != 0)
+                return fail(GDN_ERR_SEQLENS, "cu_seqlens is NULL and N (%d) does not divide total_T (%lld)",
+                            N, (long long)total_T);
+            *eq_len = total_T / N;
+        }
+    }
+    return GDN_OK;
+}
+
+// The optional block parts: which gates they transform, and the norm's operands.
+gdn_status check_ops(const gdn_block_ops *ops, gdn_variant variant, const float *beta, int64_t tokens) {
+    if (!ops) return GDN_OK;
+    if (ops->A_log && !variant_gated(variant))
+        return fail(GDN_ERR_UNSUPPORTED, "A_log is set but the variant has no decay");
+    if (ops->z && !(ops->norm_eps >= 0.f)) return fail(GDN_ERR_VALUE, "norm_eps must be >= 0");
+    if (tokens == 0) return GDN_OK;
+    if (ops->beta_logits && !beta) return fail(GDN_ERR_NULL, "beta_logits needs a non-NULL beta");
+    if (ops->z && !ops->norm_w) return fail(GDN_ERR_NULL, "norm_w must be non-NULL with z");
+    if (!aligned(ops->A_log, 4) || !aligned(ops->dt_bias, 4) || !aligned(ops->norm_w, 4))
+        return fail(GDN_ERR_ALIGN, "A_log, dt_bias and norm_w must be 4-byte aligned");
+    if (!aligned(ops->z, 16)) return fail(GDN_ERR_ALIGN, "z must be 16-byte aligned");
+    return GDN_OK;
+}
+
+// [a, a + na) and [b, b + nb) overlap without being the same start
+bool partial_overlap(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || a == b) return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+gdn::GateArgs gate_args(const gdn_block_ops *ops, gdn_variant variant) {
+    gdn::GateArgs ga;
+    if (ops) {
+        ga.A_log = variant_gated(variant) ? ops->A_log : nullptr;
+        ga.dt_bias = ga.A_log ? ops->dt_bias : nullptr;
+        ga.beta_logit = ops->beta_logits ? 1 : 0;
+    }
+    return ga;
+}
+
 gdn_status hip_status(hipError_t e, const char *what) {
     if (e == hipSuccess) return GDN_OK;
     return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -74,13 +134,15 @@ const char *gdn_status_str(gdn_status s) {
         case GDN_ERR_SEQLENS: return "bad sequence lengths";
         case GDN_ERR_WORKSPACE: return "workspace too small";
         case GDN_ERR_HIP: return "HIP runtime error";
+        case GDN_ERR_ALIAS: return "overlapping buffers";
+        case GDN_ERR_VALUE: return "argument out of range";
     }
     return "unknown status";
 }
 
 const char *gdn_last_error(void) { return g_last_error; }
 
-int32_t gdn_version(void) { return 100; /* 0.1.0 */ }
+int32_t gdn_version(void) { return 200; /* 0.2.0 */ }
 
 gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
                            const float *beta, float *S, void *o, int32_t N, int32_t HQK,
@@ -94,15 +156,35 @@ gdn_status gdn_decode_step_v(const void *q, const void *k, const void *v, const 
                              const float *beta, float *S, void *o, int32_t N, int32_t HQK,
                              int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype, float scale,
                              gdn_variant variant, hipStream_t stream) {
+    return gdn_decode_step_ex(q, k, v, g, beta, S, o, N, HQK, HV, dk, dv, dtype, scale, variant, nullptr,
+                              stream);
+}
+
+gdn_status gdn_decode_step_ex(const void *q, const void *k, const void *v, const float *g,
+                              const float *beta, float *S, void *o, int32_t N, int32_t HQK,
+                              int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype, float scale,
+                              gdn_variant variant, const gdn_block_ops *ops, hipStream_t stream) {
     g_last_error[0] = 0;
     gdn_status st = check_common(q, k, v, g, beta, o, N, HQK, HV, dk, dv, dtype, N, variant);
     if (st != GDN_OK) return st;
+    st = check_ops(ops, variant, beta, N);
+    if (st != GDN_OK) return st;
+    if (ops && ops->z) {
+        const size_t ob = (size_t)N * HV * dv * (dtype == GDN_BF16 ? 2 : 4);
+        if (partial_overlap(ops->z, ob, o, ob)) return fail(GDN_ERR_ALIAS, "z partly overlaps o");
+    }
     if (N == 0) return GDN_OK;
     if (!S) return fail(GDN_ERR_NULL, "S must be non-NULL");
     if (!aligned(S, 16)) return fail(GDN_ERR_ALIGN, "S must be 16-byte aligned");
     if ((int64_t)N * HV > 0x7fffffffLL) return fail(GDN_ERR_SHAPE, "N * HV exceeds the grid limit");
     gdn::DecodeArgs a{q, k, v, variant_gated(variant) ? g : nullptr, beta, S, o, N, HQK, HV, dk, dv, scale,
                       variant_delta(variant) ? 1 : 0};
+    a.gate = gate_args(ops, variant);
+    if (ops && ops->z) {
+        a.z = ops->z;
+        a.norm_w = ops->norm_w;
+        a.norm_eps = ops->norm_eps;
+    }
     return hip_status(gdn::launch_decode(a, dtype == GDN_BF16, stream), "decode launch");
 }
 
@@ -130,36 +212,34 @@ gdn_status gdn_prefill_v(const void *q, const void *k, const void *v, const floa
                          const float *S0, void *o, float *S_T, int32_t HQK, int32_t HV, int32_t dk,
                          int32_t dv, gdn_dtype dtype, float scale, gdn_variant variant, void *workspace,
                          size_t workspace_bytes, hipStream_t stream) {
+    return gdn_prefill_ex(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, N, total_T, S0, o, S_T, HQK, HV, dk, dv,
+                          dtype, scale, variant, nullptr, workspace, workspace_bytes, stream);
+}
+
+gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const int32_t *cu_seqlens,
+                          const int32_t *cu_seqlens_host, int32_t N, int64_t total_T,
+                          const float *S0, void *o, float *S_T, int32_t HQK, int32_t HV, int32_t dk,
+                          int32_t dv, gdn_dtype dtype, float scale, gdn_variant variant,
+                          const gdn_block_ops *ops, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
     g_last_error[0] = 0;
     if (total_T < 0) return fail(GDN_ERR_SHAPE, "total_T = %lld is negative", (long long)total_T);
     gdn_status st = check_common(q, k, v, g, beta, o, N, HQK, HV, dk, dv, dtype, total_T, variant);
     if (st != GDN_OK) return st;
+    st = check_ops(ops, variant, beta, total_T);
+    if (st != GDN_OK) return st;
+    if (ops && ops->z) {
+        // the norm runs in place on o after the scan, reading z
+        const size_t ob = (size_t)total_T * HV * dv * (dtype == GDN_BF16 ? 2 : 4);
+        if (ops->z == o || partial_overlap(ops->z, ob, o, ob)) return fail(GDN_ERR_ALIAS, "z overlaps o");
+    }
     if (S0 && !aligned(S0, 16)) return fail(GDN_ERR_ALIGN, "S0 must be 16-byte aligned");
     if (S_T && !aligned(S_T, 16)) return fail(GDN_ERR_ALIGN, "S_T must be 16-byte aligned");
-    if (cu_seqlens && !aligned(cu_seqlens, 4)) return fail(GDN_ERR_ALIGN, "cu_seqlens must be 4-byte aligned");
     if ((int64_t)N * HV > 0x7fffffffLL) return fail(GDN_ERR_SHAPE, "N * HV exceeds the grid limit");
-    if (total_T > 0x7fffffffLL) return fail(GDN_ERR_SHAPE, "total_T must fit in int32");
-
     int64_t eq_len = 0;
-    if (cu_seqlens_host) {
-        if (N > 0 && cu_seqlens_host[0] != 0) return fail(GDN_ERR_SEQLENS, "cu_seqlens[0] must be 0");
-        for (int32_t i = 0; i < N; ++i)
-            if (cu_seqlens_host[i + 1] < cu_seqlens_host[i])
-                return fail(GDN_ERR_SEQLENS, "cu_seqlens decreases at %d", i);
-        if (N > 0 && (int64_t)cu_seqlens_host[N] != total_T)
-            return fail(GDN_ERR_SEQLENS, "cu_seqlens[N] = %d but total_T = %lld", cu_seqlens_host[N],
-                        (long long)total_T);
-    }
-    if (!cu_seqlens) {
-        if (N == 0) {
-            if (total_T != 0) return fail(GDN_ERR_SEQLENS, "N = 0 with total_T = %lld", (long long)total_T);
-        } else {
-            if (total_T % N != 0)
-                return fail(GDN_ERR_SEQLENS, "cu_seqlens is NULL and N (%d) does not divide total_T (%lld)",
-                            N, (long long)total_T);
-            eq_len = total_T / N;
-        }
-    }
+    st = check_seqlens(cu_seqlens, cu_seqlens_host, N, total_T, &eq_len);
+    if (st != GDN_OK) return st;
     const size_t need = gdn_prefill_workspace_size(N, total_T, HQK, HV, dk, dv, dtype);
     if (workspace_bytes < need)
         return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
@@ -187,10 +267,62 @@ gdn_status gdn_prefill_v(const void *q, const void *k, const void *v, const floa
     gdn::PrefillArgs a{q, k, v, variant_gated(variant) ? g : nullptr, beta, cu_seqlens, order, eq_len, N,
                        total_T, S0, o, S_T, HQK, HV, dk, dv, scale, workspace, workspace_bytes,
                        variant_delta(variant) ? 1 : 0};
+    a.gate = gate_args(ops, variant);
     const bool bf16 = dtype == GDN_BF16;
     if (gdn::prefill_chunked_supported(dk, dv, bf16))
-        return hip_status(gdn::launch_prefill_chunked(a, stream), "chunked prefill launch");
-    return hip_status(gdn::launch_prefill_recurrent(a, bf16, stream), "prefill launch");
+        st = hip_status(gdn::launch_prefill_chunked(a, stream), "chunked prefill launch");
+    else
+        st = hip_status(gdn::launch_prefill_recurrent(a, bf16, stream), "prefill launch");
+    if (st != GDN_OK || !ops || !ops->z || total_T == 0) return st;
+    gdn::NormArgs na{o, ops->z, ops->norm_w, o, total_T * HV, dv, ops->norm_eps};
+    return hip_status(gdn::launch_gated_rmsnorm(na, bf16, stream), "gated norm launch");
+}
+
+gdn_status gdn_conv_silu(const void *x, const float *w, const int32_t *cu_seqlens,
+                         const int32_t *cu_seqlens_host, int32_t N, int64_t total_T,
+                         const void *state_in, void *state_out, void *q, void *k, void *v,
+                         int32_t HQK, int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype,
+                         hipStream_t stream) {
+    g_last_error[0] = 0;
+    if (dtype != GDN_BF16 && dtype != GDN_F32) return fail(GDN_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+    if (N < 0 || total_T < 0) return fail(GDN_ERR_SHAPE, "N and total_T must be >= 0");
+    if (HQK <= 0 || HV <= 0) return fail(GDN_ERR_SHAPE, "head counts must be positive (HQK=%d, HV=%d)", HQK, HV);
+    if (!dim_ok(dk) || !dim_ok(dv))
+        return fail(GDN_ERR_UNSUPPORTED, "dk=%d, dv=%d: each must be 32, 64 or 128", dk, dv);
+    const int64_t Ct = 2 * (int64_t)HQK * dk + (int64_t)HV * dv;
+    if (Ct > (1LL << 30)) return fail(GDN_ERR_SHAPE, "2 HQK dk + HV dv = %lld channels is too many", (long long)Ct);
+    int64_t eq_len = 0;
+    gdn_status st = check_seqlens(cu_seqlens, cu_seqlens_host, N, total_T, &eq_len);
+    if (st != GDN_OK) return st;
+    if (N == 0) return GDN_OK;
+    if (total_T > 0 && (!x || !w || !q || !k || !v)) return fail(GDN_ERR_NULL, "x, w, q, k and v must be non-NULL");
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+        !aligned(state_in, 16) || !aligned(state_out, 16))
+        return fail(GDN_ERR_ALIGN, "x, w, q, k, v and the states must be 16-byte aligned");
+    const size_t es = dtype == GDN_BF16 ? 2 : 4;
+    const size_t sbytes = (size_t)N * 3 * (size_t)Ct * es;
+    if (partial_overlap(state_in, sbytes, state_out, sbytes))
+        return fail(GDN_ERR_ALIAS, "state_out overlaps state_in without being the same buffer");
+    gdn::ConvArgs a{x, w, cu_seqlens, eq_len, N, total_T, state_in, state_out, q, k, v, HQK * dk, HV * dv};
+    return hip_status(gdn::launch_conv_silu(a, dtype == GDN_BF16, stream), "conv launch");
+}
+
+gdn_status gdn_gated_rmsnorm(const void *x, const void *z, const float *w, float eps, void *y,
+                             int64_t rows, int32_t dv, gdn_dtype dtype, hipStream_t stream) {
+    g_last_error[0] = 0;
+    if (dtype != GDN_BF16 && dtype != GDN_F32) return fail(GDN_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+    if (rows < 0) return fail(GDN_ERR_SHAPE, "rows = %lld is negative", (long long)rows);
+    if (!dim_ok(dv)) return fail(GDN_ERR_UNSUPPORTED, "dv=%d must be 32, 64 or 128", dv);
+    if (!(eps >= 0.f)) return fail(GDN_ERR_VALUE, "eps must be >= 0");
+    if (rows == 0) return GDN_OK;
+    if (!x || !z || !w || !y) return fail(GDN_ERR_NULL, "x, z, w and y must be non-NULL");
+    if (!aligned(x, 16) || !aligned(z, 16) || !aligned(y, 16) || !aligned(w, 4))
+        return fail(GDN_ERR_ALIGN, "x, z and y must be 16-byte aligned, w 4-byte");
+    const size_t bytes = (size_t)rows * dv * (dtype == GDN_BF16 ? 2 : 4);
+    if (partial_overlap(x, bytes, y, bytes) || partial_overlap(z, bytes, y, bytes) || z == y)
+        return fail(GDN_ERR_ALIAS, "y may be x, but must not otherwise overlap x or z");
+    gdn::NormArgs a{x, z, w, y, rows, dv, eps};
+    return hip_status(gdn::launch_gated_rmsnorm(a, dtype == GDN_BF16, stream), "gated norm launch");
 }
 
 const char *gdn_prefill_kernel_name(int32_t N, int64_t total_T, int32_t HQK, int32_t HV, int32_t dk,

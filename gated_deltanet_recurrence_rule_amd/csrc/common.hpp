@@ -46,6 +46,19 @@ __device__ __forceinline__ float inv_norm(float ss) {
     return ss > 1e-24f ? __builtin_amdgcn_rsqf(ss) : 1e12f;
 }
 
+// ------------------------------------------------------------------ gates and activations
+// The GatedDeltaNet block's gate maps (handbook page "7. Gated DeltaNet: the token-by-token
+// recurrence", parts table): log-decay -exp(A_log) softplus(a + dt_bias), write strength
+// sigmoid(b), output gate silu(z).  The per-(token, head) gate maps go through the device
+// math library; silu, applied to every element of the streamed block parts, uses the
+// hardware exp2 and reciprocal (about 1 ulp each): x / (1 + 2^(-x log2 e)).  Very negative
+// x gives 2^(+big) = inf and a reciprocal of 0, so silu -> -0 as it should.
+__device__ __forceinline__ float softplus_f(float x) { return x > 20.f ? x : log1pf(expf(x)); }
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
+__device__ __forceinline__ float silu_f(float x) {
+    return x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x * -1.44269504088896341f));
+}
+
 // ------------------------------------------------------------------ streaming access
 // The state is touched exactly once per decode step: keep it out of the caches.
 __device__ __forceinline__ f32x4 ld_stream(const float *p) {

@@ -32,7 +32,8 @@ template <int DK, int DV, typename T>
 __global__ __launch_bounds__(4 * DV) void decode_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float *__restrict__ S,
-    T *__restrict__ o, int HV, int rep, float scale, int delta) {
+    T *__restrict__ o, int HV, int rep, float scale, int delta, GateArgs gate,
+    const T *__restrict__ z, const float *__restrict__ norm_w, float norm_eps) {
     constexpr int NQ = DV / 4;          // column quads
     constexpr int NT = NQ * kRowGroups; // threads
     constexpr int RPT = DK / kRowGroups;
@@ -44,6 +45,7 @@ __global__ __launch_bounds__(4 * DV) void decode_kernel(
     __shared__ float part_s[NW][2][DV];  // per-wave partial S^T k and S^T q
     __shared__ float d_s[DV];
     __shared__ float qk_s;
+    __shared__ float ss_s[(DV + 63) / 64];
 
     const int unit = blockIdx.x;  // n * HV + h
     const int h = unit % HV;
@@ -62,8 +64,13 @@ __global__ __launch_bounds__(4 * DV) void decode_kernel(
 #pragma unroll
     for (int m = 0; m < RPT; ++m) s[m] = ld_stream(Sp + (size_t)(rg + kRowGroups * m) * DV + 4 * cq);
 
-    const float a = g ? expf(g[unit]) : 1.f;
-    const float b = beta ? beta[unit] : 1.f;
+    float a = 1.f, b = 1.f;
+    if (g) {
+        float x = g[unit];
+        if (gate.A_log) x = -expf(gate.A_log[h]) * softplus_f(x + (gate.dt_bias ? gate.dt_bias[h] : 0.f));
+        a = expf(x);
+    }
+    if (beta) b = gate.beta_logit ? sigmoid_f(beta[unit]) : beta[unit];
 
     // Wave 0: normalise this token's q and k (shared by the `rep` V heads of QK head hq).
     if (wave == 0) {
@@ -122,6 +129,8 @@ __global__ __launch_bounds__(4 * DV) void decode_kernel(
     (void)RG_PER_WAVE;
     __syncthreads();
 
+    float oj = 0.f;
+    const size_t vo = (size_t)unit * DV + tid;
     if (tid < DV) {
         const int j = tid;
         float ak = 0.f, aq = 0.f;
@@ -130,12 +139,25 @@ __global__ __launch_bounds__(4 * DV) void decode_kernel(
             ak += part_s[w][0][j];
             aq += part_s[w][1][j];
         }
-        const size_t vo = (size_t)unit * DV + j;
         const float d = b * (elem<T>::ld(v + vo) - (delta ? a * ak : 0.f));
         d_s[j] = d;
-        elem<T>::st(o + vo, a * aq + qk_s * d);
+        oj = a * aq + qk_s * d;
+        if (!z) elem<T>::st(o + vo, oj);
+    }
+    if (z && wave < (DV + 63) / 64) {
+        const float ss = wave_sum(tid < DV ? oj * oj : 0.f);
+        if (lane == 0) ss_s[wave] = ss;
     }
     __syncthreads();
+
+    // Gated RMS norm of the read (the block's output gate), in fp32 before the one rounding.
+    if (z && tid < DV) {
+        float ss = 0.f;
+#pragma unroll
+        for (int w = 0; w < (DV + 63) / 64; ++w) ss += ss_s[w];
+        const float r = __builtin_amdgcn_rsqf(ss * (1.f / DV) + norm_eps);
+        elem<T>::st(o + vo, norm_w[tid] * (oj * r) * silu_f(elem<T>::ld(z + vo)));
+    }
 
     // Write pass: S <- a S + k d^T.
     const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&d_s[4 * cq]);
@@ -153,7 +175,7 @@ hipError_t launch(const DecodeArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((decode_kernel<DK, DV, T>), grid, dim3(4 * DV), 0, stream,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), a.g, a.beta, a.S, static_cast<T *>(a.o), a.HV,
-                       rep, a.scale, a.delta);
+                       rep, a.scale, a.delta, a.gate, static_cast<const T *>(a.z), a.norm_w, a.norm_eps);
     return hipGetLastError();
 }
 

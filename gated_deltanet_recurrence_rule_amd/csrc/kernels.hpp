@@ -6,6 +6,14 @@
 
 namespace gdn {
 
+// Gates from raw projections: with A_log set, g holds the raw decay projection a and the
+// log-decay is -exp(A_log[h]) softplus(a + dt_bias[h]) (dt_bias may be null = 0); with
+// beta_logit set, beta holds the raw projection b and the write strength is sigmoid(b).
+struct GateArgs {
+    const float *A_log = nullptr, *dt_bias = nullptr;
+    int32_t beta_logit = 0;
+};
+
 // Arguments shared by the launchers, already validated by the C-ABI layer.
 // g == nullptr means a = 1 (no decay); beta == nullptr means b = 1; delta == 0 drops the
 // look-up (the write is b v instead of b (v - a S^T k)).
@@ -17,6 +25,11 @@ struct DecodeArgs {
     int32_t N, HQK, HV, dk, dv;
     float scale;
     int32_t delta;
+    GateArgs gate = {};
+    // gated RMS norm of the read (z == nullptr: none): o <- w o / sqrt(mean(o^2) + eps) silu(z)
+    const void *z = nullptr;
+    const float *norm_w = nullptr;
+    float norm_eps = 0.f;
 };
 
 struct PrefillArgs {
@@ -35,10 +48,41 @@ struct PrefillArgs {
     void *workspace;
     size_t workspace_bytes;
     int32_t delta;
+    GateArgs gate = {};
+};
+
+// Gated RMS norm over rows of dv values (rows = tokens x heads; z rows alike; w [dv]):
+// y = w x / sqrt(mean(x^2) + eps) silu(z).  y may equal x.
+struct NormArgs {
+    const void *x, *z;
+    const float *w;
+    void *y;
+    int64_t rows;
+    int32_t dv;
+    float eps;
+};
+
+// Causal depthwise convolution of width 4 + SiLU over the concatenated q | k | v channels
+// (Ctot = 2 HQK dk + HV dv), written out as separate q, k, v.  state_in / state_out
+// [N, 3, Ctot] hold the three inputs before / at the end of each sequence (null: zeros /
+// not written).  cu_seqlens as for prefill.
+struct ConvArgs {
+    const void *x;
+    const float *w;  // [Ctot, 4], w[c][3] weighs the current token
+    const int32_t *cu_seqlens;
+    int64_t eq_len;
+    int32_t N;
+    int64_t total_T;
+    const void *state_in;
+    void *state_out;
+    void *q, *k, *v;
+    int32_t Cq, Cv;  // HQK dk, HV dv
 };
 
 // Each returns hipSuccess or the launch error.  `bf16` selects the I/O type.
 hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t stream);
+hipError_t launch_gated_rmsnorm(const NormArgs &a, bool bf16, hipStream_t stream);
+hipError_t launch_conv_silu(const ConvArgs &a, bool bf16, hipStream_t stream);
 hipError_t launch_prefill_recurrent(const PrefillArgs &a, bool bf16, hipStream_t stream);
 
 // Longest-first order of the N sequences of cu_seqlens (device) into order[N] (device).

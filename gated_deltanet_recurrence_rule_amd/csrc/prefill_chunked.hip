@@ -206,7 +206,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     const float *__restrict__ g, const float *__restrict__ beta,
     const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ order, int64_t eq_len,
     const float *__restrict__ S0, uint16_t *__restrict__ o, float *__restrict__ S_T, int HV, int DV,
-    int rep, int NG, int M, float scale) {
+    int rep, int NG, int M, float scale, GateArgs gate) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
     // Everything belonging to chunk c lives in the buffers of parity c % 2: K and Q rows, K^T,
     // the per-token scalars, and the solve / read operands built from them.  Scalars:
@@ -509,6 +509,11 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     // times the 16-byte segment s = gt % 16 of their q and k rows (d = 8 s .. 8 s + 7).
     uint4 kreg[2][2], qreg[2][2];  // [p][token of the pair]
     float greg = 0.f, breg = 0.f;  // Gram wave 3: token = lane
+    // gates from raw projections: the head's exp(A_log) and dt_bias (padding tokens carry
+    // -inf raw values, which both maps send to 0)
+    const float g_ea = gate.A_log ? expf(gate.A_log[h]) : 0.f;
+    const float g_dtb = gate.dt_bias ? gate.dt_bias[h] : 0.f;
+    const bool g_raw = gate.A_log != nullptr, b_raw = gate.beta_logit != 0;
     const size_t rs = (size_t)HQK * DK;  // token stride of q and k
     // token row of item (p, u) = 8 gw + 32 p + u (uniform) + 2 lq (lane)
     const int gwu = wu - 4;
@@ -554,11 +559,13 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             breg = ok ? 1.f : 0.f;
             if (g) {
                 const rsrc_t gr = make_rsrc(g + (size_t)cs * HV + h, gbytes);
-                greg = ok ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gr, goff, 0, 0)) : 0.f;
+                greg = ok ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gr, goff, 0, 0))
+                          : (gate.A_log ? -INFINITY : 0.f);
             }
             if (beta) {
                 const rsrc_t br = make_rsrc(beta + (size_t)cs * HV + h, gbytes);
-                breg = ok ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(br, goff, 0, 0)) : 0.f;
+                breg = ok ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(br, goff, 0, 0))
+                          : (gate.beta_logit ? -INFINITY : 0.f);
             }
         }
     };
@@ -621,7 +628,15 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         if (gw == 3) {
             // inclusive prefix sum over the 64 lanes: within rows of 16 by row shifts, then
             // across rows by the row-15 and row-31 broadcasts (DPP, no LDS traffic)
-            float x = greg * 1.44269504088896341f;  // log2(e)
+            // raw gates, straight-line so the staging above can hide them: softplus(t) =
+            // max(t, 0) + ln(1 + e^-|t|) and sigmoid(b) = 1 / (1 + e^-b) on the hardware exp2,
+            // log2 and reciprocal (when 1 + e^-|t| rounds to 1 the term dropped is < 6e-8)
+            const float tt = greg + g_dtb;
+            const float sp = fmaxf(tt, 0.f) +
+                             0.69314718055994531f * __builtin_amdgcn_logf(1.f + exp2_hw(-1.44269504088896341f * fabsf(tt)));
+            const float gl = g_raw ? -g_ea * sp : greg;
+            breg = b_raw ? __builtin_amdgcn_rcpf(1.f + exp2_hw(-1.44269504088896341f * breg)) : breg;
+            float x = gl * 1.44269504088896341f;  // log2(e)
 #define GDN_DPP_ADD(ctrl, row_mask) \
     x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, row_mask, 0xF, true))
             GDN_DPP_ADD(0x111, 0xF);  // row_shr:1
@@ -914,7 +929,7 @@ hipError_t launch_prefill_chunked(const PrefillArgs &a, hipStream_t stream) {
                        dim3(NT), 0, stream,
                        static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
                        static_cast<const uint16_t *>(a.v), a.g, a.beta, a.cu_seqlens, a.order, a.eq_len,
-                       a.S0, static_cast<uint16_t *>(a.o), a.S_T, a.HV, a.dv, rep, (int)NG, (int)M, a.scale);
+                       a.S0, static_cast<uint16_t *>(a.o), a.S_T, a.HV, a.dv, rep, (int)NG, (int)M, a.scale, a.gate);
     return hipGetLastError();
 }
 

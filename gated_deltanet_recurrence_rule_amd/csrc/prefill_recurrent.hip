@@ -27,7 +27,7 @@ __global__ __launch_bounds__(64) void prefill_recurrent_kernel(
     const float *__restrict__ g, const float *__restrict__ beta,
     const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ order, int64_t eq_len,
     const float *__restrict__ S0, T *__restrict__ o, float *__restrict__ S_T, int HV, int DV, int rep,
-    float scale, int delta) {
+    float scale, int delta, GateArgs gate) {
     constexpr int EPL = (DK + 63) / 64;  // q/k elements per lane
     __shared__ float kh_s[DK];
     __shared__ float qh_s[DK];
@@ -88,8 +88,13 @@ __global__ __launch_bounds__(64) void prefill_recurrent_kernel(
         __syncthreads();
 
         const size_t tv = (size_t)t * HV + h;
-        const float a = g ? expf(g[tv]) : 1.f;
-        const float b = beta ? beta[tv] : 1.f;
+        float a = 1.f, b = 1.f;
+        if (g) {
+            float x = g[tv];
+            if (gate.A_log) x = -expf(gate.A_log[h]) * softplus_f(x + (gate.dt_bias ? gate.dt_bias[h] : 0.f));
+            a = expf(x);
+        }
+        if (beta) b = gate.beta_logit ? sigmoid_f(beta[tv]) : beta[tv];
         const float vj = active ? elem<T>::ld(v + tv * DV + j) : 0.f;
 
         float p = 0.f, r = 0.f;
@@ -118,7 +123,7 @@ hipError_t launch(const PrefillArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((prefill_recurrent_kernel<DK, T>), grid, dim3(64), 0, stream,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), a.g, a.beta, a.cu_seqlens, a.order, a.eq_len, a.S0,
-                       static_cast<T *>(a.o), a.S_T, a.HV, a.dv, rep, a.scale, a.delta);
+                       static_cast<T *>(a.o), a.S_T, a.HV, a.dv, rep, a.scale, a.delta, a.gate);
     return hipGetLastError();
 }
 

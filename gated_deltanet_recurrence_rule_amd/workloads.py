@@ -245,3 +245,75 @@ def random_small(seed: int, seqlens, HQK: int, HV: int, dk: int, dv: int, dtype:
     """Small random batch for parity tests (any lengths, including zero)."""
     return make_inputs("random", seed, seqlens, HQK, HV, dk, dv, dtype, g_mu, g_sd,
                        0.05 if s0 else None, p_g0=p_g0, p_beta1=p_beta1)
+
+
+# ---------------------------------------------------------------- the block around the scan
+@dataclasses.dataclass
+class BlockInputs:
+    """Raw inputs of the GatedDeltaNet block's parts around the scan.
+
+      x          [total_T, 2 HQK dk + HV dv]  concatenated q | k | v channels before the
+                                              short convolution (bf16 bits or float32)
+      conv_w     [Ctot, 4] float32            convolution weights, column 3 = current token
+      conv_state [N, 3, Ctot] or None         the three inputs before each sequence
+      a, b       [total_T, HV] float32        raw decay / write-strength projections
+      A_log, dt_bias [HV] float32             per-head decay parameters
+      z          [total_T, HV, dv]            output gate (bf16 bits or float32)
+      norm_w     [dv] float32                 gated-norm weight
+    """
+
+    dtype: str
+    x: np.ndarray
+    conv_w: np.ndarray
+    conv_state: Optional[np.ndarray]
+    a: np.ndarray
+    b: np.ndarray
+    A_log: np.ndarray
+    dt_bias: np.ndarray
+    z: np.ndarray
+    norm_w: np.ndarray
+    cu_seqlens: np.ndarray
+    HQK: int
+    HV: int
+    dk: int
+    dv: int
+
+    def as_f64(self, name: str) -> np.ndarray:
+        a = getattr(self, name)
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            a = bf16_bits_to_f32(a)
+        return a.astype(np.float64)
+
+
+def block_inputs(seed: int, seqlens, HQK: int, HV: int, dk: int, dv: int, dtype: str = BF16,
+                 conv_state: bool = True) -> BlockInputs:
+    """Synthetic raw projections and block parameters.
+
+    Recipe: x, z ~ N(0, 1); conv weights ~ U(-0.5, 0.5) (the default initialisation range
+    of a width-4 depthwise convolution); a, b ~ N(0, 1); exp(A_log) ~ U(0.01, 1.3) (the
+    handbook page "7. Gated DeltaNet: the token-by-token recurrence", section "Run it",
+    prints per-head forgetting speeds exp(A_log) from 0.00 to 1.29); dt_bias ~ N(1, 0.5)
+    around the block's initial value 1; norm weight 1 + N(0, 0.1) around its initial 1;
+    conv state ~ N(0, 1).
+    """
+    seqlens = np.asarray(seqlens, dtype=np.int64)
+    cu = np.zeros(len(seqlens) + 1, dtype=np.int64)
+    np.cumsum(seqlens, out=cu[1:])
+    T, N = int(cu[-1]), len(seqlens)
+    Ct = 2 * HQK * dk + HV * dv
+    io = np.uint16 if dtype == BF16 else np.float32
+    normal = lambda r, s: _pack(r.standard_normal(s, dtype=np.float32), dtype)
+    x = _fill_blocks(seed, 10, (T, Ct), io, normal)
+    z = _fill_blocks(seed, 11, (T, HV, dv), io, normal)
+    a = _fill_blocks(seed, 12, (T, HV), np.float32, lambda r, s: r.standard_normal(s, dtype=np.float32))
+    b = _fill_blocks(seed, 13, (T, HV), np.float32, lambda r, s: r.standard_normal(s, dtype=np.float32))
+    rng = np.random.default_rng([seed, 14])
+    conv_w = rng.uniform(-0.5, 0.5, size=(Ct, 4)).astype(np.float32)
+    A_log = np.log(rng.uniform(0.01, 1.3, size=HV)).astype(np.float32)
+    dt_bias = rng.normal(1.0, 0.5, size=HV).astype(np.float32)
+    norm_w = (1.0 + rng.normal(0.0, 0.1, size=dv)).astype(np.float32)
+    st = _fill_blocks(seed, 15, (N, 3, Ct), io, normal) if conv_state and N > 0 else None
+    return BlockInputs(dtype, x, conv_w, st, a, b, A_log, dt_bias, z, norm_w, cu.astype(np.int32),
+                       HQK, HV, dk, dv)

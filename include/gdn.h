@@ -62,7 +62,9 @@ typedef enum {
     GDN_ERR_ALIGN = -5,       /* a pointer breaks the alignment rule above             */
     GDN_ERR_SEQLENS = -6,     /* cu_seqlens_host malformed, or N does not divide T     */
     GDN_ERR_WORKSPACE = -7,   /* workspace smaller than gdn_prefill_workspace_size()   */
-    GDN_ERR_HIP = -8          /* the HIP runtime reported an error at launch           */
+    GDN_ERR_HIP = -8,         /* the HIP runtime reported an error at launch           */
+    GDN_ERR_ALIAS = -9,       /* an output partly overlaps an input it must not        */
+    GDN_ERR_VALUE = -10       /* a scalar argument out of range (e.g. norm_eps < 0)    */
 } gdn_status;
 
 typedef enum {
@@ -173,6 +175,100 @@ gdn_status gdn_prefill_v(const void *q, const void *k, const void *v, const floa
                          const float *S0, void *o, float *S_T, int32_t HQK, int32_t HV, int32_t dk,
                          int32_t dv, gdn_dtype dtype, float scale, gdn_variant variant, void *workspace,
                          size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gdn_block_ops -- optional parts of the GatedDeltaNet block run together with the scan
+ * by gdn_decode_step_ex / gdn_prefill_ex (handbook page "7. Gated DeltaNet: the
+ * token-by-token recurrence": the block's forward listing and the table of its parts).
+ * Zero-initialise, then set what is wanted; a NULL gdn_block_ops pointer means none.
+ *
+ * Gates from the raw projections (parts table, rows "in_proj_b -> sigmoid" and
+ * "in_proj_a, dt_bias, A_log"), computed in the scan kernels instead of a separate pass:
+ *   A_log       [HV] fp32 or NULL.  Non-NULL: the g array holds the raw decay projection a
+ *               and the log-decay used is  g = -exp(A_log[h]) * softplus(a + dt_bias[h])
+ *               (always <= 0).  Only for the gated variants (g is read); else
+ *               GDN_ERR_UNSUPPORTED.
+ *   dt_bias     [HV] fp32, or NULL for zeros; read only with A_log.
+ *   beta_logits non-zero: the beta array holds the raw projection b and the write strength
+ *               used is sigmoid(b).  Needs a non-NULL beta (GDN_ERR_NULL).
+ *
+ * Gated RMS norm of the read (parts table, row "in_proj_z + GatedRMSNorm"; its body is not
+ * on the page -- the reading taken is y = w * o / sqrt(mean_j o_j^2 + eps) * silu(z) over
+ * each (token, V head) vector of dv values):
+ *   z           output gate, same shape and element type as o, 16-byte aligned, or NULL
+ *               for no norm.  Non-NULL: o receives y instead of the raw read.
+ *   norm_w      [dv] fp32 weight, shared by all heads; required with z.
+ *   norm_eps    >= 0 (GDN_ERR_VALUE otherwise).
+ * Decode normalises the fp32 read before its one rounding.  Prefill runs the scan, then
+ * the norm kernel (gdn_gated_rmsnorm) in place on o: for bf16 the read is rounded once
+ * before the norm (the chunked kernel spreads a head's dv columns over workgroups, so no
+ * workgroup holds a whole vector).
+ */
+typedef struct gdn_block_ops {
+    const float *A_log;
+    const float *dt_bias;
+    int32_t beta_logits;
+    const void *z;
+    const float *norm_w;
+    float norm_eps;
+} gdn_block_ops;
+
+/* gdn_decode_step_v plus the block parts in `ops` (may be NULL). */
+gdn_status gdn_decode_step_ex(const void *q, const void *k, const void *v, const float *g,
+                              const float *beta, float *S, void *o, int32_t N, int32_t HQK,
+                              int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype, float scale,
+                              gdn_variant variant, const gdn_block_ops *ops, hipStream_t stream);
+
+/* gdn_prefill_v plus the block parts in `ops` (may be NULL); z is [total_T, HV, dv]. */
+gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const int32_t *cu_seqlens,
+                          const int32_t *cu_seqlens_host, int32_t N, int64_t total_T,
+                          const float *S0, void *o, float *S_T, int32_t HQK, int32_t HV, int32_t dk,
+                          int32_t dv, gdn_dtype dtype, float scale, gdn_variant variant,
+                          const gdn_block_ops *ops, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/*
+ * gdn_conv_silu -- the block's causal depthwise short convolution + SiLU, in front of the
+ * scan (handbook page "7. Gated DeltaNet: the token-by-token recurrence": the block listing
+ * and the parts table, row "in_proj_qkv + conv1d", with the note under the table: the
+ * output at position t uses the inputs t-3 .. t only, every channel with its own 4
+ * weights).  For every token t of sequence n and channel c:
+ *
+ *     y[t, c] = silu( w[c, 0] e[t-3, c] + w[c, 1] e[t-2, c] + w[c, 2] e[t-1, c] + w[c, 3] x[t, c] )
+ *
+ * where e is the sequence's inputs preceded by its carried state (zeros without one).
+ *   x          [total_T, Ctot] in dtype, Ctot = 2 HQK dk + HV dv: the concatenated q | k | v
+ *              channels of each token (the block's in_proj_qkv output).
+ *   w          [Ctot, 4] fp32, 16-byte aligned; w[c][3] weighs the current token.
+ *   cu_seqlens, cu_seqlens_host, N, total_T: as for gdn_prefill (NULL cu_seqlens = N equal
+ *              lengths; N sequences of one token each is a decode step).
+ *   state_in   [N, 3, Ctot] in dtype or NULL (zeros): each sequence's three previous inputs,
+ *              oldest first.
+ *   state_out  [N, 3, Ctot] or NULL (not written): the last three entries of (state ++ x)
+ *              for each sequence; an empty sequence passes its state through.  It may be
+ *              the same buffer as state_in; a partial overlap is GDN_ERR_ALIAS.
+ *   q, k       [total_T, HQK, dk] and v [total_T, HV, dv] in dtype: y split into the
+ *              arrays gdn_prefill and gdn_decode_step read.  fp32 arithmetic; bf16 outputs
+ *              rounded once to nearest even.
+ * Alignment: every array 16 bytes.  Sizes: dk, dv in {32, 64, 128}, HQK, HV > 0.
+ */
+gdn_status gdn_conv_silu(const void *x, const float *w, const int32_t *cu_seqlens,
+                         const int32_t *cu_seqlens_host, int32_t N, int64_t total_T,
+                         const void *state_in, void *state_out, void *q, void *k, void *v,
+                         int32_t HQK, int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype,
+                         hipStream_t stream);
+
+/*
+ * gdn_gated_rmsnorm -- the block's gated RMS norm on its own (see gdn_block_ops for the
+ * formula and the reading):  y[r] = w * x[r] / sqrt(mean_j x[r, j]^2 + eps) * silu(z[r])
+ * for every row r of dv values (rows = tokens x V heads).
+ *   x, z, y    [rows, dv] in dtype, 16-byte aligned; y may be x (in place), a partial
+ *              overlap of y with x or z is GDN_ERR_ALIAS.
+ *   w          [dv] fp32.   eps >= 0.   dv in {32, 64, 128}.
+ */
+gdn_status gdn_gated_rmsnorm(const void *x, const void *z, const float *w, float eps, void *y,
+                             int64_t rows, int32_t dv, gdn_dtype dtype, hipStream_t stream);
 
 /*
  * gdn_prefill_kernel_name -- which kernel gdn_prefill runs for these sizes
