@@ -9,7 +9,11 @@ in HBM:
     (512 MiB) updated in place.
 
 `value` is the prefill throughput in Mtok/s (prefill tokens / prefill time);
-the decode leg is reported beside it as state GB/s (2 |S| / time).  Kernel
+the decode leg is reported beside it as state GB/s (2 |S| / time).  Beside the
+step, "block" reports the parts of the GatedDeltaNet block around the scan on
+the same prefill batch: the causal convolution + SiLU (gdn_conv_silu), the gated
+RMS norm (gdn_gated_rmsnorm), the prefill and decode calls with the gates taken
+from raw projections (and, for decode, the norm fused).  Kernel
 times come from HIP events recorded on the stream the library launches on.
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -50,6 +54,15 @@ def decode_alg(N, HQK, HV, dk, dv, e):
     return int(bytes_), int(N * HV * 7 * dk * dv), int(N * HV * 2 * dk * dv * 4)
 
 
+def conv_alg(T, N, Ct, e):
+    """x read once, q | k | v written once, the carried state read and written."""
+    return int(2 * T * Ct * e + 2 * N * 3 * Ct * e + Ct * 16)
+
+
+def norm_alg(rows, dv, e):
+    return int(3 * rows * dv * e + dv * 4)
+
+
 def recorded_traffic(kernel: str):
     """HBM bytes per dispatch measured with rocprofv3 counters (profiles/traffic.json),
     or None when the kernel's source has changed since the counters were taken."""
@@ -77,6 +90,7 @@ def main():
     ap.add_argument("--settle-ms", type=float, default=200.0,
                     help="before the warm-up steps, run steps for at least this long so the GPU "
                          "reaches its sustained clock (untimed; 0 disables)")
+    ap.add_argument("--no-block", action="store_true", help="skip the block-parts leg")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run one 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -155,6 +169,10 @@ def main():
     dec_avg = e1.elapsed_time(e2) / args.steps
     step_ms = e0.elapsed_time(e2) / args.steps
 
+    block = None
+    if not args.no_block:
+        block = block_leg(args, binding, W, P, D, pf, dc, o_p, S_T, o_d, ws, up, dev)
+
     if args.copy_probe:
         # a plain device copy of known size, for scaling HBM counters (FETCH_SIZE/WRITE_SIZE)
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -222,9 +240,87 @@ def main():
         "roofline": pre_roof if pre_avg >= dec_avg else dec_roof,
         "roofline_prefill": pre_roof, "roofline_decode": dec_roof,
         "cpu_baseline": cpu,
+        "block": block,
         "wall_s_timed": wall,
     }
     print(json.dumps(out), flush=True)
+
+
+def block_leg(args, binding, W, P, D, pf, dc, o_p, S_T, o_d, ws, up, dev):
+    """Time the block parts on the prefill batch (K calls each between HIP events)."""
+    import torch
+
+    t0 = time.time()
+    bi = W.block_inputs(7, [pf.total_T // pf.N] * pf.N, pf.HQK, pf.HV, pf.dk, pf.dv)
+    bd = W.block_inputs(8, [1] * dc.N, dc.HQK, dc.HV, dc.dk, dc.dv)
+    log(f"block inputs generated in {time.time() - t0:.1f} s")
+    x, w, st_in = up(bi.x), up(bi.conv_w), up(bi.conv_state)
+    st_out = torch.empty_like(st_in)
+    z, nw = up(bi.z), up(bi.norm_w)
+    a, b, A_log, dt_bias = up(bi.a), up(bi.b), up(bi.A_log), up(bi.dt_bias)
+    zd, ad, bd_, nwd = up(bd.z), up(bd.a), up(bd.b), up(bd.norm_w)
+    Ad, dtd = up(bd.A_log), up(bd.dt_bias)
+    q = torch.empty_like(P["q"])
+    k = torch.empty_like(P["k"])
+    v = torch.empty_like(P["v"])
+    y = torch.empty_like(o_p)
+    T, Ct = bi.x.shape
+
+    def conv():
+        binding.conv_silu(x, w, HQK=pf.HQK, HV=pf.HV, dk=pf.dk, dv=pf.dv, cu_seqlens=P["cu"],
+                          state_in=st_in, state_out=st_out, q=q, k=k, v=v)
+
+    def norm():
+        binding.gated_rmsnorm(o_p, z, nw, 1e-6, y=y)
+
+    def prefill_raw():
+        binding.prefill(P["q"], P["k"], P["v"], a, b, cu_seqlens=P["cu"], cu_seqlens_host=pf.cu_seqlens,
+                        S0=P["S0"], o=o_p, S_T=S_T, workspace=ws, A_log=A_log, dt_bias=dt_bias,
+                        beta_logits=True)
+
+    Sd = D["S"].clone()
+
+    def decode_block():
+        binding.decode_step(D["q"], D["k"], D["v"], ad, bd_, Sd, o=o_d, A_log=Ad, dt_bias=dtd,
+                            beta_logits=True, z=zd, norm_w=nwd, norm_eps=1e-6)
+
+    stream = torch.cuda.current_stream(dev)
+    # the input generation above left the GPU idle: settle its clock again (untimed)
+    if args.settle_ms > 0:
+        t_set = time.perf_counter()
+        while (time.perf_counter() - t_set) * 1e3 < args.settle_ms:
+            conv()
+            norm()
+            prefill_raw()
+            torch.cuda.synchronize()
+    res = {}
+    for name, f in (("conv", conv), ("norm", norm), ("prefill_raw_gates", prefill_raw),
+                    ("decode_raw_gates_norm", decode_block)):
+        for _ in range(max(1, args.warmup)):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / args.steps
+    cb = conv_alg(T, pf.N, Ct, 2)
+    nb = norm_alg(pf.total_T * pf.HV, pf.dv, 2)
+
+    def hbm(bytes_, ms, key):
+        gbps = bytes_ / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": gbps / PEAK_HBM_GBPS, "traffic": recorded_traffic(key), "alg_bytes": bytes_}
+
+    return {
+        "workload": f"{pf.N} x {pf.total_T // pf.N} tokens, {Ct} conv channels (16 QK / 32 V heads, d 128), bf16",
+        "conv_silu_us": res["conv"] * 1e3, "conv_silu_roofline": hbm(cb, res["conv"], "conv_silu"),
+        "gated_rmsnorm_us": res["norm"] * 1e3, "gated_rmsnorm_roofline": hbm(nb, res["norm"], "gated_rmsnorm"),
+        "prefill_raw_gates_ms": res["prefill_raw_gates"],
+        "decode_raw_gates_norm_us": res["decode_raw_gates_norm"] * 1e3,
+    }
 
 
 if __name__ == "__main__":

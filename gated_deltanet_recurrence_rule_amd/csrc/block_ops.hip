@@ -56,7 +56,10 @@ template <> struct vec8<float> {
 // holding 8 channels; a wave covers 64 / LPR rows per step and the sum of squares is reduced
 // over the row's lanes with xor shuffles.
 constexpr int kNormThreads = 256;
-constexpr int kNormSteps = 4;  // row groups per wave
+#ifndef GDN_NORM_STEPS
+#define GDN_NORM_STEPS 1
+#endif
+constexpr int kNormSteps = GDN_NORM_STEPS;  // row groups per wave
 
 template <int DV, typename T>
 __global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(
@@ -128,7 +131,14 @@ hipError_t dispatch_norm(const NormArgs &a, hipStream_t stream) {
 // spans 2048 channels of the same tokens, so every load and store instruction of a wave
 // covers 1 KiB (bf16) of one token row.
 constexpr int kConvThreads = 256;
-constexpr int kConvTokens = 64;
+#ifndef GDN_CONV_TOKENS
+#define GDN_CONV_TOKENS 64
+#endif
+#ifndef GDN_CONV_GROUP
+#define GDN_CONV_GROUP 4
+#endif
+constexpr int kConvTokens = GDN_CONV_TOKENS;  // tokens per thread
+constexpr int kConvGroup = GDN_CONV_GROUP;    // token rows loaded before their arithmetic
 
 // sequence holding token t: the largest n with cu[n] <= t (cu non-decreasing, cu[0] = 0)
 __device__ __forceinline__ int seq_of(const int32_t *cu, int N, int64_t eq_len, int64_t t) {
@@ -215,13 +225,13 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_kernel(
             fetch(t - 1, e3);
         }
         const int64_t stop = te < s1 ? te : s1;
-        // eight rows in flight at a time, then their arithmetic
-        for (; t + 8 <= stop; t += 8) {
-            float cur[8][8];
+        // kConvGroup rows in flight at a time, then their arithmetic
+        for (; t + kConvGroup <= stop; t += kConvGroup) {
+            float cur[kConvGroup][8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) vec8<T>::ld(x + (t + u) * Ct + c, cur[u]);
+            for (int u = 0; u < kConvGroup; ++u) vec8<T>::ld(x + (t + u) * Ct + c, cur[u]);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) step(t + u, cur[u]);
+            for (int u = 0; u < kConvGroup; ++u) step(t + u, cur[u]);
         }
         for (; t < stop; ++t) {
             float cur[8];

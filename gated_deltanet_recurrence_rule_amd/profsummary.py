@@ -39,6 +39,12 @@ KERNELS = {
     "decode": ("decode_kernel<128, 128, unsigned short>", "decode.hip", "decode_b256_h32_d128.txt",
                "decode step, 256 sequences, 16 QK / 32 V heads, dk = dv = 128, bf16 q/k/v/o, "
                "fp32 state updated in place (512 MiB)"),
+    "conv_silu": ("conv_silu_kernel", "block_ops.hip", "conv_silu_4x16384_c8192.txt",
+                  "causal conv (width 4) + SiLU, 4 sequences x 16384 tokens, 8192 bf16 channels "
+                  "(q | k | v of 16 QK / 32 V heads, d = 128), carried state in and out"),
+    "gated_rmsnorm": ("gated_rmsnorm_kernel<128, unsigned short>", "block_ops.hip",
+                      "gated_rmsnorm_4x16384_h32_d128.txt",
+                      "gated RMS norm of 4 x 16384 tokens x 32 V heads (rows of 128 bf16), bf16 z"),
 }
 
 CMD_KT = ("rocprofv3 --kernel-trace --stats --output-format csv -d {kt} -o bench -- "
@@ -98,6 +104,8 @@ def main(argv=None):
     alg = {
         "prefill_chunked": bench.prefill_alg(4, 16384, 16, 32, 128, 128, 2, True)[0],
         "decode": bench.decode_alg(256, 16, 32, 128, 128, 2)[0],
+        "conv_silu": bench.conv_alg(4 * 16384, 4, 8192, 2),
+        "gated_rmsnorm": bench.norm_alg(4 * 16384 * 32, 128, 2),
     }
     cmds = [CMD_KT.format(kt=args.kt), CMD_PMC.format(ctr="FETCH_SIZE", d=args.fetch),
             CMD_PMC.format(ctr="WRITE_SIZE", d=args.write),
