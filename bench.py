@@ -21,6 +21,8 @@ from __future__ import annotations
 
 import argparse
 import json
+
+import numpy as np
 import os
 import sys
 import time
@@ -91,6 +93,10 @@ def main():
                     help="before the warm-up steps, run steps for at least this long so the GPU "
                          "reaches its sustained clock (untimed; 0 disables)")
     ap.add_argument("--no-block", action="store_true", help="skip the block-parts leg")
+    ap.add_argument("--extra-configs", action="store_true",
+                    help="also time the tiny fp32 scan, the single 8192-token sequence and the packed "
+                         "variable-length batch with its 262144-token sequence (reported under "
+                         "extra_configs; adds about a minute)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run one 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -101,7 +107,6 @@ def main():
               "multi-GPU to time here.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from gated_deltanet_recurrence_rule_amd import binding, workloads as W
@@ -151,35 +156,56 @@ def main():
     torch.cuda.synchronize()
 
     # Timed region: K prefill calls back to back, then K decode steps back to back,
-    # bracketed by HIP events on the stream the library launches on.
+    # bracketed by HIP events on the stream the library launches on (an event between
+    # calls gives the per-call times for the median and minimum).
     stream = torch.cuda.current_stream(dev)
-    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    ev_p = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev_d = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
+    ev_p[0].record(stream)
+    for i in range(args.steps):
         prefill()
-    e1.record(stream)
-    for _ in range(args.steps):
+        ev_p[i + 1].record(stream)
+    for i in range(args.steps):
         decode()
-    e2.record(stream)
+        ev_d[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    e0, e1, e2 = ev_p[0], ev_p[-1], ev_d[-1]
     pre_avg = e0.elapsed_time(e1) / args.steps
     dec_avg = e1.elapsed_time(e2) / args.steps
     step_ms = e0.elapsed_time(e2) / args.steps
+    pre_calls = sorted(ev_p[i].elapsed_time(ev_p[i + 1]) for i in range(args.steps))
+    dec_calls = sorted((ev_p[-1] if i == 0 else ev_d[i - 1]).elapsed_time(ev_d[i]) for i in range(args.steps))
 
     block = None
     if not args.no_block:
         block = block_leg(args, binding, W, P, D, pf, dc, o_p, S_T, o_d, ws, up, dev)
 
+    extra = None
+    if args.extra_configs:
+        extra = extra_leg(args, binding, W, up, dev)
+
+    # A plain 1 GiB device copy: the measured copy bandwidth reported beside the peaks, and
+    # (one call, --copy-probe) the known-size dispatch that scales the HBM counters.
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    copy_gbps = None
     if args.copy_probe:
-        # a plain device copy of known size, for scaling HBM counters (FETCH_SIZE/WRITE_SIZE)
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
-        del src, dst
+    else:
+        for _ in range(3):
+            dst.copy_(src)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(10):
+            dst.copy_(src)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        copy_gbps = 2.0 * (1 << 30) / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
+    del src, dst
 
     e = 2  # bf16 bytes
     pb, pf_chunk, pf_rec = prefill_alg(N, T, pf.HQK, pf.HV, pf.dk, pf.dv, e, True)
@@ -235,15 +261,80 @@ def main():
                                "dk=dv=128, bf16, fp32 S0) + decode step (256 sequences, same heads, "
                                "512 MiB fp32 state)",
                    "prefill_tokens": N * T, "decode_sequences": dc.N, "parallelism": "none"},
-        "prefill_ms": pre_avg, "prefill_hbm_frac": pre_hbm_frac,
-        "decode_us": dec_avg * 1e3, "decode_state_GBps": state_gbps,
+        "prefill_ms": pre_avg, "prefill_ms_median": pre_calls[len(pre_calls) // 2],
+        "prefill_ms_min": pre_calls[0], "prefill_hbm_frac": pre_hbm_frac,
+        "prefill_roofline_frac": max(pf_chunk / (PEAK_BF16_TFLOPS * 1e12), pb / (PEAK_HBM_GBPS * 1e9)) / (pre_avg * 1e-3),
+        "prefill_recurrence_TFLOPs": pf_rec / (pre_avg * 1e-3) / 1e12,
+        "decode_us": dec_avg * 1e3, "decode_us_median": dec_calls[len(dec_calls) // 2] * 1e3,
+        "decode_us_min": dec_calls[0] * 1e3, "decode_state_GBps": state_gbps,
+        "copy_GBps": copy_gbps,
         "roofline": pre_roof if pre_avg >= dec_avg else dec_roof,
         "roofline_prefill": pre_roof, "roofline_decode": dec_roof,
         "cpu_baseline": cpu,
         "block": block,
+        "extra_configs": extra,
+        "host": {"cpu": host_cpu(), "cpu_count": os.cpu_count()},
         "wall_s_timed": wall,
     }
     print(json.dumps(out), flush=True)
+
+
+def host_cpu():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def extra_leg(args, binding, W, up, dev):
+    """The other workloads, each timed over K calls between HIP events after a short settle."""
+    import torch
+
+    out = {}
+    stream = torch.cuda.current_stream(dev)
+    for name, make in (("tiny_fp32", W.tiny), ("single_8192", W.prefill), ("varlen", W.varlen)):
+        t0 = time.time()
+        inp = make()
+        log(f"{name}: inputs generated in {time.time() - t0:.1f} s")
+        d = {x: up(getattr(inp, x)) for x in ("q", "k", "v", "g", "beta")}
+        cu = up(inp.cu_seqlens)
+        S0 = None if inp.S0 is None else up(inp.S0)
+        tdt = torch.bfloat16 if inp.dtype == "bf16" else torch.float32
+        o = torch.empty((inp.total_T, inp.HV, inp.dv), dtype=tdt, device=dev)
+        ST = torch.empty((inp.N, inp.HV, inp.dk, inp.dv), dtype=torch.float32, device=dev)
+        nws = binding.prefill_workspace_size(inp.N, inp.total_T, inp.HQK, inp.HV, inp.dk, inp.dv, tdt)
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+
+        def call():
+            binding.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu,
+                            cu_seqlens_host=inp.cu_seqlens, S0=S0, o=o, S_T=ST, workspace=ws)
+
+        t_set = time.perf_counter()
+        while (time.perf_counter() - t_set) * 1e3 < max(args.settle_ms, 1.0):
+            call()
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        e = 2 if inp.dtype == "bf16" else 4
+        lens = np.diff(inp.cu_seqlens)
+        ab = sum(prefill_alg(1, int(L), inp.HQK, inp.HV, inp.dk, inp.dv, e, inp.S0 is not None)[0] for L in lens)
+        fl = sum(prefill_alg(1, int(L), inp.HQK, inp.HV, inp.dk, inp.dv, e, False)[1] for L in lens)
+        kname = binding.prefill_kernel_name(inp.N, inp.total_T, inp.HQK, inp.HV, inp.dk, inp.dv, tdt)
+        out[name] = {"sequences": inp.N, "tokens": inp.total_T, "heads": [inp.HQK, inp.HV], "d": [inp.dk, inp.dv],
+                     "dtype": inp.dtype, "kernel": kname, "ms": ms, "Mtok_s": inp.total_T / (ms * 1e-3) / 1e6,
+                     "mfma_frac": fl / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12) if "chunk" in kname else None,
+                     "hbm_frac": ab / (ms * 1e-3) / (PEAK_HBM_GBPS * 1e9)}
+        del d, o, ST, ws, S0, cu
+        torch.cuda.empty_cache()
+    return out
 
 
 def block_leg(args, binding, W, P, D, pf, dc, o_p, S_T, o_d, ws, up, dev):

@@ -9,9 +9,14 @@ Three runs feed it (each writes CSV files into its own directory):
   HBM writes     timeout -s KILL 180 rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE> -o bench -- \
                      python3 bench.py --steps 2 --warmup 1 --settle-ms 0 --no-cpu-baseline --copy-probe
 
+and, for the MFMA evidence of the prefill kernel (optional),
+
+  MFMA use       timeout -s KILL 180 rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 --output-format csv -d <MFMA> -o bench -- \
+                     python3 bench.py --steps 2 --warmup 1 --settle-ms 0 --no-cpu-baseline --no-block
+
 then
 
-  python3 -m gated_deltanet_recurrence_rule_amd.profsummary <KT> <FETCH> <WRITE> [--out profiles]
+  python3 -m gated_deltanet_recurrence_rule_amd.profsummary <KT> <FETCH> <WRITE> [--mfma <MFMA>] [--out profiles]
 
 writes one summary per kernel and traffic.json.  The counters are per dispatch, in KiB;
 each is scaled by (1 GiB / what the same counter read for the plain 1 GiB device copy
@@ -51,7 +56,9 @@ CMD_KT = ("rocprofv3 --kernel-trace --stats --output-format csv -d {kt} -o bench
           "python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline")
 CMD_PMC = ("timeout -s KILL 180 rocprofv3 --pmc {ctr} --output-format csv -d {d} -o bench -- "
            "python3 bench.py --steps 2 --warmup 1 --settle-ms 0 --no-cpu-baseline --copy-probe")
-CMD_SUM = "python3 -m gated_deltanet_recurrence_rule_amd.profsummary {kt} {fetch} {write} --out profiles"
+CMD_MFMA = ("timeout -s KILL 180 rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 --output-format csv -d {d} -o bench -- "
+            "python3 bench.py --steps 2 --warmup 1 --settle-ms 0 --no-cpu-baseline --no-block")
+CMD_SUM = "python3 -m gated_deltanet_recurrence_rule_amd.profsummary {kt} {fetch} {write}{mfma} --out profiles"
 
 
 def _one(d: str, suffix: str) -> str:
@@ -64,6 +71,13 @@ def _one(d: str, suffix: str) -> str:
 def kernel_stats(kt_dir: str) -> list:
     with open(_one(kt_dir, "kernel_stats.csv")) as f:
         return list(csv.DictReader(f))
+
+
+def kernel_counter(d: str, name: str, frag: str) -> list:
+    """Per-dispatch values of counter `name` for kernels whose name contains `frag`."""
+    with open(_one(d, "counter_collection.csv")) as f:
+        return [float(r["Counter_Value"]) for r in csv.DictReader(f)
+                if r["Counter_Name"] == name and frag in r["Kernel_Name"]]
 
 
 def counters(d: str, name: str):
@@ -90,6 +104,7 @@ def main(argv=None):
     ap.add_argument("kt")
     ap.add_argument("fetch")
     ap.add_argument("write")
+    ap.add_argument("--mfma", default=None, help="directory of the MfmaUtil / MfmaFlopsBF16 run")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     args = ap.parse_args(argv)
 
@@ -109,7 +124,24 @@ def main(argv=None):
     }
     cmds = [CMD_KT.format(kt=args.kt), CMD_PMC.format(ctr="FETCH_SIZE", d=args.fetch),
             CMD_PMC.format(ctr="WRITE_SIZE", d=args.write),
-            CMD_SUM.format(kt=args.kt, fetch=args.fetch, write=args.write)]
+            CMD_SUM.format(kt=args.kt, fetch=args.fetch, write=args.write,
+                           mfma=f" --mfma {args.mfma}" if args.mfma else "")]
+    mfma_lines = {}
+    if args.mfma:
+        frag = KERNELS["prefill_chunked"][0]
+        util = kernel_counter(args.mfma, "MfmaUtil", frag)
+        flops = kernel_counter(args.mfma, "MfmaFlopsBF16", frag)
+        if util and flops:
+            f_alg = bench.prefill_alg(4, 16384, 16, 32, 128, 128, 2, True)[1]
+            fx = sum(flops) / len(flops)
+            mfma_lines["prefill_chunked"] = [
+                f"  MFMA use:      {CMD_MFMA.format(d=args.mfma)}",
+                f"MFMA busy (MfmaUtil = MFMA-busy cycles / (GPU-active cycles x SIMDs)): "
+                f"{sum(util) / len(util):.1f}% average over {len(util)} dispatches "
+                f"(min {min(util):.1f}%, max {max(util):.1f}%)",
+                f"bf16 MFMA flops executed per dispatch (MfmaFlopsBF16): {fx:.4e} = {fx / f_alg:.2f}x the "
+                f"algorithmic {f_alg:.4e} (hi/lo operand splits, Grams recomputed per column slice)",
+            ]
     traffic = {
         "note": "HBM bytes per dispatch from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (KiB), each "
                 "scaled by 1 GiB / (the counter's reading for a plain 1 GiB device copy in the same run)",
@@ -139,6 +171,7 @@ def main(argv=None):
             f"  HBM fetch:     {cmds[1]}",
             f"  HBM write:     {cmds[2]}",
             f"  this summary:  {cmds[3]}",
+            *mfma_lines.get(key, []),
             f"Counter calibration: a 1 GiB device copy (bench.py --copy-probe) read FETCH_SIZE = {fetch_copy:.0f} KiB "
             f"and WRITE_SIZE = {write_copy:.0f} KiB,",
             f"so FETCH_SIZE is scaled by {scale_f:.4f} and WRITE_SIZE by {scale_w:.4f}.",
