@@ -33,11 +33,21 @@ template <> struct elem<uint16_t> {
 };
 
 // ------------------------------------------------------------------ wave64 reductions
+// Sum over the 64 lanes, returned to every lane: an inclusive scan by DPP row shifts
+// within each row of 16 lanes, then the row-15 and row-31 broadcasts across rows, leaves
+// the total in lane 63, which is read back as a uniform value.  No LDS round trips.
+#define GDN_DPP_ADD_(x, ctrl, row_mask) \
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, row_mask, 0xF, true))
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-    return x;
+    GDN_DPP_ADD_(x, 0x111, 0xF);  // row_shr:1
+    GDN_DPP_ADD_(x, 0x112, 0xF);  // row_shr:2
+    GDN_DPP_ADD_(x, 0x114, 0xF);  // row_shr:4
+    GDN_DPP_ADD_(x, 0x118, 0xF);  // row_shr:8
+    GDN_DPP_ADD_(x, 0x142, 0xA);  // row_bcast:15 into rows 1 and 3
+    GDN_DPP_ADD_(x, 0x143, 0xC);  // row_bcast:31 into rows 2 and 3
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
+#undef GDN_DPP_ADD_
 
 // 1 / max(sqrt(ss), eps) with eps = 1e-12: the L2-normalisation factor x / max(|x|, eps).
 // Uses the hardware reciprocal square root (about 1 ulp); ss <= eps^2 (zero included)

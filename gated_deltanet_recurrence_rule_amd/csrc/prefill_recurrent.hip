@@ -57,16 +57,37 @@ __global__ __launch_bounds__(64) void prefill_recurrent_kernel(
 #pragma unroll
     for (int i = 0; i < DK; ++i) s[i] = (S0 && active) ? S0[tab + (size_t)i * DV + j] : 0.f;
 
-    for (int64_t t = t0; t < t1; ++t) {
+    // this token's raw q, k, v, g, beta in registers, loaded one token ahead so the global
+    // memory latency overlaps the previous token's arithmetic
+    float qn[EPL], kn[EPL], vn = 0.f, gn = 0.f, bn = 1.f;
+    auto fetch = [&](int64_t t) {
         const T *qp = q + ((size_t)t * HQK + hq) * DK;
         const T *kp = k + ((size_t)t * HQK + hq) * DK;
-        float qx[EPL], kx[EPL];
-        float sq = 0.f, sk = 0.f, sqk = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
             const int i = lane + 64 * e;
-            qx[e] = i < DK ? elem<T>::ld(qp + i) : 0.f;
-            kx[e] = i < DK ? elem<T>::ld(kp + i) : 0.f;
+            qn[e] = i < DK ? elem<T>::ld(qp + i) : 0.f;
+            kn[e] = i < DK ? elem<T>::ld(kp + i) : 0.f;
+        }
+        const size_t tv = (size_t)t * HV + h;
+        vn = active ? elem<T>::ld(v + tv * DV + j) : 0.f;
+        gn = g ? g[tv] : 0.f;
+        bn = beta ? beta[tv] : 1.f;
+    };
+    if (t0 < t1) fetch(t0);
+
+    for (int64_t t = t0; t < t1; ++t) {
+        float qx[EPL], kx[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            qx[e] = qn[e];
+            kx[e] = kn[e];
+        }
+        const float vj = vn, graw = gn, braw = bn;
+        if (t + 1 < t1) fetch(t + 1);
+        float sq = 0.f, sk = 0.f, sqk = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
             sq += qx[e] * qx[e];
             sk += kx[e] * kx[e];
             sqk += qx[e] * kx[e];
@@ -90,12 +111,11 @@ __global__ __launch_bounds__(64) void prefill_recurrent_kernel(
         const size_t tv = (size_t)t * HV + h;
         float a = 1.f, b = 1.f;
         if (g) {
-            float x = g[tv];
+            float x = graw;
             if (gate.A_log) x = -expf(gate.A_log[h]) * softplus_f(x + (gate.dt_bias ? gate.dt_bias[h] : 0.f));
             a = expf(x);
         }
-        if (beta) b = gate.beta_logit ? sigmoid_f(beta[tv]) : beta[tv];
-        const float vj = active ? elem<T>::ld(v + tv * DV + j) : 0.f;
+        if (beta) b = gate.beta_logit ? sigmoid_f(braw) : braw;
 
         float p = 0.f, r = 0.f;
 #pragma unroll
