@@ -14,10 +14,11 @@
 // Both S^T k and S^T q are therefore reduced from the same registers while
 // the table streams in; the write pass needs only d.
 //
-// Thread layout (NT = 4 DV threads): thread t owns the column quad
-// c = t % (DV/4) (columns 4c..4c+3) and the rows r = t / (DV/4) + 16 m,
-// m < DK/16.  One wave load instruction therefore covers 64 float4 = whole
-// contiguous rows of the table, and each thread keeps DK/16 float4 of S in
+// Thread layout (NT = DV / 4 * kRowGroups threads, 4 DV at the default 16 row groups; 8
+// and 32 measured the same on the 256-sequence batch): thread t owns the column quad
+// c = t % (DV/4) (columns 4c..4c+3) and the rows r = t / (DV/4) + kRowGroups m,
+// m < DK/kRowGroups.  One wave load instruction therefore covers 64 float4 = whole
+// contiguous rows of the table, and each thread keeps DK/kRowGroups float4 of S in
 // registers between the read and the write.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -26,10 +27,13 @@ namespace gdn {
 
 namespace {
 
-constexpr int kRowGroups = 16;
+#ifndef GDN_DECODE_ROW_GROUPS
+#define GDN_DECODE_ROW_GROUPS 16
+#endif
+constexpr int kRowGroups = GDN_DECODE_ROW_GROUPS;
 
 template <int DK, int DV, typename T>
-__global__ __launch_bounds__(4 * DV) void decode_kernel(
+__global__ __launch_bounds__((DV / 4) * kRowGroups) void decode_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float *__restrict__ S,
     T *__restrict__ o, int HV, int rep, float scale, int delta, GateArgs gate,
@@ -172,7 +176,9 @@ template <int DK, int DV, typename T>
 hipError_t launch(const DecodeArgs &a, hipStream_t stream) {
     const int rep = a.HV / a.HQK;
     dim3 grid((unsigned)((int64_t)a.N * a.HV));
-    hipLaunchKernelGGL((decode_kernel<DK, DV, T>), grid, dim3(4 * DV), 0, stream,
+    static_assert(DK % kRowGroups == 0 && (DV / 4) * kRowGroups >= DV && (DV / 4) * kRowGroups <= 1024,
+                  "row groups must divide DK and give DV..1024 threads");
+    hipLaunchKernelGGL((decode_kernel<DK, DV, T>), grid, dim3((DV / 4) * kRowGroups), 0, stream,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), a.g, a.beta, a.S, static_cast<T *>(a.o), a.HV,
                        rep, a.scale, a.delta, a.gate, static_cast<const T *>(a.z), a.norm_w, a.norm_eps);
