@@ -114,6 +114,56 @@ gdn::GateArgs gate_args(const gdn_block_ops *ops, gdn_variant variant) {
     return ga;
 }
 
+// Compute units of the current device (cached per device; 256, MI355X's count, if the
+// runtime cannot say).
+int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        cache[dev] = cus;
+    }
+    return cache[dev];
+}
+
+// Segments per sequence for the chunked prefill.  A batch whose (sequence, V head, 64-column)
+// workgroups fill at most half the compute units has its sequences cut into P segments
+// (doubling P while P times the workgroups still fits the units, at most 16), provided the
+// average sequence leaves every segment at least 4 chunks.
+int32_t split_segments(int32_t N, int64_t total_T, int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype) {
+    if (N <= 0 || !gdn::prefill_chunked_supported(dk, dv, dtype == GDN_BF16)) return 1;
+    const int64_t cus = device_cus();
+    const int64_t units = (int64_t)N * HV * (dv / 64);
+    int32_t P = 1;
+    while (P < 16 && units * P * 2 <= cus) P *= 2;
+    while (P > 1 && total_T < (int64_t)N * P * 4 * 64) P /= 2;
+    return P;
+}
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace parts: the longest-first order, then (split sequences) the segment maps and
+// the segment start tables.
+struct WorkspacePlan {
+    size_t order = 0, maps = 0, starts = 0;
+    int32_t P = 1;
+    size_t total() const { return order + maps + starts; }
+};
+
+WorkspacePlan workspace_plan(int32_t N, int64_t total_T, int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype) {
+    WorkspacePlan w;
+    if (N > 1 && N <= gdn::kMaxOrderedSequences) w.order = round256((size_t)N * 4);
+    w.P = split_segments(N, total_T, HV, dk, dv, dtype);
+    if (w.P > 1) {
+        w.maps = round256((size_t)N * (w.P - 1) * HV * dk * (dv + dk) * 4);
+        w.starts = round256((size_t)N * w.P * HV * dk * dv * 4);
+    }
+    return w;
+}
+
 gdn_status hip_status(hipError_t e, const char *what) {
     if (e == hipSuccess) return GDN_OK;
     return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -190,10 +240,9 @@ gdn_status gdn_decode_step_ex(const void *q, const void *k, const void *v, const
 
 size_t gdn_prefill_workspace_size(int32_t N, int64_t total_T, int32_t HQK, int32_t HV,
                                   int32_t dk, int32_t dv, gdn_dtype dtype) {
-    (void)total_T; (void)HQK; (void)HV; (void)dk; (void)dv; (void)dtype;
-    // the longest-first launch order: one int32 per sequence, rounded to 256 bytes
-    if (N <= 1 || N > gdn::kMaxOrderedSequences) return 0;
-    return ((size_t)N * 4 + 255) / 256 * 256;
+    (void)HQK;
+    if (N < 0 || total_T < 0 || HV <= 0) return 0;
+    return workspace_plan(N, total_T, HV, dk, dv, dtype).total();
 }
 
 gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float *g,
@@ -240,7 +289,8 @@ gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v, const flo
     int64_t eq_len = 0;
     st = check_seqlens(cu_seqlens, cu_seqlens_host, N, total_T, &eq_len);
     if (st != GDN_OK) return st;
-    const size_t need = gdn_prefill_workspace_size(N, total_T, HQK, HV, dk, dv, dtype);
+    const WorkspacePlan plan = workspace_plan(N, total_T, HV, dk, dv, dtype);
+    const size_t need = plan.total();
     if (workspace_bytes < need)
         return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
     if (need > 0 && !workspace) return fail(GDN_ERR_NULL, "workspace must be non-NULL");
@@ -250,7 +300,7 @@ gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v, const flo
     // Launch order: longest sequences first.  Equal lengths (cu_seqlens NULL) and host
     // lengths that are already non-increasing keep the given order.
     const int32_t *order = nullptr;
-    if (cu_seqlens && need > 0) {
+    if (cu_seqlens && plan.order > 0) {
         bool sorted = false;
         if (cu_seqlens_host) {
             sorted = true;
@@ -269,10 +319,23 @@ gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v, const flo
                        variant_delta(variant) ? 1 : 0};
     a.gate = gate_args(ops, variant);
     const bool bf16 = dtype == GDN_BF16;
-    if (gdn::prefill_chunked_supported(dk, dv, bf16))
+    if (plan.P > 1) {
+        // split sequences: segment maps, their chain, then every segment from its start table
+        float *maps = reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.order);
+        float *starts = reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.order + plan.maps);
+        a.split = gdn::SplitArgs{plan.P, 1, maps};
+        st = hip_status(gdn::launch_prefill_chunked(a, stream), "chunked prefill (segment maps) launch");
+        if (st == GDN_OK)
+            st = hip_status(gdn::launch_split_chain(maps, S0, starts, N, plan.P, HV, dv, stream), "segment chain launch");
+        if (st == GDN_OK) {
+            a.split = gdn::SplitArgs{plan.P, 2, starts};
+            st = hip_status(gdn::launch_prefill_chunked(a, stream), "chunked prefill (segments) launch");
+        }
+    } else if (gdn::prefill_chunked_supported(dk, dv, bf16)) {
         st = hip_status(gdn::launch_prefill_chunked(a, stream), "chunked prefill launch");
-    else
+    } else {
         st = hip_status(gdn::launch_prefill_recurrent(a, bf16, stream), "prefill launch");
+    }
     if (st != GDN_OK || !ops || !ops->z || total_T == 0) return st;
     gdn::NormArgs na{o, ops->z, ops->norm_w, o, total_T * HV, dv, ops->norm_eps};
     return hip_status(gdn::launch_gated_rmsnorm(na, bf16, stream), "gated norm launch");
@@ -327,8 +390,11 @@ gdn_status gdn_gated_rmsnorm(const void *x, const void *z, const float *w, float
 
 const char *gdn_prefill_kernel_name(int32_t N, int64_t total_T, int32_t HQK, int32_t HV, int32_t dk,
                                     int32_t dv, gdn_dtype dtype) {
-    (void)N; (void)total_T; (void)HQK; (void)HV;
-    if (gdn::prefill_chunked_supported(dk, dv, dtype == GDN_BF16)) return "prefill_chunked";
+    (void)HQK;
+    if (gdn::prefill_chunked_supported(dk, dv, dtype == GDN_BF16))
+        return (N > 0 && HV > 0 && total_T >= 0 && split_segments(N, total_T, HV, dk, dv, dtype) > 1)
+                   ? "prefill_chunked_split"
+                   : "prefill_chunked";
     return "prefill_recurrent";
 }
 

@@ -14,6 +14,15 @@ struct GateArgs {
     int32_t beta_logit = 0;
 };
 
+// Split sequences for the chunked prefill (see prefill_chunked.hip): P segments per sequence;
+// mode 0 = no split, 1 = map pass (state = [N][P - 1][HV][DK][DV + DK] output), 2 = segment
+// pass (state = [N][P][HV][DK][DV] start tables).
+struct SplitArgs {
+    int32_t P = 1;
+    int32_t mode = 0;
+    float *state = nullptr;
+};
+
 // Arguments shared by the launchers, already validated by the C-ABI layer.
 // g == nullptr means a = 1 (no decay); beta == nullptr means b = 1; delta == 0 drops the
 // look-up (the write is b v instead of b (v - a S^T k)).
@@ -49,6 +58,7 @@ struct PrefillArgs {
     size_t workspace_bytes;
     int32_t delta;
     GateArgs gate = {};
+    SplitArgs split = {};
 };
 
 // Gated RMS norm over rows of dv values (rows = tokens x heads; z rows alike; w [dv]):
@@ -92,6 +102,10 @@ constexpr int32_t kMaxOrderedSequences = 16384;
 
 // Chunked MFMA prefill: bf16 I/O, dk = 128, dv a multiple of 64.
 bool prefill_chunked_supported(int dk, int dv, bool bf16);
+// Start tables of every segment of split sequences: S_in[n][0] = S0[n] (or zeros),
+// S_in[n][j + 1] = M_j S_in[n][j] + B_j with [B_j | M_j] = maps[n][j] (dk = 128).
+hipError_t launch_split_chain(const float *maps, const float *S0, float *S_in, int32_t N, int32_t P,
+                              int32_t HV, int32_t dv, hipStream_t stream);
 hipError_t launch_prefill_chunked(const PrefillArgs &a, hipStream_t stream);
 
 }  // namespace gdn

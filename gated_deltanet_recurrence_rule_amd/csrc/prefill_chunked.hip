@@ -200,13 +200,14 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // DELTA = false drops the look-up (A = 0, so T = I and Delta = Z = diag(b) V): the decayed
 // linear-attention rule of the learn-llm page's update-rule table.
-template <bool DELTA>
+// SPLIT = false compiles the split-sequence passes out (mode 0 only).
+template <bool DELTA, bool SPLIT>
 __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
     const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ order, int64_t eq_len,
     const float *__restrict__ S0, uint16_t *__restrict__ o, float *__restrict__ S_T, int HV, int DV,
-    int rep, int NG, int M, float scale, GateArgs gate) {
+    int rep, int NG, int M, float scale, GateArgs gate, SplitArgs sp) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
     // Everything belonging to chunk c lives in the buffers of parity c % 2: K and Q rows, K^T,
     // the per-token scalars, and the solve / read operands built from them.  Scalars:
@@ -235,17 +236,32 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     // that read the same q and k rows (one sequence, one QK head: group G) get linear ids
     // L = 8 (M (G / 8) + m) + G % 8, i.e. the same L mod 8, so round-robin dispatch over the
     // eight XCDs places them on one XCD and one L2, launched one after another.  Groups are
-    // numbered in launch order (sequence rank, then QK head); ids past the last group exit.
+    // numbered in launch order (sequence rank, segment, then QK head); ids past the last
+    // group exit.
+    //
+    // Split sequences (P = sp.P > 1 segments of equal whole-chunk length per sequence):
+    //  * map pass (sp.mode 1, segments 0 .. P-2): the table is widened to DW = DV + DK
+    //    columns, started at [0 | I], and the extra columns read v = 0.  Each column of the
+    //    table evolves on its own and affinely in the start state, so the segment's final
+    //    table is [B | M] with S_out = M S_in + B.  Reads are not stored; the final table
+    //    goes to sp.state, [P - 1 segments][HV][DK][DW] per sequence.
+    //  * segment pass (sp.mode 2): every segment starts from sp.state, [P][HV][DK][DV] per
+    //    sequence (the start tables chained from the maps), writes its reads, and the last
+    //    segment writes S_T.
     const int HQK = HV / rep;
+    const int mode = SPLIT ? sp.mode : 0;
+    const int PS = mode == 1 ? sp.P - 1 : (mode == 2 ? sp.P : 1);  // segments launched
+    const int DW = mode == 1 ? DV + DK : DV;                       // table width
     const int Lid = blockIdx.x;
     const int G = 8 * ((Lid >> 3) / M) + (Lid & 7);
     if (G >= NG) return;
     const int mem = (Lid >> 3) % M;
-    const int rank = G / HQK;
+    const int rank = G / (PS * HQK);
+    const int seg = (G / HQK) % PS;
     const int hq = G % HQK;
     const int nseq = order ? order[rank] : rank;
-    const int h = hq * rep + mem / (DV / DVS);
-    const int col0 = (mem % (DV / DVS)) * DVS;
+    const int h = hq * rep + mem / (DW / DVS);
+    const int col0 = (mem % (DW / DVS)) * DVS;
     const int unit = nseq * HV + h;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -263,6 +279,15 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         t0 = (int64_t)nseq * eq_len;
         t1 = t0 + eq_len;
     }
+    if (mode != 0) {
+        // segment seg: chunks [seg cps, (seg + 1) cps) of the sequence, cps = ceil(chunks / P)
+        const int64_t len = t1 - t0;
+        const int64_t cps = ((len + C - 1) / C + sp.P - 1) / sp.P;
+        const int64_t a = (int64_t)seg * cps * C, bnd = a + cps * C;
+        const int64_t s1 = t0 + (bnd < len ? bnd : len);
+        t0 += a < len ? a : len;
+        t1 = s1;
+    }
 
     const int nchunks = (int)((t1 - t0 + C - 1) / C);
     auto chunk_len = [&](int c) { return (int)((t1 - t0 - (int64_t)c * C) < C ? (t1 - t0 - (int64_t)c * C) : C); };
@@ -276,20 +301,34 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         // ====================== column waves: the table and the per-chunk chain ======
         // Element e of S[dt] is S[16 dt + 4 lq + e][col0 + 16 w + lr].
         f32x4 S[8];
-        const size_t tab = (size_t)unit * DK * DV;
         const int mycol = col0 + 16 * w + lr;
+        // start table (row stride DW) and where the final table goes
+        const float *Sin = S0 ? S0 + (size_t)unit * DK * DV : nullptr;
+        float *Sout = S_T ? S_T + (size_t)unit * DK * DV : nullptr;
+        if (mode == 1) {
+            Sin = nullptr;
+            Sout = sp.state + ((size_t)(nseq * (sp.P - 1) + seg) * HV + h) * DK * DW;
+        } else if (mode == 2) {
+            Sin = sp.state + ((size_t)(nseq * sp.P + seg) * HV + h) * DK * DV;
+            if (seg != sp.P - 1) Sout = nullptr;
+        }
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                S[dt][e] = S0 ? S0[tab + (size_t)(16 * dt + 4 * lq + e) * DV + mycol] : 0.f;
-        if (nchunks == 0) {
-            if (S_T) {
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * dt + 4 * lq + e;
+                S[dt][e] = Sin ? Sin[(size_t)r * DW + mycol] : ((SPLIT && mycol - DV == r) ? 1.f : 0.f);
+            }
+        auto store_table = [&]() {
+            if (Sout) {
 #pragma unroll
                 for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) S_T[tab + (size_t)(16 * dt + 4 * lq + e) * DV + mycol] = S[dt][e];
+                    for (int e = 0; e < 4; ++e) Sout[(size_t)(16 * dt + 4 * lq + e) * DW + mycol] = S[dt][e];
             }
+        };
+        if (nchunks == 0) {
+            store_table();
             return;
         }
 
@@ -298,10 +337,14 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         const size_t vrs = (size_t)HV * DV;  // token stride of v and o
         const uint32_t rowb = 2u * (uint32_t)vrs;  // bytes per token row of v and o
         const uint16_t *vwave = v + (size_t)h * DV + col0 + 16 * wu;
+        // the map pass's identity columns (col0 >= DV) read v = 0 and store no reads: their
+        // buffer descriptors cover no bytes, so the hardware returns zeros and drops stores
+        const bool vio = !SPLIT || (col0 < DV && mode != 1);
+        const bool vin = !SPLIT || col0 < DV;
         uint16_t *owave = o + (size_t)h * DV + col0 + 16 * wu;
         auto prefetch_v = [&](int c) {
             const int nn = chunk_len(c);
-            const rsrc_t vr = make_rsrc(vwave + (size_t)(t0 + (int64_t)c * C) * vrs, (uint32_t)nn * rowb);
+            const rsrc_t vr = make_rsrc(vwave + (size_t)(t0 + (int64_t)c * C) * vrs, vin ? (uint32_t)nn * rowb : 0u);
             const uint32_t off = 2u * (uint32_t)lr + (uint32_t)(4 * lq) * rowb;
             if (nn == C) {
 #pragma unroll
@@ -439,7 +482,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             }
             // O^T = gamma r_q (Q S)^T + (P Delta)^T: token 16 rt + lr, 4 adjacent columns per lane
             {
-                const rsrc_t orr = make_rsrc(owave + (size_t)c0 * vrs, (uint32_t)n * rowb);
+                const rsrc_t orr = make_rsrc(owave + (size_t)c0 * vrs, vio ? (uint32_t)n * rowb : 0u);
                 const uint32_t ooff = (uint32_t)lrr * rowb + 8u * (uint32_t)lqq;
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
@@ -492,12 +535,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         phase_b(nchunks - 1);
         __syncthreads();
         __syncthreads();
-        if (S_T) {
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) S_T[tab + (size_t)(16 * dt + 4 * lq + e) * DV + mycol] = S[dt][e];
-        }
+        store_table();
         return;
     }
     if (nchunks == 0) return;
@@ -921,15 +959,20 @@ bool prefill_chunked_supported(int dk, int dv, bool bf16) { return bf16 && dk ==
 hipError_t launch_prefill_chunked(const PrefillArgs &a, hipStream_t stream) {
     if (a.N == 0) return hipSuccess;
     const int rep = a.HV / a.HQK;
-    const int64_t NG = (int64_t)a.N * a.HQK;            // (sequence, QK head) groups
-    const int64_t M = (int64_t)rep * (a.dv / DVS);      // workgroups per group
+    const int PS = a.split.mode == 1 ? a.split.P - 1 : (a.split.mode == 2 ? a.split.P : 1);
+    const int DW = a.split.mode == 1 ? a.dv + DK : a.dv;
+    const int64_t NG = (int64_t)a.N * PS * a.HQK;       // (sequence, segment, QK head) groups
+    const int64_t M = (int64_t)rep * (DW / DVS);        // workgroups per group
     const int64_t nwg = 8 * M * ((NG + 7) / 8);
     if (nwg > 0x7fffffffLL || NG > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(a.delta ? prefill_chunked_kernel<true> : prefill_chunked_kernel<false>, dim3((unsigned)nwg),
+    auto kern = a.split.mode != 0 ? (a.delta ? prefill_chunked_kernel<true, true> : prefill_chunked_kernel<false, true>)
+                                  : (a.delta ? prefill_chunked_kernel<true, false> : prefill_chunked_kernel<false, false>);
+    hipLaunchKernelGGL(kern, dim3((unsigned)nwg),
                        dim3(NT), 0, stream,
                        static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
                        static_cast<const uint16_t *>(a.v), a.g, a.beta, a.cu_seqlens, a.order, a.eq_len,
-                       a.S0, static_cast<uint16_t *>(a.o), a.S_T, a.HV, a.dv, rep, (int)NG, (int)M, a.scale, a.gate);
+                       a.S0, static_cast<uint16_t *>(a.o), a.S_T, a.HV, a.dv, rep, (int)NG, (int)M, a.scale, a.gate,
+                       a.split);
     return hipGetLastError();
 }
 

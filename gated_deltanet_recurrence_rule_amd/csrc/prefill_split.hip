@@ -1,0 +1,89 @@
+// prefill_split.hip -- chaining the segment maps of split sequences.
+//
+// A sequence too short of parallel work for the chip (few sequences and heads) is cut into
+// P segments of whole chunks.  The recurrence of the handbook page "7. Gated DeltaNet: the
+// token-by-token recurrence" (section "The formula") is affine in the table it starts
+// from, so a segment that starts from S_in ends at M S_in + B.  The chunked kernel's map
+// pass gives every segment's [B | M] at once; this kernel chains them, one segment after
+// another, into the start table of every segment; the segment pass then runs all segments
+// at once from those tables.
+//
+// One workgroup per (sequence, V head, 16 columns of dv): columns of the table evolve
+// independently, so a column block chains on its own.  Per step it stages M (128 x 128
+// fp32, rows padded to 132 floats so that 16 rows read in one wave fall in distinct
+// banks) in LDS; each thread forms 2 rows x 4 columns of M S + B with fp32 FMAs.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace gdn {
+
+namespace {
+
+constexpr int SDK = 128;      // dk of the chunked path
+constexpr int SLM = SDK + 4;  // padded LDS row of M
+constexpr int SCB = 16;       // columns per workgroup
+
+__global__ __launch_bounds__(256) void split_chain_kernel(const float *__restrict__ maps,
+                                                          const float *__restrict__ S0, float *__restrict__ S_in,
+                                                          int P, int HV, int DV) {
+    __shared__ __attribute__((aligned(16))) float Ms[SDK * SLM];
+    __shared__ __attribute__((aligned(16))) float Sb[SDK * SCB];
+    const int unit = blockIdx.x;  // n * HV + h
+    const int n = unit / HV, h = unit % HV;
+    const int c0 = blockIdx.y * SCB;
+    const int DW = DV + SDK;
+    const int tid = threadIdx.x;
+    const int c4 = tid & 3, r = tid >> 2;  // columns c0 + 4 c4 .., rows r and r + 64
+
+    auto sin_at = [&](int j) { return S_in + ((size_t)(n * P + j) * HV + h) * SDK * DV; };
+    // segment 0 starts from S0 (or zeros)
+    for (int idx = tid; idx < SDK * SCB; idx += 256) {
+        const int row = idx / SCB, col = idx % SCB;
+        const float x = S0 ? S0[((size_t)unit * SDK + row) * DV + c0 + col] : 0.f;
+        Sb[idx] = x;
+        sin_at(0)[(size_t)row * DV + c0 + col] = x;
+    }
+    for (int j = 0; j + 1 < P; ++j) {
+        const float *map = maps + ((size_t)(n * (P - 1) + j) * HV + h) * SDK * DW;
+        __syncthreads();  // Sb holds S_in(j); Ms is free
+#pragma unroll 4
+        for (int i = 0; i < SDK * SDK / 4 / 256; ++i) {
+            const int f = tid + 256 * i;
+            const int rr = f / (SDK / 4), kq = f % (SDK / 4);
+            *reinterpret_cast<float4 *>(&Ms[rr * SLM + 4 * kq]) =
+                *reinterpret_cast<const float4 *>(map + (size_t)rr * DW + DV + 4 * kq);
+        }
+        __syncthreads();
+        f32x4 acc0 = *reinterpret_cast<const f32x4 *>(map + (size_t)r * DW + c0 + 4 * c4);
+        f32x4 acc1 = *reinterpret_cast<const f32x4 *>(map + (size_t)(r + 64) * DW + c0 + 4 * c4);
+        for (int k = 0; k < SDK; k += 4) {
+            const f32x4 m0 = *reinterpret_cast<const f32x4 *>(&Ms[r * SLM + k]);
+            const f32x4 m1 = *reinterpret_cast<const f32x4 *>(&Ms[(r + 64) * SLM + k]);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const f32x4 sv = *reinterpret_cast<const f32x4 *>(&Sb[(k + kk) * SCB + 4 * c4]);
+                acc0 += m0[kk] * sv;
+                acc1 += m1[kk] * sv;
+            }
+        }
+        __syncthreads();  // every read of Sb done
+        *reinterpret_cast<f32x4 *>(&Sb[r * SCB + 4 * c4]) = acc0;
+        *reinterpret_cast<f32x4 *>(&Sb[(r + 64) * SCB + 4 * c4]) = acc1;
+        float *dst = sin_at(j + 1);
+        *reinterpret_cast<f32x4 *>(dst + (size_t)r * DV + c0 + 4 * c4) = acc0;
+        *reinterpret_cast<f32x4 *>(dst + (size_t)(r + 64) * DV + c0 + 4 * c4) = acc1;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_split_chain(const float *maps, const float *S0, float *S_in, int32_t N, int32_t P, int32_t HV,
+                              int32_t dv, hipStream_t stream) {
+    if (N == 0) return hipSuccess;
+    if (dv % SCB != 0 || (int64_t)N * HV > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(split_chain_kernel, dim3((unsigned)(N * HV), (unsigned)(dv / SCB)), dim3(256), 0, stream,
+                       maps, S0, S_in, P, HV, dv);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

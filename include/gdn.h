@@ -123,9 +123,21 @@ gdn_status gdn_decode_step_v(const void *q, const void *k, const void *v, const 
 
 /*
  * gdn_prefill_workspace_size -- bytes of device workspace gdn_prefill needs for
- * these sizes (0 means the workspace pointer may be NULL).  The workspace holds
- * the launch order of the sequences (one int32 each); it is 0 for N <= 1 and
- * for N above 16384 (such batches run in the given order).
+ * these sizes on the current device (0 means the workspace pointer may be NULL).
+ * Two parts, each rounded to 256 bytes:
+ *  - the launch order of the sequences (one int32 each); none for N <= 1 and for
+ *    N above 16384 (such batches run in the given order);
+ *  - for a batch the chunked kernel runs (bf16, dk = 128, dv a multiple of 64) whose
+ *    (sequence, V head, 64-column) workgroups fill at most half the device's compute
+ *    units: each sequence is cut into P segments (P doubles while P times the
+ *    workgroups still fits the units, at most 16, and halves until total_T >= N P 256).
+ *    The recurrence is affine in the table a segment starts from, S_out = M S_in + B
+ *    (handbook page "7. Gated DeltaNet: the token-by-token recurrence", section "The
+ *    formula"): the library forms every segment's [B | M] at once, chains them into
+ *    each segment's start table, then runs all segments at once.  This part holds
+ *    N (P-1) HV dk (dv + dk) + N P HV dk dv floats.
+ * The size depends on the current device's compute-unit count: query it with the
+ * device current that gdn_prefill will run on.
  */
 size_t gdn_prefill_workspace_size(int32_t N, int64_t total_T, int32_t HQK, int32_t HV,
                                   int32_t dk, int32_t dv, gdn_dtype dtype);
@@ -275,6 +287,8 @@ gdn_status gdn_gated_rmsnorm(const void *x, const void *z, const float *w, float
  * (static text, for profiling and reports):
  *   "prefill_chunked"    bf16, dk = 128, dv a multiple of 64: chunks of 64 tokens
  *                        on bf16 MFMA with an fp32 table;
+ *   "prefill_chunked_split"  the same kernel over split sequences (see
+ *                        gdn_prefill_workspace_size), plus the chaining kernel;
  *   "prefill_recurrent"  every other case: token-serial, fp32 arithmetic.
  */
 const char *gdn_prefill_kernel_name(int32_t N, int64_t total_T, int32_t HQK, int32_t HV,

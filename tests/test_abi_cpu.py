@@ -367,3 +367,30 @@ def test_gated_rmsnorm_rejects(lib, kw, status):
     assert lib.gdn_gated_rmsnorm(a["x"], a["z"], a["w"], a["eps"], a["y"], a["rows"], a["dv"], a["dtype"],
                                  None) == status
     assert all(np.all(t == 7.0) for t in (x, z, y, w))
+
+
+# ------------------------------------------------------------------ split sequences
+def test_split_workspace_plan(lib):
+    """Host planning of split sequences (no GPU here, so the device is taken to have 256
+    compute units): 1 x 8192 tokens, 16 heads, d = 128, bf16 -> 32 workgroups -> P = 8:
+    7 maps of 128 x 256 and 8 start tables of 128 x 128 per head."""
+    need = lib.gdn_prefill_workspace_size(1, 8192, 16, 16, 128, 128, 0)
+    assert need == 7 * 16 * 128 * 256 * 4 + 8 * 16 * 128 * 128 * 4
+    assert lib.gdn_prefill_kernel_name(1, 8192, 16, 16, 128, 128, 0) == b"prefill_chunked_split"
+    # shorter sequences: segments may not fall under 4 chunks -> fewer segments, or none
+    assert lib.gdn_prefill_workspace_size(1, 1000, 16, 16, 128, 128, 0) == 1 * 16 * 128 * 256 * 4 + 2 * 16 * 128 * 128 * 4
+    assert lib.gdn_prefill_workspace_size(1, 400, 16, 16, 128, 128, 0) == 0
+    # the 4 x 16384 batch fills the device (256 workgroups): no split
+    assert lib.gdn_prefill_workspace_size(4, 65536, 16, 32, 128, 128, 0) == 256
+    assert lib.gdn_prefill_kernel_name(4, 65536, 16, 32, 128, 128, 0) == b"prefill_chunked"
+    # fp32 runs the token-serial kernel: never split
+    assert lib.gdn_prefill_workspace_size(1, 8192, 16, 16, 128, 128, 1) == 0
+
+
+def test_split_workspace_too_small_is_rejected(lib):
+    B = Bufs(T=8192, N=1, HQK=1, HV=2, dk=128, dv=128)
+    need = lib.gdn_prefill_workspace_size(1, 8192, 1, 2, 128, 128, 0)
+    assert need > 0
+    ws = np.zeros(16, np.float32)
+    assert _prefill(lib, B, dtype=0, ws=B.p(ws), ws_bytes=need - 1) == E_WS
+    assert B.untouched()

@@ -64,7 +64,8 @@ def test_decode_variant(dtype, variant, with_beta):
     o = binding.decode_step(d["q"], d["k"], d["v"], g, b, S, variant=variant)
     torch.cuda.synchronize()
     o_ref, S_ref = _oracle(inp, variant, with_beta)
-    assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), dtype, f"decode {variant}")
+    assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), dtype, f"decode {variant}",
+                  grows=not DELTA[variant])
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -82,7 +83,8 @@ def test_prefill_variant(dtype, variant, with_beta):
                            variant=variant)
     torch.cuda.synchronize()
     o_ref, S_ref = _oracle(inp, variant, with_beta)
-    assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), dtype, f"prefill {variant}")
+    assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), dtype, f"prefill {variant}",
+                  grows=not DELTA[variant])
 
 
 def test_prefill_variant_ignores_unused_gates():
