@@ -22,6 +22,16 @@ namespace {
 // 8 consecutive channels of one token: one 16-byte access for bf16, two for fp32.
 template <typename T> struct vec8;
 template <> struct vec8<uint16_t> {
+    struct raw_t { uint4 a; };
+    static __device__ __forceinline__ raw_t ld_raw(const uint16_t *p) { return {*reinterpret_cast<const uint4 *>(p)}; }
+    static __device__ __forceinline__ void decode(const raw_t &r, float (&x)[8]) {
+        const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(w[i] << 16);
+            x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
     static __device__ __forceinline__ void ld(const uint16_t *p, float (&x)[8]) {
         const uint4 u = *reinterpret_cast<const uint4 *>(p);
         const uint32_t w[4] = {u.x, u.y, u.z, u.w};
@@ -40,6 +50,14 @@ template <> struct vec8<uint16_t> {
     }
 };
 template <> struct vec8<float> {
+    struct raw_t { float4 a, b; };
+    static __device__ __forceinline__ raw_t ld_raw(const float *p) {
+        return {reinterpret_cast<const float4 *>(p)[0], reinterpret_cast<const float4 *>(p)[1]};
+    }
+    static __device__ __forceinline__ void decode(const raw_t &r, float (&x)[8]) {
+        x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
+        x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
+    }
     static __device__ __forceinline__ void ld(const float *p, float (&x)[8]) {
         const float4 a = reinterpret_cast<const float4 *>(p)[0], b = reinterpret_cast<const float4 *>(p)[1];
         x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
@@ -225,13 +243,30 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_kernel(
             fetch(t - 1, e3);
         }
         const int64_t stop = te < s1 ? te : s1;
-        // kConvGroup rows in flight at a time, then their arithmetic
-        for (; t + kConvGroup <= stop; t += kConvGroup) {
-            float cur[kConvGroup][8];
+        // groups of kConvGroup rows; the next group's loads are issued before this group's
+        // arithmetic, so a thread keeps a group in flight while it computes
+        if (t + kConvGroup <= stop) {
+            typename vec8<T>::raw_t rw[kConvGroup];
 #pragma unroll
-            for (int u = 0; u < kConvGroup; ++u) vec8<T>::ld(x + (t + u) * Ct + c, cur[u]);
+            for (int u = 0; u < kConvGroup; ++u) rw[u] = vec8<T>::ld_raw(x + (t + u) * Ct + c);
+            for (; t + kConvGroup <= stop; t += kConvGroup) {
+                typename vec8<T>::raw_t nx[kConvGroup];
+                const bool more = t + 2 * kConvGroup <= stop;
+                if (more) {
 #pragma unroll
-            for (int u = 0; u < kConvGroup; ++u) step(t + u, cur[u]);
+                    for (int u = 0; u < kConvGroup; ++u) nx[u] = vec8<T>::ld_raw(x + (t + kConvGroup + u) * Ct + c);
+                }
+#pragma unroll
+                for (int u = 0; u < kConvGroup; ++u) {
+                    float cur[8];
+                    vec8<T>::decode(rw[u], cur);
+                    step(t + u, cur);
+                }
+                if (more) {
+#pragma unroll
+                    for (int u = 0; u < kConvGroup; ++u) rw[u] = nx[u];
+                }
+            }
         }
         for (; t < stop; ++t) {
             float cur[8];
