@@ -2,8 +2,10 @@
 
     from gated_deltanet_recurrence_rule_amd import decode_step, prefill
 
-Both calls go through libgdn.so (include/gdn.h); there is no CPU fallback.
+Every call goes through libgdn.so (include/gdn.h); there is no CPU fallback.
 """
-from .binding import GdnError, decode_step, load, prefill, prefill_workspace_size, version
+from .binding import (VARIANTS, BlockOps, GdnError, conv_silu, decode_step, gated_rmsnorm, load, prefill,
+                      prefill_kernel_name, prefill_workspace_size, version)
 
-__all__ = ["GdnError", "decode_step", "load", "prefill", "prefill_workspace_size", "version"]
+__all__ = ["VARIANTS", "BlockOps", "GdnError", "conv_silu", "decode_step", "gated_rmsnorm", "load", "prefill",
+           "prefill_kernel_name", "prefill_workspace_size", "version"]
