@@ -341,6 +341,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         // buffer descriptors cover no bytes, so the hardware returns zeros and drops stores
         const bool vio = !SPLIT || (col0 < DV && mode != 1);
         const bool vin = !SPLIT || col0 < DV;
+        const bool reads = !SPLIT || mode != 1;  // the map pass forms no reads
         uint16_t *owave = o + (size_t)h * DV + col0 + 16 * wu;
         auto prefetch_v = [&](int c) {
             const int nn = chunk_len(c);
@@ -394,12 +395,12 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
                     kk[rt] = ld_std(sK, LK, 16 * rt, 32 * ks, ln);
-                    qq[rt] = ld_std(sQ, LK, 16 * rt, 32 * ks, ln);
+                    if (reads) qq[rt] = ld_std(sQ, LK, 16 * rt, 32 * ks, ln);
                 }
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
                     if constexpr (DELTA) y[rt] = mfma32(kk[rt], Sh, y[rt]);
-                    Ot[rt] = mfma32(Sh, qq[rt], Ot[rt]);
+                    if (reads) Ot[rt] = mfma32(Sh, qq[rt], Ot[rt]);
                 }
                 if constexpr (DELTA) {
 #pragma unroll
@@ -481,7 +482,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                 Dsg[1] = to_bf16(cat(Dl[2], Dl[3]));
             }
             // O^T = gamma r_q (Q S)^T + (P Delta)^T: token 16 rt + lr, 4 adjacent columns per lane
-            {
+            if (reads) {
                 const rsrc_t orr = make_rsrc(owave + (size_t)c0 * vrs, vio ? (uint32_t)n * rowb : 0u);
                 const uint32_t ooff = (uint32_t)lrr * rowb + 8u * (uint32_t)lqq;
 #pragma unroll

@@ -8,10 +8,11 @@
 // another, into the start table of every segment; the segment pass then runs all segments
 // at once from those tables.
 //
-// One workgroup per (sequence, V head, 16 columns of dv): columns of the table evolve
+// One workgroup per (sequence, V head, 8 columns of dv): columns of the table evolve
 // independently, so a column block chains on its own.  Per step it stages M (128 x 128
 // fp32, rows padded to 132 floats so that 16 rows read in one wave fall in distinct
-// banks) in LDS; each thread forms 2 rows x 4 columns of M S + B with fp32 FMAs.
+// banks) in LDS, the next step's M already on its way in registers; each thread forms
+// 4 columns of one row of M S + B with fp32 FMAs.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -21,7 +22,7 @@ namespace {
 
 constexpr int SDK = 128;      // dk of the chunked path
 constexpr int SLM = SDK + 4;  // padded LDS row of M
-constexpr int SCB = 16;       // columns per workgroup
+constexpr int SCB = 8;        // columns per workgroup
 
 __global__ __launch_bounds__(256) void split_chain_kernel(const float *__restrict__ maps,
                                                           const float *__restrict__ S0, float *__restrict__ S_in,
@@ -33,7 +34,7 @@ __global__ __launch_bounds__(256) void split_chain_kernel(const float *__restric
     const int c0 = blockIdx.y * SCB;
     const int DW = DV + SDK;
     const int tid = threadIdx.x;
-    const int c4 = tid & 3, r = tid >> 2;  // columns c0 + 4 c4 .., rows r and r + 64
+    const int c4 = tid & 1, r = tid >> 1;  // columns c0 + 4 c4 .. + 3 of row r
 
     auto sin_at = [&](int j) { return S_in + ((size_t)(n * P + j) * HV + h) * SDK * DV; };
     // segment 0 starts from S0 (or zeros)
@@ -43,35 +44,47 @@ __global__ __launch_bounds__(256) void split_chain_kernel(const float *__restric
         Sb[idx] = x;
         sin_at(0)[(size_t)row * DV + c0 + col] = x;
     }
-    for (int j = 0; j + 1 < P; ++j) {
-        const float *map = maps + ((size_t)(n * (P - 1) + j) * HV + h) * SDK * DW;
-        __syncthreads();  // Sb holds S_in(j); Ms is free
-#pragma unroll 4
-        for (int i = 0; i < SDK * SDK / 4 / 256; ++i) {
+    // M of the next step is loaded into registers while this step computes (16 float4 per
+    // thread), then stored to LDS once every thread is done reading the current one.
+    constexpr int NLD = SDK * SDK / 4 / 256;
+    auto map_at = [&](int j) { return maps + ((size_t)(n * (P - 1) + j) * HV + h) * SDK * DW; };
+    f32x4 mreg[NLD];
+    auto load_m = [&](int j) {
+        const float *map = map_at(j);
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
             const int f = tid + 256 * i;
             const int rr = f / (SDK / 4), kq = f % (SDK / 4);
-            *reinterpret_cast<float4 *>(&Ms[rr * SLM + 4 * kq]) =
-                *reinterpret_cast<const float4 *>(map + (size_t)rr * DW + DV + 4 * kq);
+            mreg[i] = *reinterpret_cast<const f32x4 *>(map + (size_t)rr * DW + DV + 4 * kq);
         }
+    };
+    auto store_m = [&]() {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int f = tid + 256 * i;
+            const int rr = f / (SDK / 4), kq = f % (SDK / 4);
+            *reinterpret_cast<f32x4 *>(&Ms[rr * SLM + 4 * kq]) = mreg[i];
+        }
+    };
+    if (P > 1) load_m(0);
+    for (int j = 0; j + 1 < P; ++j) {
+        const float *map = map_at(j);
+        __syncthreads();  // Sb holds S_in(j); every read of Ms is done
+        store_m();
         __syncthreads();
-        f32x4 acc0 = *reinterpret_cast<const f32x4 *>(map + (size_t)r * DW + c0 + 4 * c4);
-        f32x4 acc1 = *reinterpret_cast<const f32x4 *>(map + (size_t)(r + 64) * DW + c0 + 4 * c4);
+        if (j + 2 < P) load_m(j + 1);
+        f32x4 acc = *reinterpret_cast<const f32x4 *>(map + (size_t)r * DW + c0 + 4 * c4);
         for (int k = 0; k < SDK; k += 4) {
             const f32x4 m0 = *reinterpret_cast<const f32x4 *>(&Ms[r * SLM + k]);
-            const f32x4 m1 = *reinterpret_cast<const f32x4 *>(&Ms[(r + 64) * SLM + k]);
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 const f32x4 sv = *reinterpret_cast<const f32x4 *>(&Sb[(k + kk) * SCB + 4 * c4]);
-                acc0 += m0[kk] * sv;
-                acc1 += m1[kk] * sv;
+                acc += m0[kk] * sv;
             }
         }
         __syncthreads();  // every read of Sb done
-        *reinterpret_cast<f32x4 *>(&Sb[r * SCB + 4 * c4]) = acc0;
-        *reinterpret_cast<f32x4 *>(&Sb[(r + 64) * SCB + 4 * c4]) = acc1;
-        float *dst = sin_at(j + 1);
-        *reinterpret_cast<f32x4 *>(dst + (size_t)r * DV + c0 + 4 * c4) = acc0;
-        *reinterpret_cast<f32x4 *>(dst + (size_t)(r + 64) * DV + c0 + 4 * c4) = acc1;
+        *reinterpret_cast<f32x4 *>(&Sb[r * SCB + 4 * c4]) = acc;
+        *reinterpret_cast<f32x4 *>(sin_at(j + 1) + (size_t)r * DV + c0 + 4 * c4) = acc;
     }
 }
 
