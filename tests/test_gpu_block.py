@@ -169,12 +169,13 @@ def _check_normed(y, o_ref, v_ref, bi, dtype, rounded_o, what):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("norm", [False, True])
-def test_decode_block_ops(dtype, norm):
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 32), (32, 64)])
+def test_decode_block_ops(dtype, norm, dk, dv):
     """Decode with g, beta given as raw projections (A_log, dt_bias, sigmoid) and the fused norm."""
-    _say(f"decode block ops {dtype} norm={norm}")
-    N, HQK, HV, d = 40, 2, 4, 128
-    inp = W.make_inputs("dec", 64, [1] * N, HQK, HV, d, d, dtype, 3.0, 1.0, 0.05)
-    bi = W.block_inputs(65, [1] * N, HQK, HV, d, d, dtype)
+    _say(f"decode block ops {dtype} norm={norm} dk={dk} dv={dv}")
+    N, HQK, HV = 40, 2, 4
+    inp = W.make_inputs("dec", 64, [1] * N, HQK, HV, dk, dv, dtype, 3.0, 1.0, 0.05)
+    bi = W.block_inputs(65, [1] * N, HQK, HV, dk, dv, dtype)
     dd = to_device(inp)
     S = dd["S0"].clone()
     kw = dict(A_log=_dev(bi.A_log, dtype), dt_bias=_dev(bi.dt_bias, dtype), beta_logits=True)
