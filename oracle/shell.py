@@ -13,7 +13,12 @@ stated here in float64, in the order the page applies them:
 * ``gates_np``        -- the decay and write-strength gates from their raw
                          projections: g = -exp(A_log) softplus(a + dt_bias),
                          beta = sigmoid(b)  ([HB7] table row "in_proj_a, dt_bias,
-                         A_log" and row "in_proj_b -> sigmoid").
+                         A_log" and row "in_proj_b -> sigmoid"); or, as the
+                         learn-llm page 13_linear_attention_viz ([LLV]) describes
+                         its RecurrentMixer (an a projection with a bias started at
+                         3.0, so that alpha = sigmoid(3) ~ 0.95 at the start of
+                         training), alpha = sigmoid(a + bias), i.e.
+                         g = log sigmoid(a + bias).
 * ``conv_silu_np``    -- the depthwise causal short convolution (window 4,
                          every channel on its own) followed by SiLU, on the
                          concatenated q | k | v channels ([HB7] table row
@@ -61,17 +66,22 @@ def silu(x):
     return x * sigmoid(x)
 
 
-def gates_np(a, b, A_log, dt_bias):
+def gates_np(a, b, A_log, dt_bias, *, alpha_sigmoid=False):
     """Raw projections a, b [T, HV] and per-head A_log, dt_bias [HV] -> (g, beta) [T, HV].
 
     [HB7] block listing / parts table: g = -exp(A_log) * softplus(a + dt_bias) (always
     <= 0, so the decay exp(g) lies in (0, 1]); beta = sigmoid(b).
+    alpha_sigmoid=True ([LLV] RecurrentMixer): alpha = sigmoid(a + dt_bias), so
+    g = log sigmoid(a + dt_bias) = -softplus(-(a + dt_bias)); A_log is not used.
     """
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
-    A_log = np.asarray(A_log, dtype=np.float64)
     dt_bias = np.asarray(dt_bias, dtype=np.float64)
-    g = -np.exp(A_log)[None, :] * softplus(a + dt_bias[None, :])
+    if alpha_sigmoid:
+        g = -softplus(-(a + dt_bias[None, :]))
+    else:
+        A_log = np.asarray(A_log, dtype=np.float64)
+        g = -np.exp(A_log)[None, :] * softplus(a + dt_bias[None, :])
     return g, sigmoid(b)
 
 

@@ -49,6 +49,19 @@ def test_gates_forget_faster_with_larger_A_log():
     assert (g[:, 0] > g[:, 1]).all() and (g[:, 1] > g[:, 2]).all()
 
 
+def test_alpha_sigmoid_gate():
+    """[LLV]: the alpha bias starts at 3.0, so alpha = sigmoid(3) ~ 0.95 at the start of training."""
+    g, _ = shell.gates_np([[0.0, -3.0, 40.0]], [[0.0, 0.0, 0.0]], None, [3.0, 3.0, 3.0], alpha_sigmoid=True)
+    assert math.exp(g[0, 0]) == pytest.approx(1.0 / (1.0 + math.exp(-3.0)), rel=1e-15)
+    assert round(math.exp(g[0, 0]), 2) == 0.95
+    assert g[0, 1] == pytest.approx(math.log(0.5), abs=1e-15)          # a + bias = 0
+    assert -1e-18 < g[0, 2] <= 0.0                                      # alpha -> 1
+    rng = np.random.default_rng(7)
+    a = rng.normal(0, 5, (50, 4))
+    g2, _ = shell.gates_np(a, a, None, np.zeros(4), alpha_sigmoid=True)
+    np.testing.assert_allclose(np.exp(g2), 1.0 / (1.0 + np.exp(-a)), rtol=1e-14)
+
+
 # ------------------------------------------------------------------ SiLU
 def test_silu_values():
     assert shell.silu(0.0) == 0.0
