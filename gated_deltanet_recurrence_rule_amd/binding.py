@@ -32,7 +32,8 @@ _lib = None
 class BlockOps(ctypes.Structure):
     """gdn_block_ops: gates from raw projections and the gated RMS norm (include/gdn.h)."""
     _fields_ = [("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p), ("beta_logits", ctypes.c_int32),
-                ("z", ctypes.c_void_p), ("norm_w", ctypes.c_void_p), ("norm_eps", ctypes.c_float)]
+                ("z", ctypes.c_void_p), ("norm_w", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
+                ("alpha_sigmoid", ctypes.c_int32)]
 
 
 class GdnError(RuntimeError):
@@ -127,20 +128,20 @@ def _need_opt(t: Optional[torch.Tensor], name: str, dtype):
         _need(t, name, dtype)
 
 
-def _block_ops(A_log, dt_bias, beta_logits, z, norm_w, norm_eps, io_dtype):
+def _block_ops(A_log, dt_bias, beta_logits, z, norm_w, norm_eps, io_dtype, alpha_sigmoid=False):
     """A BlockOps for the given parts, or None when none is asked for."""
-    if A_log is None and dt_bias is None and not beta_logits and z is None:
+    if A_log is None and dt_bias is None and not beta_logits and z is None and not alpha_sigmoid:
         return None
     _need_opt(A_log, "A_log", torch.float32)
     _need_opt(dt_bias, "dt_bias", torch.float32)
     _need_opt(z, "z", io_dtype)
     _need_opt(norm_w, "norm_w", torch.float32)
-    if dt_bias is not None and A_log is None:
-        raise ValueError("dt_bias is only used with A_log")
+    if dt_bias is not None and A_log is None and not alpha_sigmoid:
+        raise ValueError("dt_bias is only used with A_log or alpha_sigmoid")
     return BlockOps(None if A_log is None else A_log.data_ptr(),
                     None if dt_bias is None else dt_bias.data_ptr(), 1 if beta_logits else 0,
                     None if z is None else z.data_ptr(), None if norm_w is None else norm_w.data_ptr(),
-                    float(norm_eps))
+                    float(norm_eps), 1 if alpha_sigmoid else 0)
 
 
 def _need(t: torch.Tensor, name: str, dtype=None):
@@ -155,7 +156,8 @@ def _need(t: torch.Tensor, name: str, dtype=None):
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch.Tensor],
                 beta: Optional[torch.Tensor], S: torch.Tensor, *, scale: float = 1.0,
                 o: Optional[torch.Tensor] = None, variant="gated_delta", A_log=None, dt_bias=None,
-                beta_logits: bool = False, z=None, norm_w=None, norm_eps: float = 1e-6) -> torch.Tensor:
+                beta_logits: bool = False, z=None, norm_w=None, norm_eps: float = 1e-6,
+                alpha_sigmoid: bool = False) -> torch.Tensor:
     """One token for every sequence and V head; S [N, HV, dk, dv] fp32 is updated in place.
 
     q, k [N, HQK, dk]; v [N, HV, dv] (bf16 or fp32, one type); g, beta [N, HV] fp32.
@@ -163,7 +165,8 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[t
     "gated_linear" or "linear" (gdn_variant); the library decides which of g / beta
     may be None for it.  Block parts (gdn_block_ops): A_log, dt_bias [HV] fp32 make g the
     raw decay projection; beta_logits makes beta the raw projection b; z [N, HV, dv] with
-    norm_w [dv] and norm_eps applies the gated RMS norm to o.
+    norm_w [dv] and norm_eps applies the gated RMS norm to o; alpha_sigmoid (with dt_bias as
+    the bias) makes g the raw a of alpha = sigmoid(a + bias) instead.
     """
     N, HQK, dk = q.shape
     HV, dv = v.shape[1], v.shape[2]
@@ -177,7 +180,7 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[t
     _need(o, "o", v.dtype)
     var = _variant_code(variant)
     lib = load()
-    ops = _block_ops(A_log, dt_bias, beta_logits, z, norm_w, norm_eps, v.dtype)
+    ops = _block_ops(A_log, dt_bias, beta_logits, z, norm_w, norm_eps, v.dtype, alpha_sigmoid)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(o), N, HQK, HV, dk, dv,
             _dtype_code(q), float(scale))
     if ops is not None:
@@ -202,7 +205,8 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch
             S_T: Optional[torch.Tensor] = None, output_state: bool = True,
             workspace: Optional[torch.Tensor] = None,
             variant="gated_delta", A_log=None, dt_bias=None, beta_logits: bool = False, z=None,
-            norm_w=None, norm_eps: float = 1e-6) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+            norm_w=None, norm_eps: float = 1e-6,
+            alpha_sigmoid: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Whole sequences of a packed batch.
 
     q, k [total_T, HQK, dk]; v [total_T, HV, dv]; g, beta [total_T, HV] fp32.
@@ -249,7 +253,7 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch
     var = _variant_code(variant)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), host_ptr, n_seq, total_T,
             _ptr(S0), _ptr(o), _ptr(S_T), HQK, HV, dk, dv, code, float(scale))
-    ops = _block_ops(A_log, dt_bias, beta_logits, z, norm_w, norm_eps, v.dtype)
+    ops = _block_ops(A_log, dt_bias, beta_logits, z, norm_w, norm_eps, v.dtype, alpha_sigmoid)
     if ops is not None:
         _check(lib.gdn_prefill_ex(*args, var, ctypes.byref(ops), _ptr(workspace), ws_bytes,
                                   _stream(q.device)))

@@ -85,8 +85,10 @@ gdn_status check_seqlens(const int32_t *cu_seqlens, const int32_t *cu_seqlens_ho
 // The optional block parts: which gates they transform, and the norm's operands.
 gdn_status check_ops(const gdn_block_ops *ops, gdn_variant variant, const float *beta, int64_t tokens) {
     if (!ops) return GDN_OK;
-    if (ops->A_log && !variant_gated(variant))
-        return fail(GDN_ERR_UNSUPPORTED, "A_log is set but the variant has no decay");
+    if ((ops->A_log || ops->alpha_sigmoid) && !variant_gated(variant))
+        return fail(GDN_ERR_UNSUPPORTED, "a decay gate form is set but the variant has no decay");
+    if (ops->A_log && ops->alpha_sigmoid)
+        return fail(GDN_ERR_VALUE, "A_log and alpha_sigmoid are two forms of the decay gate: set one");
     if (ops->z && !(ops->norm_eps >= 0.f)) return fail(GDN_ERR_VALUE, "norm_eps must be >= 0");
     if (tokens == 0) return GDN_OK;
     if (ops->beta_logits && !beta) return fail(GDN_ERR_NULL, "beta_logits needs a non-NULL beta");
@@ -108,7 +110,8 @@ gdn::GateArgs gate_args(const gdn_block_ops *ops, gdn_variant variant) {
     gdn::GateArgs ga;
     if (ops) {
         ga.A_log = variant_gated(variant) ? ops->A_log : nullptr;
-        ga.dt_bias = ga.A_log ? ops->dt_bias : nullptr;
+        ga.alpha_sigmoid = (variant_gated(variant) && ops->alpha_sigmoid) ? 1 : 0;
+        ga.dt_bias = (ga.A_log || ga.alpha_sigmoid) ? ops->dt_bias : nullptr;
         ga.beta_logit = ops->beta_logits ? 1 : 0;
     }
     return ga;

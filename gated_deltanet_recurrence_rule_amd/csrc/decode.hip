@@ -71,7 +71,8 @@ __global__ __launch_bounds__((DV / 4) * kRowGroups) void decode_kernel(
     float a = 1.f, b = 1.f;
     if (g) {
         float x = g[unit];
-        if (gate.A_log) x = -expf(gate.A_log[h]) * softplus_f(x + (gate.dt_bias ? gate.dt_bias[h] : 0.f));
+        if (gate.alpha_sigmoid) x = -softplus_f(-(x + (gate.dt_bias ? gate.dt_bias[h] : 0.f)));
+        else if (gate.A_log) x = -expf(gate.A_log[h]) * softplus_f(x + (gate.dt_bias ? gate.dt_bias[h] : 0.f));
         a = expf(x);
     }
     if (beta) b = gate.beta_logit ? sigmoid_f(beta[unit]) : beta[unit];

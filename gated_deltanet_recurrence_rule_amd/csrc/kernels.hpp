@@ -9,9 +9,12 @@ namespace gdn {
 // Gates from raw projections: with A_log set, g holds the raw decay projection a and the
 // log-decay is -exp(A_log[h]) softplus(a + dt_bias[h]) (dt_bias may be null = 0); with
 // beta_logit set, beta holds the raw projection b and the write strength is sigmoid(b).
+// With alpha_sigmoid set instead, g holds the raw a and the log-decay is
+// log sigmoid(a + dt_bias[h]).
 struct GateArgs {
     const float *A_log = nullptr, *dt_bias = nullptr;
     int32_t beta_logit = 0;
+    int32_t alpha_sigmoid = 0;
 };
 
 // Split sequences for the chunked prefill (see prefill_chunked.hip): P segments per sequence;

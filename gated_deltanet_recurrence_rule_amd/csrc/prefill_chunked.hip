@@ -548,11 +548,13 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     // times the 16-byte segment s = gt % 16 of their q and k rows (d = 8 s .. 8 s + 7).
     uint4 kreg[2][2], qreg[2][2];  // [p][token of the pair]
     float greg = 0.f, breg = 0.f;  // Gram wave 3: token = lane
-    // gates from raw projections: the head's exp(A_log) and dt_bias (padding tokens carry
-    // -inf raw values, which both maps send to 0)
+    // gates from raw projections: the head's exp(A_log) and dt_bias (padding tokens carry raw
+    // values that every map sends to 0: -inf for -exp(A_log) softplus and for sigmoid(b), +inf
+    // for log sigmoid)
     const float g_ea = gate.A_log ? expf(gate.A_log[h]) : 0.f;
     const float g_dtb = gate.dt_bias ? gate.dt_bias[h] : 0.f;
-    const bool g_raw = gate.A_log != nullptr, b_raw = gate.beta_logit != 0;
+    const bool g_raw = gate.A_log != nullptr || gate.alpha_sigmoid, b_raw = gate.beta_logit != 0;
+    const bool g_sig = gate.alpha_sigmoid != 0;
     const size_t rs = (size_t)HQK * DK;  // token stride of q and k
     // token row of item (p, u) = 8 gw + 32 p + u (uniform) + 2 lq (lane)
     const int gwu = wu - 4;
@@ -599,7 +601,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             if (g) {
                 const rsrc_t gr = make_rsrc(g + (size_t)cs * HV + h, gbytes);
                 greg = ok ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gr, goff, 0, 0))
-                          : (gate.A_log ? -INFINITY : 0.f);
+                          : (g_sig ? INFINITY : (gate.A_log ? -INFINITY : 0.f));
             }
             if (beta) {
                 const rsrc_t br = make_rsrc(beta + (size_t)cs * HV + h, gbytes);
@@ -667,13 +669,13 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         if (gw == 3) {
             // inclusive prefix sum over the 64 lanes: within rows of 16 by row shifts, then
             // across rows by the row-15 and row-31 broadcasts (DPP, no LDS traffic)
-            // raw gates, straight-line so the staging above can hide them: softplus(t) =
-            // max(t, 0) + ln(1 + e^-|t|) and sigmoid(b) = 1 / (1 + e^-b) on the hardware exp2,
-            // log2 and reciprocal (when 1 + e^-|t| rounds to 1 the term dropped is < 6e-8)
+            // raw gates, straight-line so the staging above can hide them: softplus(+-t) =
+            // max(+-t, 0) + ln(1 + e^-|t|), log sigmoid(t) = -softplus(-t), and sigmoid(b) =
+            // 1 / (1 + e^-b) on the hardware exp2, log2 and reciprocal (when 1 + e^-|t| rounds
+            // to 1 the term dropped is < 6e-8)
             const float tt = greg + g_dtb;
-            const float sp = fmaxf(tt, 0.f) +
-                             0.69314718055994531f * __builtin_amdgcn_logf(1.f + exp2_hw(-1.44269504088896341f * fabsf(tt)));
-            const float gl = g_raw ? -g_ea * sp : greg;
+            const float lt = 0.69314718055994531f * __builtin_amdgcn_logf(1.f + exp2_hw(-1.44269504088896341f * fabsf(tt)));
+            const float gl = g_raw ? (g_sig ? -(fmaxf(-tt, 0.f) + lt) : -g_ea * (fmaxf(tt, 0.f) + lt)) : greg;
             breg = b_raw ? __builtin_amdgcn_rcpf(1.f + exp2_hw(-1.44269504088896341f * breg)) : breg;
             float x = gl * 1.44269504088896341f;  // log2(e)
 #define GDN_DPP_ADD(ctrl, row_mask) \

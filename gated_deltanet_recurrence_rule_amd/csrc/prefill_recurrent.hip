@@ -112,7 +112,8 @@ __global__ __launch_bounds__(64) void prefill_recurrent_kernel(
         float a = 1.f, b = 1.f;
         if (g) {
             float x = graw;
-            if (gate.A_log) x = -expf(gate.A_log[h]) * softplus_f(x + (gate.dt_bias ? gate.dt_bias[h] : 0.f));
+            if (gate.alpha_sigmoid) x = -softplus_f(-(x + (gate.dt_bias ? gate.dt_bias[h] : 0.f)));
+            else if (gate.A_log) x = -expf(gate.A_log[h]) * softplus_f(x + (gate.dt_bias ? gate.dt_bias[h] : 0.f));
             a = expf(x);
         }
         if (beta) b = gate.beta_logit ? sigmoid_f(braw) : braw;

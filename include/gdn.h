@@ -200,7 +200,12 @@ gdn_status gdn_prefill_v(const void *q, const void *k, const void *v, const floa
  *               and the log-decay used is  g = -exp(A_log[h]) * softplus(a + dt_bias[h])
  *               (always <= 0).  Only for the gated variants (g is read); else
  *               GDN_ERR_UNSUPPORTED.
- *   dt_bias     [HV] fp32, or NULL for zeros; read only with A_log.
+ *   dt_bias     [HV] fp32, or NULL for zeros: the bias added to a (both decay forms).
+ *   alpha_sigmoid  non-zero: the other decay form, that of the learn-llm page
+ *               13_linear_attention_viz (its RecurrentMixer computes alpha from an a
+ *               projection with a bias): the g array holds the raw a and the decay is
+ *               alpha = sigmoid(a + dt_bias[h]), i.e. g = log sigmoid(a + dt_bias[h]).
+ *               Gated variants only (GDN_ERR_UNSUPPORTED); excludes A_log (GDN_ERR_VALUE).
  *   beta_logits non-zero: the beta array holds the raw projection b and the write strength
  *               used is sigmoid(b).  Needs a non-NULL beta (GDN_ERR_NULL).
  *
@@ -223,6 +228,7 @@ typedef struct gdn_block_ops {
     const void *z;
     const float *norm_w;
     float norm_eps;
+    int32_t alpha_sigmoid;
 } gdn_block_ops;
 
 /* gdn_decode_step_v plus the block parts in `ops` (may be NULL). */

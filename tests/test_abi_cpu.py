@@ -224,9 +224,10 @@ E_ALIAS, E_VALUE = -9, -10
 
 def _ops(B, **kw):
     from gated_deltanet_recurrence_rule_amd.binding import BlockOps
-    a = dict(A_log=None, dt_bias=None, beta_logits=0, z=None, norm_w=None, norm_eps=1e-6)
+    a = dict(A_log=None, dt_bias=None, beta_logits=0, z=None, norm_w=None, norm_eps=1e-6, alpha_sigmoid=0)
     a.update(kw)
-    return BlockOps(a["A_log"], a["dt_bias"], a["beta_logits"], a["z"], a["norm_w"], a["norm_eps"])
+    return BlockOps(a["A_log"], a["dt_bias"], a["beta_logits"], a["z"], a["norm_w"], a["norm_eps"],
+                    a["alpha_sigmoid"])
 
 
 def _decode_ex(lib, B, variant, ops, **kw):
@@ -255,6 +256,7 @@ def _prefill_ex(lib, B, variant, ops, **kw):
     ("logits_without_beta", GATED_LINEAR, E_NULL), ("z_without_w", GATED_DELTA, E_NULL),
     ("negative_eps", GATED_DELTA, E_VALUE), ("nan_eps", GATED_DELTA, E_VALUE),
     ("z_misaligned", GATED_DELTA, E_ALIGN), ("z_overlaps_o", GATED_DELTA, E_ALIAS),
+    ("alpha_ungated", DELTA, E_UNSUP), ("alpha_and_A_log", GATED_DELTA, E_VALUE),
 ])
 def test_block_ops_rejects(lib, call, case, variant, status):
     B = Bufs()
@@ -276,6 +278,10 @@ def test_block_ops_rejects(lib, call, case, variant, status):
         okw = dict(z=B.p(z, 4).value, norm_w=B.p(w).value)
     elif case == "z_overlaps_o":
         okw = dict(z=B.p(B.o, 64).value, norm_w=B.p(w).value)
+    elif case == "alpha_ungated":
+        okw, kw = dict(alpha_sigmoid=1), dict(g=None)
+    elif case == "alpha_and_A_log":
+        okw = dict(alpha_sigmoid=1, A_log=B.p(w).value)
     assert call(lib, B, variant, _ops(B, **okw), **kw) == status, lib.gdn_last_error()
     assert B.untouched() and np.all(z == 7.0)
 

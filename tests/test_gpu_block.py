@@ -315,3 +315,32 @@ def test_block_full_size_qwen3next():
                                 bi.norm_w, None, 1, 1, d, d)
             _check_normed(to_f64(o[t0:t1, h:h + 1]), o_ref, vn, sub, "bf16", True,
                           f"full-size normed read seq {n} head {h}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("call", ["decode", "prefill"])
+def test_alpha_sigmoid_gate(dtype, call):
+    """The learn-llm page's decay form alpha = sigmoid(a + bias), its bias near the page's
+    initial 3.0 (alpha ~ 0.95); prefill on ragged sequences (chunked MFMA kernel for bf16)."""
+    _say(f"alpha sigmoid gate {call} {dtype}")
+    HQK, HV, d = 2, 4, 128
+    lens = [1] * 24 if call == "decode" else [0, 1, 63, 64, 65, 260]
+    if call == "decode":
+        inp = W.make_inputs("dec", 73, lens, HQK, HV, d, d, dtype, 3.0, 1.0, 0.05)
+    else:
+        inp = W.random_small(73, lens, HQK, HV, d, d, dtype=dtype, s0=True)
+    bi = W.block_inputs(74, lens, HQK, HV, d, d, dtype)
+    bias = (bi.dt_bias + 2.0).astype(np.float32)               # ~ N(3, 0.5)
+    dd = to_device(inp)
+    kw = dict(alpha_sigmoid=True, dt_bias=_dev(bias, dtype), beta_logits=True)
+    if call == "decode":
+        S = dd["S0"].clone()
+        o = binding.decode_step(dd["q"], dd["k"], dd["v"], _dev(bi.a, dtype), _dev(bi.b, dtype), S, **kw)
+    else:
+        o, S = binding.prefill(dd["q"], dd["k"], dd["v"], _dev(bi.a, dtype), _dev(bi.b, dtype), cu_seqlens=dd["cu"],
+                               cu_seqlens_host=inp.cu_seqlens, S0=dd["S0"], **kw)
+    torch.cuda.synchronize()
+    g, beta = shell.gates_np(bi.a, bi.b, None, bias, alpha_sigmoid=True)
+    o_ref, S_ref = oracle.run(inp.as_f64("q"), inp.as_f64("k"), inp.as_f64("v"), g, beta, inp.cu_seqlens,
+                              inp.as_f64("S0"))
+    assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), dtype, f"alpha sigmoid {call}")
