@@ -38,7 +38,7 @@ CSRC = os.path.join(ROOT, "gated_deltanet_recurrence_rule_amd", "csrc")
 
 KERNELS = {
     # key: (kernel-name fragment, source file, summary file, workload text)
-    "prefill_chunked": ("prefill_chunked_kernel", "prefill_chunked.hip", "prefill_chunked_qwen3next_4x16384.txt",
+    "prefill_chunked": ("prefill_chunked_kernel<true, false>", "prefill_chunked.hip", "prefill_chunked_qwen3next_4x16384.txt",
                         "prefill, 4 sequences x 16384 tokens, 16 QK / 32 V heads, dk = dv = 128, "
                         "bf16 q/k/v/o, fp32 S0 -> S_T"),
     "decode": ("decode_kernel<128, 128, unsigned short>", "decode.hip", "decode_b256_h32_d128.txt",
