@@ -143,15 +143,22 @@ def main():
     def decode():
         binding.decode_step(D["q"], D["k"], D["v"], D["g"], D["beta"], D["S"], o=o_d)
 
-    # Clock settle (untimed): the first ~10 ms of load run ~20% slower than sustained.
+    # Clock settle (untimed): the first ~10 ms of load run ~20% slower than sustained.  It
+    # repeats the timed region's pattern (K prefill calls, then K decode steps), so that a
+    # kernel trace of the whole run averages calls made the way the timed ones are: a decode
+    # step launched right after the MFMA-heavy prefill runs ~10% slower than one after
+    # another decode step.
     if args.settle_ms > 0:
         t_set = time.perf_counter()
         while (time.perf_counter() - t_set) * 1e3 < args.settle_ms:
-            prefill()
-            decode()
+            for _ in range(args.steps):
+                prefill()
+            for _ in range(args.steps):
+                decode()
             torch.cuda.synchronize()
     for _ in range(args.warmup):
         prefill()
+    for _ in range(args.warmup):
         decode()
     torch.cuda.synchronize()
 

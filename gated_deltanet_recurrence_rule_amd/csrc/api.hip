@@ -238,6 +238,7 @@ gdn_status gdn_decode_step_ex(const void *q, const void *k, const void *v, const
         a.norm_w = ops->norm_w;
         a.norm_eps = ops->norm_eps;
     }
+    a.max_wgs = 4 * device_cus();
     return hip_status(gdn::launch_decode(a, dtype == GDN_BF16, stream), "decode launch");
 }
 

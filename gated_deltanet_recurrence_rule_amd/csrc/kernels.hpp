@@ -42,6 +42,7 @@ struct DecodeArgs {
     const void *z = nullptr;
     const float *norm_w = nullptr;
     float norm_eps = 0.f;
+    int32_t max_wgs = 0;  // grid cap of the persistent kernel (0: one workgroup per table)
 };
 
 struct PrefillArgs {

@@ -65,6 +65,21 @@ def test_decode_full_size():
     assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), "bf16", "decode B=256")
 
 
+@pytest.mark.parametrize("N,HV,dv", [(300, 4, 128), (1030, 1, 64), (257, 8, 32)])
+def test_decode_persistent_walk(N, HV, dv):
+    """More tables than the capped grid, and a count that does not divide it: workgroups
+    walk several tables each and some take one more than others.  Every table must be
+    stepped exactly once (a table stepped twice or skipped fails the state check)."""
+    _say(f"decode persistent walk N={N} HV={HV} dv={dv}")
+    inp = W.make_inputs("dec", 33, [1] * N, 1, HV, 128, dv, "bf16", 3.0, 1.0, 0.05)
+    d = to_device(inp)
+    S = d["S0"].clone()
+    o = binding.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], S)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.run_inputs(inp)
+    assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), "bf16", "decode walk")
+
+
 def test_decode_scale_and_repeat():
     """A second step continues from the first; scale multiplies only the read."""
     inp = W.make_inputs("dec", 32, [1] * 3, 1, 2, 128, 128, "bf16", 3.0, 1.0, 0.05)
