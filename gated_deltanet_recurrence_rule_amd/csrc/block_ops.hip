@@ -192,15 +192,17 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_kernel(
     else if (c < 2 * Cq) { dst = k; ld = Cq; col = c - Cq; }
     else { dst = v; ld = Cv; col = c - 2 * Cq; }
 
+    // device entries are clamped into [0, total_T] and made non-decreasing, so no cu_seqlens
+    // contents can send the kernel outside its buffers
     int n = seq_of(cu, N, eq_len, tb);
-    int64_t s0 = cu ? (int64_t)cu[n] : (int64_t)n * eq_len;
-    int64_t s1 = cu ? (int64_t)cu[n + 1] : s0 + eq_len;
+    int64_t s0 = cu ? clamp_tok(cu[n], 0, total_T) : (int64_t)n * eq_len;
+    int64_t s1 = cu ? clamp_tok(cu[n + 1], s0, total_T) : s0 + eq_len;
 
     // input at absolute token t of sequence n (t may be up to 3 before its start)
     auto fetch = [&](int64_t t, float (&e)[8]) {
         if (t >= s0) {
             vec8<T>::ld(x + t * Ct + c, e);
-        } else if (state_in) {
+        } else if (state_in && s0 - t <= 3) {
             vec8<T>::ld(state_in + ((size_t)n * 3 + (size_t)(3 - (s0 - t))) * Ct + c, e);
         } else {
 #pragma unroll
@@ -229,13 +231,18 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_kernel(
     };
     int64_t t = tb;
     while (t < te) {
-        if (t == s1) {
-            // the next non-empty sequence starts here: refill the window from its state
+        if (t >= s1) {
+            // the next non-empty sequence starts here (t == s1 for a consistent array):
+            // refill the window from its state
             do {
-                ++n;
                 s0 = s1;
-                s1 = cu ? (int64_t)cu[n + 1] : s0 + eq_len;
-            } while (s1 == s0);
+                if (n + 1 < N) {
+                    ++n;
+                    s1 = cu ? clamp_tok(cu[n + 1], s0, total_T) : s0 + eq_len;
+                } else {
+                    s1 = total_T;  // only an inconsistent device array gets here
+                }
+            } while (s1 <= t);
             fetch(t - 3, e1);
             fetch(t - 2, e2);
             fetch(t - 1, e3);
@@ -279,13 +286,14 @@ __global__ __launch_bounds__(kConvThreads) void conv_silu_kernel(
 // each thread reads its three entries before it writes them.
 template <typename T>
 __global__ __launch_bounds__(kConvThreads) void conv_state_kernel(
-    const T *__restrict__ x, const int32_t *__restrict__ cu, int64_t eq_len, int N, const T *state_in,
+    const T *__restrict__ x, const int32_t *__restrict__ cu, int64_t eq_len, int N, int64_t total_T,
+    const T *state_in,
     T *state_out, int Ct) {
     const int c = 8 * (blockIdx.y * kConvThreads + threadIdx.x);
     const int n = blockIdx.x;
     if (c >= Ct || n >= N) return;
-    const int64_t s0 = cu ? (int64_t)cu[n] : (int64_t)n * eq_len;
-    const int64_t len = (cu ? (int64_t)cu[n + 1] : s0 + eq_len) - s0;
+    const int64_t s0 = cu ? clamp_tok(cu[n], 0, total_T) : (int64_t)n * eq_len;
+    const int64_t len = (cu ? clamp_tok(cu[n + 1], s0, total_T) : s0 + eq_len) - s0;
     float e[3][8];
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
@@ -319,7 +327,7 @@ hipError_t launch_conv(const ConvArgs &a, hipStream_t stream) {
     }
     if (a.state_out) {
         hipLaunchKernelGGL((conv_state_kernel<T>), dim3((unsigned)a.N, cblocks), dim3(kConvThreads), 0, stream,
-                           static_cast<const T *>(a.x), a.cu_seqlens, a.eq_len, a.N,
+                           static_cast<const T *>(a.x), a.cu_seqlens, a.eq_len, a.N, a.total_T,
                            static_cast<const T *>(a.state_in), static_cast<T *>(a.state_out), Ct);
         return hipGetLastError();
     }

@@ -63,6 +63,12 @@ __device__ __forceinline__ float inv_norm(float ss) {
 // math library; silu, applied to every element of the streamed block parts, uses the
 // hardware exp2 and reciprocal (about 1 ulp each): x / (1 + 2^(-x log2 e)).  Very negative
 // x gives 2^(+big) = inf and a reciprocal of 0, so silu -> -0 as it should.
+// a token index read from a device cu_seqlens array, clamped into [lo, hi]
+__device__ __forceinline__ int64_t clamp_tok(int32_t x, int64_t lo, int64_t hi) {
+    const int64_t v = x;
+    return v < lo ? lo : (v > hi ? hi : v);
+}
+
 __device__ __forceinline__ float softplus_f(float x) { return x > 20.f ? x : log1pf(expf(x)); }
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
 __device__ __forceinline__ float silu_f(float x) {

@@ -56,6 +56,9 @@ struct PrefillArgs {
     const float *S0;
     void *o;
     float *S_T;
+    // what the kernels take for the sequence bounds: eq_len without cu_seqlens, else total_T
+    // (the range every device entry is clamped into)
+    int64_t span() const { return cu_seqlens ? total_T : eq_len; }
     int32_t HQK, HV, dk, dv;
     float scale;
     void *workspace;

@@ -205,7 +205,7 @@ template <bool DELTA, bool SPLIT>
 __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
-    const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ order, int64_t eq_len,
+    const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ order, int64_t span,
     const float *__restrict__ S0, uint16_t *__restrict__ o, float *__restrict__ S_T, int HV, int DV,
     int rep, int NG, int M, float scale, GateArgs gate, SplitArgs sp) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
@@ -273,11 +273,13 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
 
     int64_t t0, t1;
     if (cu_seqlens) {
-        t0 = cu_seqlens[nseq];
-        t1 = cu_seqlens[nseq + 1];
+        // span = total_T here: entries are clamped into [0, total_T] and made non-decreasing,
+        // so no device array can send the kernel outside the token buffers
+        t0 = clamp_tok(cu_seqlens[nseq], 0, span);
+        t1 = clamp_tok(cu_seqlens[nseq + 1], t0, span);
     } else {
-        t0 = (int64_t)nseq * eq_len;
-        t1 = t0 + eq_len;
+        t0 = (int64_t)nseq * span;
+        t1 = t0 + span;
     }
     if (mode != 0) {
         // segment seg: chunks [seg cps, (seg + 1) cps) of the sequence, cps = ceil(chunks / P)
@@ -973,7 +975,7 @@ hipError_t launch_prefill_chunked(const PrefillArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(kern, dim3((unsigned)nwg),
                        dim3(NT), 0, stream,
                        static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
-                       static_cast<const uint16_t *>(a.v), a.g, a.beta, a.cu_seqlens, a.order, a.eq_len,
+                       static_cast<const uint16_t *>(a.v), a.g, a.beta, a.cu_seqlens, a.order, a.span(),
                        a.S0, static_cast<uint16_t *>(a.o), a.S_T, a.HV, a.dv, rep, (int)NG, (int)M, a.scale, a.gate,
                        a.split);
     return hipGetLastError();

@@ -25,7 +25,7 @@ template <int DK, typename T>
 __global__ __launch_bounds__(64) void prefill_recurrent_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
-    const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ order, int64_t eq_len,
+    const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ order, int64_t span,
     const float *__restrict__ S0, T *__restrict__ o, float *__restrict__ S_T, int HV, int DV, int rep,
     float scale, int delta, GateArgs gate) {
     constexpr int EPL = (DK + 63) / 64;  // q/k elements per lane
@@ -44,12 +44,12 @@ __global__ __launch_bounds__(64) void prefill_recurrent_kernel(
     const bool active = j < DV;
 
     int64_t t0, t1;
-    if (cu_seqlens) {
-        t0 = cu_seqlens[n];
-        t1 = cu_seqlens[n + 1];
+    if (cu_seqlens) {  // span = total_T: entries clamped into [0, total_T], non-decreasing
+        t0 = clamp_tok(cu_seqlens[n], 0, span);
+        t1 = clamp_tok(cu_seqlens[n + 1], t0, span);
     } else {
-        t0 = (int64_t)n * eq_len;
-        t1 = t0 + eq_len;
+        t0 = (int64_t)n * span;
+        t1 = t0 + span;
     }
 
     float s[DK];
@@ -143,7 +143,7 @@ hipError_t launch(const PrefillArgs &a, hipStream_t stream) {
     dim3 grid((unsigned)((int64_t)a.N * a.HV), (unsigned)((a.dv + 63) / 64));
     hipLaunchKernelGGL((prefill_recurrent_kernel<DK, T>), grid, dim3(64), 0, stream,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
-                       static_cast<const T *>(a.v), a.g, a.beta, a.cu_seqlens, a.order, a.eq_len, a.S0,
+                       static_cast<const T *>(a.v), a.g, a.beta, a.cu_seqlens, a.order, a.span(), a.S0,
                        static_cast<T *>(a.o), a.S_T, a.HV, a.dv, rep, a.scale, a.delta, a.gate);
     return hipGetLastError();
 }

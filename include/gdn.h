@@ -154,8 +154,11 @@ size_t gdn_prefill_workspace_size(int32_t N, int64_t total_T, int32_t HQK, int32
  *               cu[N] = total_T.  Empty sequences are allowed.  NULL means N
  *               equal sequences of total_T / N tokens (N must divide total_T).
  *   cu_seqlens_host  optional host copy of the same array.  When given it is
- *               validated (GDN_ERR_SEQLENS); when NULL the device array is
- *               trusted as is.
+ *               validated (GDN_ERR_SEQLENS); when NULL the device array is not
+ *               validated, but the kernels clamp every entry they read into
+ *               [0, total_T] (and each sequence's end to at least its start), so
+ *               no contents of it can make them access memory outside the
+ *               buffers; the results for an inconsistent array are unspecified.
  *               Sequences are launched longest first: unless the host copy shows
  *               lengths that never increase, a small ranking kernel writes the
  *               order into the workspace ahead of the scan (same stream).  A HIP

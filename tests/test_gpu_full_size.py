@@ -66,3 +66,30 @@ def test_varlen_with_long_tail():
     lens = np.diff(inp.cu_seqlens)
     short = [int(i) for i in np.argsort(lens)[:3]] + [int(np.argsort(lens)[32])]
     _run_and_check(inp, [(short, [0, 5, 31]), ([inp.N - 1], [2, 29])], "varlen")
+
+
+def test_decode_large_batch():
+    """1024 sequences x 32 V heads (16 QK), d = 128: 32768 tables, 2 GiB of state, so every
+    workgroup of the capped decode grid walks 32 tables.  Sampled units against the oracle;
+    then every table and read against the same step run in slices of 16 sequences (512
+    tables, one workgroup each, no walk), which must agree bit for bit: a table skipped or
+    stepped twice by the walk cannot."""
+    _say("full size: decode 1024 sequences x 32 heads")
+    inp = W.decode(seed=12, N=1024)
+    d = to_device(inp)
+    S = d["S0"].clone()
+    o = binding.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], S)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    ref = oracle_units(inp, [0, 1, 511, 1000, 1023], [0, 7, 16, 31])
+    for (n, h), (o_ref, S_ref) in ref.items():
+        v_ref = inp.as_f64_rows("v", n, n + 1)[:, h]
+        assert_parity(to_f64(o[n:n + 1, h]), to_f64(S[n, h]), o_ref, S_ref, v_ref, "bf16",
+                      f"decode seq {n} head {h}")
+    for a in range(0, 1024, 16):
+        b = a + 16
+        Sb = d["S0"][a:b].clone()
+        ob = binding.decode_step(d["q"][a:b], d["k"][a:b], d["v"][a:b], d["g"][a:b], d["beta"][a:b], Sb)
+        torch.cuda.synchronize()
+        assert torch.equal(ob, o[a:b]), f"reads of sequences {a}..{b - 1} differ from the sliced step"
+        assert torch.equal(Sb, S[a:b]), f"tables of sequences {a}..{b - 1} differ from the sliced step"

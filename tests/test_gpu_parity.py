@@ -223,3 +223,32 @@ def test_prefill_rejects_bad_args_on_device():
     with pytest.raises(binding.GdnError):
         binding.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu"],
                         cu_seqlens_host=[0, 9, 15])
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_device_seqlens_out_of_range_are_clamped(dtype, d):
+    """Without the host copy the device cu_seqlens is not validated, but every entry the
+    kernels read is clamped into [0, total_T]: [-5, 40, 40, 300] over 120 tokens runs
+    exactly as [0, 40, 40, 120] (prefill and the convolution, bit for bit)."""
+    _say(f"device seqlens clamp {dtype} d={d}")
+    inp = W.random_small(49, [40, 0, 80], 2, 4, d, d, dtype=dtype, s0=True)
+    dd = to_device(inp)
+    bad = torch.tensor([-5, 40, 40, 300], dtype=torch.int32, device="cuda")
+    o1, S1 = binding.prefill(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], cu_seqlens=dd["cu"],
+                             cu_seqlens_host=inp.cu_seqlens, S0=dd["S0"])
+    o2, S2 = binding.prefill(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], cu_seqlens=bad, S0=dd["S0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    Ct = 2 * 2 * d + 4 * d
+    gen = torch.Generator(device="cpu").manual_seed(49)
+    x = torch.randn(120, Ct, generator=gen).to(dd["v"].dtype).cuda()
+    w = torch.randn(Ct, 4, generator=gen).cuda()
+    st = torch.randn(3, 3, Ct, generator=gen).to(dd["v"].dtype).cuda()
+    so1, so2 = torch.empty_like(st), torch.empty_like(st)
+    r1 = binding.conv_silu(x, w, HQK=2, HV=4, dk=d, dv=d, cu_seqlens=dd["cu"], cu_seqlens_host=inp.cu_seqlens,
+                           state_in=st, state_out=so1)
+    r2 = binding.conv_silu(x, w, HQK=2, HV=4, dk=d, dv=d, cu_seqlens=bad, state_in=st, state_out=so2)
+    torch.cuda.synchronize()
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+    assert torch.equal(so1, so2)
