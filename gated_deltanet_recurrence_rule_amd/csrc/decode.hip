@@ -4,7 +4,7 @@
 // section "The formula"; the four steps of its figure "one step of the delta
 // rule"):  S <- a S;  p = S^T k;  S <- S + k (b (v - p))^T;  o = S^T q.
 //
-// One workgroup owns one (sequence, V head) table S [DK, DV] fp32 and touches
+// A workgroup owns one (sequence, V head) table S [DK, DV] fp32 at a time and touches
 // it in exactly one read pass and one write pass, which is what makes the step
 // HBM-bound at ~8 bytes of state traffic per table element.  The single pass
 // rests on two rewrites of the same arithmetic:
