@@ -3,6 +3,7 @@
 // Every check runs before anything is enqueued, so a failing call writes
 // nothing.  The declarations and their contracts are in include/gdn.h.
 #include <stdarg.h>
+#include <atomic>
 #include <stdio.h>
 #include <string.h>
 
@@ -117,19 +118,19 @@ gdn::GateArgs gate_args(const gdn_block_ops *ops, gdn_variant variant) {
     return ga;
 }
 
-// Compute units of the current device (cached per device; 256, MI355X's count, if the
-// runtime cannot say).
+// Compute units of the current device (cached per device, safe to call from several host
+// threads; 256, MI355X's count, if the runtime cannot say).
 int device_cus() {
-    static int cache[64] = {0};
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] == 0) {
-        int cus = 0;
+    int cus = cache[dev].load(std::memory_order_relaxed);
+    if (cus == 0) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
-        cache[dev] = cus;
+        cache[dev].store(cus, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return cus;
 }
 
 // Segments per sequence for the chunked prefill.  A batch whose (sequence, V head, 64-column)
@@ -182,7 +183,7 @@ const char *gdn_status_str(gdn_status s) {
         case GDN_ERR_NULL: return "null pointer";
         case GDN_ERR_SHAPE: return "bad shape";
         case GDN_ERR_DTYPE: return "bad dtype";
-        case GDN_ERR_UNSUPPORTED: return "unsupported head dimension";
+        case GDN_ERR_UNSUPPORTED: return "unsupported configuration";
         case GDN_ERR_ALIGN: return "misaligned pointer";
         case GDN_ERR_SEQLENS: return "bad sequence lengths";
         case GDN_ERR_WORKSPACE: return "workspace too small";

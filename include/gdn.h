@@ -58,7 +58,8 @@ typedef enum {
     GDN_ERR_NULL = -1,        /* a required pointer is NULL                           */
     GDN_ERR_SHAPE = -2,       /* negative size, HV % HQK != 0, mismatched lengths      */
     GDN_ERR_DTYPE = -3,       /* unknown gdn_dtype                                     */
-    GDN_ERR_UNSUPPORTED = -4, /* dk or dv not in {32, 64, 128}, or an unknown variant   */
+    GDN_ERR_UNSUPPORTED = -4, /* dk or dv not in {32, 64, 128}, an unknown variant, or a
+                                 decay gate form with a variant that has no decay      */
     GDN_ERR_ALIGN = -5,       /* a pointer breaks the alignment rule above             */
     GDN_ERR_SEQLENS = -6,     /* cu_seqlens_host malformed, or N does not divide T     */
     GDN_ERR_WORKSPACE = -7,   /* workspace smaller than gdn_prefill_workspace_size()   */
