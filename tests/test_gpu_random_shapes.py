@@ -1,6 +1,9 @@
 """GPU parity on seeded random shapes: head dims, head sharing, dtypes, ragged lengths
-(including empty sequences), with and without a start table, against the float64 oracle.
-The shapes are drawn once from a fixed seed, so every run checks the same cases.
+(including empty sequences), with and without a start table, against the float64 oracle;
+and, for the chunked kernel, random gate regimes (decay strength, runs of a = 1 and b = 1)
+and update rules over sequences of up to a few thousand tokens, which also exercises the
+split-sequence path.  The cases are drawn once from fixed seeds, so every run checks the
+same ones.
 """
 import sys
 
@@ -66,3 +69,45 @@ def test_random_decode(case):
     torch.cuda.synchronize()
     o_ref, S_ref = oracle.run_inputs(inp)
     assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), dtype, f"random decode {i}")
+
+
+_GATED = {"gated_delta": True, "delta": False, "gated_linear": True, "linear": False}
+_DELTA = {"gated_delta": True, "delta": True, "gated_linear": False, "linear": False}
+
+
+def _regime_cases(n=12, seed=2027):
+    """bf16, dk = 128 (the chunked kernel), lengths up to a few thousand tokens (few sequences
+    and heads, so the split-sequence path runs too), random gate regimes and update rules."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        N = int(rng.integers(1, 4))
+        lens = [int(x) for x in rng.choice([0, 1, 63, 64, 65, 200, 513, 1500, 2500, 4100], size=N)]
+        HQK = int(rng.choice([1, 2]))
+        HV = HQK * int(rng.choice([1, 2, 3]))
+        dv = int(rng.choice([64, 128]))
+        g_mu, g_sd = float(rng.choice([0.5, 2.0, 3.0, 6.0])), float(rng.choice([0.5, 1.5]))
+        p_g0, p_beta1 = float(rng.choice([0.0, 0.1, 0.5])), float(rng.choice([0.0, 0.1, 0.5]))
+        variant = str(rng.choice(["gated_delta", "gated_delta", "delta", "gated_linear", "linear"]))
+        s0 = bool(rng.random() < 0.6)
+        out.append((i, lens, HQK, HV, dv, g_mu, g_sd, p_g0, p_beta1, variant, s0))
+    return out
+
+
+@pytest.mark.parametrize("case", _regime_cases(), ids=lambda c: f"regime{c[0]}")
+def test_random_prefill_regimes(case):
+    i, lens, HQK, HV, dv, g_mu, g_sd, p_g0, p_beta1, variant, s0 = case
+    print(f"regime case {i}: lens={lens} HQK={HQK} HV={HV} dv={dv} g~N({g_mu},{g_sd}) p_g0={p_g0} "
+          f"p_beta1={p_beta1} {variant} s0={s0}", flush=True)
+    inp = W.make_inputs("regime", 700 + i, lens, HQK, HV, 128, dv, "bf16", g_mu, g_sd,
+                        0.05 if s0 else None, p_g0=p_g0, p_beta1=p_beta1)
+    d = to_device(inp)
+    g = d["g"] if _GATED[variant] else None
+    o, S = binding.prefill(d["q"], d["k"], d["v"], g, d["beta"], cu_seqlens=d["cu"],
+                           cu_seqlens_host=inp.cu_seqlens, S0=d["S0"], variant=variant)
+    torch.cuda.synchronize()
+    g_ref = inp.as_f64("g") if _GATED[variant] else np.zeros_like(inp.g, dtype=np.float64)
+    o_ref, S_ref = oracle.run(inp.as_f64("q"), inp.as_f64("k"), inp.as_f64("v"), g_ref, inp.as_f64("beta"),
+                              inp.cu_seqlens, inp.as_f64("S0"), delta=_DELTA[variant])
+    assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), "bf16", f"regime case {i}",
+                  grows=not _DELTA[variant])
