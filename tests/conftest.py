@@ -29,4 +29,6 @@ def pytest_terminal_summary(terminalreporter):
     for key in sorted(PARITY_LOG):
         r = PARITY_LOG[key]
         fo, fs = tolerances(r["dtype"])
-        tr.write_line(f"{key[-78:]:78s} {r['dtype']:5s} {r['units']:5d} {r['o']:11.2e} {fo:7.0e} {r['s']:9.2e} {fs:7.0e}")
+        eo = "n/a" if r["o"] is None else f"{r['o']:.2e}"
+        es = "n/a" if r["s"] is None else f"{r['s']:.2e}"
+        tr.write_line(f"{key[-78:]:78s} {r['dtype']:5s} {r['units']:5d} {eo:>11s} {fo:7.0e} {es:>9s} {fs:7.0e}")
