@@ -70,7 +70,12 @@ typedef enum {
 
 typedef enum {
     GDN_BF16 = 0, /* q, k, v, o are bfloat16; o is rounded to nearest even */
-    GDN_F32 = 1   /* q, k, v, o are float32                                */
+    GDN_F32 = 1,  /* q, k, v, o are float32                                */
+    /* Range sentinels, never valid arguments: they make every int32 value a value of the
+     * type in C++ as well, so an out-of-range argument from C is a defined value that the
+     * library rejects with GDN_ERR_DTYPE. */
+    GDN_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+    GDN_DTYPE_RANGE_MAX_ = 2147483647
 } gdn_dtype;
 
 /*
@@ -93,7 +98,10 @@ typedef enum {
     GDN_GATED_DELTA = 0,
     GDN_DELTA = 1,
     GDN_GATED_LINEAR = 2,
-    GDN_LINEAR = 3
+    GDN_LINEAR = 3,
+    /* range sentinels, never valid arguments (as for gdn_dtype): GDN_ERR_UNSUPPORTED */
+    GDN_VARIANT_RANGE_MIN_ = -2147483647 - 1,
+    GDN_VARIANT_RANGE_MAX_ = 2147483647
 } gdn_variant;
 
 /*
