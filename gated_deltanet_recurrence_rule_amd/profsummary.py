@@ -58,7 +58,40 @@ CMD_PMC = ("timeout -s KILL 180 rocprofv3 --pmc {ctr} --output-format csv -d {d}
            "python3 bench.py --steps 2 --warmup 1 --settle-ms 0 --no-cpu-baseline --copy-probe")
 CMD_MFMA = ("timeout -s KILL 180 rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 --output-format csv -d {d} -o bench -- "
             "python3 bench.py --steps 2 --warmup 1 --settle-ms 0 --no-cpu-baseline --no-block")
-CMD_SUM = "python3 -m gated_deltanet_recurrence_rule_amd.profsummary {kt} {fetch} {write}{mfma} --out profiles"
+CMD_SUM = "python3 -m gated_deltanet_recurrence_rule_amd.profsummary {kt} {fetch} {write}{mfma}{sq} --out profiles"
+CMD_SQ = ("timeout -s KILL 120 rocprofv3 --pmc {ctrs} --output-format csv -d {d} -o bench -- "
+          "python3 bench.py --steps 2 --warmup 1 --settle-ms 0 --no-cpu-baseline --no-block")
+# SQ counters that count in quad-cycles (4 clocks), per rocprofv3's counter descriptions
+SQ_QUAD = {"SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_MISC",
+           "SQ_INST_CYCLES_SALU", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY"}
+SQ_FILE = "prefill_chunked_counters_4x16384.txt"
+
+
+def sq_summary(dirs, frag: str, n_waves: int, n_chunks: int, sum_cmd: str) -> list:
+    """Lines of the SQ-counter record of one kernel: for every counter of the given passes
+    (one rocprofv3 --pmc run each), the mean over that kernel's dispatches, and per wave per
+    chunk."""
+    lines, table = [], []
+    for d in dirs:
+        with open(_one(d, "counter_collection.csv")) as f:
+            rows = [r for r in csv.DictReader(f) if frag in r["Kernel_Name"]]
+        names = list(dict.fromkeys(r["Counter_Name"] for r in rows))
+        lines.append("  " + CMD_SQ.format(ctrs=" ".join(names), d=d))
+        for n in names:
+            v = [float(r["Counter_Value"]) for r in rows if r["Counter_Name"] == n]
+            table.append((n, sum(v) / len(v), len(v)))
+    out = [f"Kernel: {frag} ({n_waves} waves, {n_chunks} chunks of 64 tokens each).",
+           "MI355X (gfx950), one GPU.  Per-dispatch SQ counters (summed over the shader engines by rocprofv3),",
+           f"averaged over the kernel's dispatches in each pass and divided by {n_waves} waves x {n_chunks} chunks.",
+           "Counters marked (q) count quad-cycles (4 clocks).",
+           "Commands (run from the repository root on the GPU host; one pass per line):", *lines,
+           f"  this summary: {sum_cmd}", "",
+           f"{'counter':34s} {'per dispatch':>16s} {'per wave per chunk':>20s}  dispatches"]
+    for n, mean, cnt in table:
+        per = mean / (n_waves * n_chunks)
+        clocks = f"   = {4 * per:.0f} clocks" if n in SQ_QUAD else ""
+        out.append(f"{n + (' (q)' if n in SQ_QUAD else ''):34s} {mean:16.0f} {per:20.1f}  {cnt}{clocks}")
+    return out
 
 
 def _one(d: str, suffix: str) -> str:
@@ -105,6 +138,8 @@ def main(argv=None):
     ap.add_argument("fetch")
     ap.add_argument("write")
     ap.add_argument("--mfma", default=None, help="directory of the MfmaUtil / MfmaFlopsBF16 run")
+    ap.add_argument("--sq", nargs="+", default=None,
+                    help="directories of SQ counter passes of the prefill kernel (writes " + SQ_FILE + ")")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     args = ap.parse_args(argv)
 
@@ -125,7 +160,8 @@ def main(argv=None):
     cmds = [CMD_KT.format(kt=args.kt), CMD_PMC.format(ctr="FETCH_SIZE", d=args.fetch),
             CMD_PMC.format(ctr="WRITE_SIZE", d=args.write),
             CMD_SUM.format(kt=args.kt, fetch=args.fetch, write=args.write,
-                           mfma=f" --mfma {args.mfma}" if args.mfma else "")]
+                           mfma=f" --mfma {args.mfma}" if args.mfma else "",
+                           sq=(" --sq " + " ".join(args.sq)) if args.sq else "")]
     mfma_lines = {}
     if args.mfma:
         frag = KERNELS["prefill_chunked"][0]
@@ -190,6 +226,13 @@ def main(argv=None):
         print("\n".join(lines))
     with open(os.path.join(args.out, "traffic.json"), "w") as f:
         json.dump(traffic, f, indent=1)
+    if args.sq:
+        # the 4 x 16384 workload: 256 workgroups of 8 waves, 256 chunks each
+        sq = sq_summary(args.sq, KERNELS["prefill_chunked"][0], 256 * 8, 16384 // 64, cmds[3])
+        sq = [f"Workload: {KERNELS['prefill_chunked'][3]}.", *sq]
+        with open(os.path.join(args.out, SQ_FILE), "w") as f:
+            f.write("\n".join(sq) + "\n")
+        print("\n".join(sq))
     return 0
 
 
