@@ -111,3 +111,28 @@ def test_random_prefill_regimes(case):
                               inp.cu_seqlens, inp.as_f64("S0"), delta=_DELTA[variant])
     assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), "bf16", f"regime case {i}",
                   grows=not _DELTA[variant])
+
+
+# The hardest gate regimes found by a random sweep: most tokens with a = 1 (g = 0) and b = 1,
+# where the table keeps every write and the triangular solve is least damped.  Pinned here so
+# that a precision change in the chunked kernel cannot erode them unnoticed.
+_EXTREME = [
+    ("delta", [700], 4.0, 0.5, 31),
+    ("gated_delta", [2000, 4100], 4.0, 1.5, 32),
+]
+
+
+@pytest.mark.parametrize("case", _EXTREME, ids=lambda c: f"{c[0]}-{'+'.join(map(str, c[1]))}")
+def test_prefill_extreme_gate_runs(case):
+    variant, lens, g_mu, g_sd, seed = case
+    print(f"extreme gate runs: {variant} lens={lens} g~N({g_mu},{g_sd}) p_g0=0.9 p_beta1=0.9", flush=True)
+    inp = W.make_inputs("extreme", seed, lens, 2, 2, 128, 128, "bf16", g_mu, g_sd, 0.05, p_g0=0.9, p_beta1=0.9)
+    d = to_device(inp)
+    g = d["g"] if _GATED[variant] else None
+    o, S = binding.prefill(d["q"], d["k"], d["v"], g, d["beta"], cu_seqlens=d["cu"],
+                           cu_seqlens_host=inp.cu_seqlens, S0=d["S0"], variant=variant)
+    torch.cuda.synchronize()
+    g_ref = inp.as_f64("g") if _GATED[variant] else np.zeros_like(inp.g, dtype=np.float64)
+    o_ref, S_ref = oracle.run(inp.as_f64("q"), inp.as_f64("k"), inp.as_f64("v"), g_ref, inp.as_f64("beta"),
+                              inp.cu_seqlens, inp.as_f64("S0"), delta=_DELTA[variant])
+    assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), "bf16", f"extreme {variant} {lens}")
