@@ -49,8 +49,11 @@
 //    and T_0, T_1 into LDS already in that MFMA operand order (computing a Gram
 //    tile with the two operand roles swapped yields it transposed, which is the
 //    operand order directly).
-// Three workgroup barriers per chunk: load | Grams + (K S, Q S, Z) | solve + state.
-// The next chunk's q, k, v, g, beta are fetched into registers one chunk ahead.
+// Two workgroup barriers per chunk, a two-stage pipeline: in phase a of chunk c the
+// column waves form K S, Q S and Z while the Gram waves stage chunk c + 1 into LDS; in
+// phase b the column waves solve, write the reads and update the table while the Gram
+// waves build chunk c + 1's operands.  The next chunk's q, k, v, g, beta are fetched into
+// registers one chunk ahead.
 #include "common.hpp"
 #include "kernels.hpp"
 
