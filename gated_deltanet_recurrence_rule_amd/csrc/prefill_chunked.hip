@@ -26,15 +26,12 @@
 // applied for s = 1, 2, 4, 8 inside a 16-block (all factors stay as small as T itself);
 // the last step, s = 16, merges the two 16-blocks of a 32-block through W = A_10 T_00.
 //
-// Precision.  MFMA operands are bf16 unless noted; a value that is not exactly bf16 is
-// either rounded once or carried as hi + lo (hi = bf16(x), lo = bf16(x - hi); two or
-// three MFMAs).  Raw q, k, v rows are exact bf16.  The table path is carried hi + lo: S
-// in K S, T_b, A_10 and Z / Delta in the solve, the scaled Delta in K^T D.  The output
-// path rounds once: S in Q S, P and Delta in P Delta.  The 16-block inverses and their
-// merge (T - T A_s T, W, T_10) are formed on fp16 MFMA with each factor rounded once to
-// fp16: every factor is bounded (|A_ij| <= b_i |k_i . k_j| <= 1 for b in [0, 1], and
-// the inverses of these blocks stay of order one), and 11 significant bits keep T within
-// ~6e-4 of the exact inverse.  All accumulation is fp32.
+// Precision.  MFMA operands are bf16; a value that is not exactly bf16 is either
+// rounded once or carried as hi + lo (hi = bf16(x), lo = bf16(x - hi); two or
+// three MFMAs).  Raw q, k, v rows are exact bf16.  The table path is carried
+// hi + lo: S in K S, T_b, A_10 and Z / Delta in the solve, the scaled Delta in
+// K^T D.  The output path rounds once: S in Q S, P and Delta in P Delta.  All
+// accumulation is fp32.
 //
 // Mapping.  One workgroup of 8 waves owns one (sequence, V head, 64-column
 // slice of dv) and walks its chunks in order; dv columns of S evolve
@@ -65,7 +62,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int C = 64;       // chunk length
 constexpr int DK = 128;     // key dimension
@@ -97,16 +93,11 @@ static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-// Y^T X of two 16 x 16 tiles held in accumulator form (element e at lane (g, j) is M[4 g + e][j]),
-// on the K = 16 fp16 MFMA: lane group g and element e enumerate the contracted index on both
-// sides, so both tiles go in as they are, rounded once to fp16.
-__device__ __forceinline__ f32x4 tprod16(f32x4 y, f32x4 x) {
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_convertvector(y, f16x4), __builtin_convertvector(x, f16x4),
-                                                 zero, 0, 0, 0);
-}
 __device__ __forceinline__ bf16x8 to_bf16(f32x8 x) { return __builtin_convertvector(x, bf16x8); }
 __device__ __forceinline__ f32x8 cat(f32x4 a, f32x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 // bf16 pair dot product a.x b.x + a.y b.y + c in one instruction (products are exact in fp32)
@@ -134,6 +125,18 @@ __device__ __forceinline__ void split(f32x8 x, bf16x8 &hi, bf16x8 &lo) {
         r[2 * p + 1] = dot2(hp[p], m1, x[2 * p + 1]);
     }
     lo = to_bf16(r);
+}
+__device__ __forceinline__ void split4(f32x4 x, bf16x4 &hi, bf16x4 &lo) {
+    hi = __builtin_convertvector(x, bf16x4);
+    const bf16x2 m0 = pair_const(0x0000bf80u), m1 = pair_const(0xbf800000u);
+    const bf16x2 hp[2] = {__builtin_shufflevector(hi, hi, 0, 1), __builtin_shufflevector(hi, hi, 2, 3)};
+    f32x4 r;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        r[2 * p] = dot2(hp[p], m0, x[2 * p]);
+        r[2 * p + 1] = dot2(hp[p], m1, x[2 * p + 1]);
+    }
+    lo = __builtin_convertvector(r, bf16x4);
 }
 // hi*hi + hi*lo + lo*hi
 __device__ __forceinline__ f32x4 mfma32_x3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, f32x4 c) {
@@ -700,8 +703,8 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     //
     // Gram wave gw owns diagonal 16-block gw.  Its matrices live in MFMA accumulator form:
     // element e at lane (g = lane/16, j = lane%16) is M[4 g + e][j].  With Y and X in that
-    // form, Y^T X needs no data movement (tprod16), so every product below keeps a matrix
-    // and its transpose.
+    // form, Y^T X needs no data movement (lane group g and element e enumerate the contracted
+    // index on both sides), so every product below keeps a matrix and its transpose.
     // Waves 0 and 2 also form W = A_10 T_00 of their 32-block and hand it to waves 1 and 3,
     // which finish the block.  The hand-over counter holds the last chunk whose W is in LDS.
     int *flag = reinterpret_cast<int *>(lds + OFF_FLAG);
@@ -784,6 +787,16 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             opA[(rt * 2 + 0) * 64 + ln] = hi;
             opA[(rt * 2 + 1) * 64 + ln] = lo;
         };
+        // Products on bf16 MFMA with hi/lo operands.  Y and X in accumulator form split into
+        // bf16 (hi, lo); one 16x16x32 MFMA with A = (Yh, Yh) and B = (Xh, Xl) gives
+        // Yh^T Xh + Yh^T Xl, a second with A = (Yl, 0) adds Yl^T Xh.
+        auto hl = [&](const f32x4 &x, bf16x4 &h, bf16x4 &l) { split4(x, h, l); };
+        auto prod3 = [&](const bf16x4 &yh, const bf16x4 &yl, const bf16x4 &xh, const bf16x4 &xl, f32x4 acc) {
+            const bf16x4 z4 = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+            const bf16x8 bx = cat(xh, xl);
+            acc = mfma32(cat(yh, yh), bx, acc);
+            return mfma32(cat(yl, z4), bx, acc);
+        };
         // Inverse T of the diagonal 16-block and its transpose, as accumulator tiles.
         auto invert_block = [&](f32x4 &T, f32x4 &Tt, bf16x8 *kd) {
             load_blk(sK, blk, kd);
@@ -818,10 +831,14 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                     const int x = (4 * lqq + e) ^ lrr;
                     Ao[e] = (x >= sl && x < 2 * sl) ? Am[e] : 0.f;
                 }
-                const f32x4 Ut = tprod16(Ao, Tt);      // (T A_s)^T
-                const f32x4 T_old = T;
-                T = T - tprod16(Ut, T_old);            // T - (T A_s) T
-                Tt = Tt - tprod16(T_old, Ut);          // its transpose
+                bf16x4 aoh, aol, tth, ttl, th, tl, uh, ul;
+                hl(Ao, aoh, aol);
+                hl(Tt, tth, ttl);
+                hl(T, th, tl);
+                const f32x4 Ut = prod3(aoh, aol, tth, ttl, zero);  // (T A_s)^T
+                hl(Ut, uh, ul);
+                T = T - prod3(uh, ul, th, tl, zero);    // T - (T A_s) T
+                Tt = Tt - prod3(th, tl, uh, ul, zero);  // its transpose
             }
         };
         // Row tile rt of T_b as a tile-order (hi, lo) operand: 8 values at lane (g, i) are
@@ -865,7 +882,10 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                 f32x4 At;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) At[e] = cr * (R4[e] * CF4[e]) * gx[e];
-                Wbuf[b * 64 + ln] = tprod16(At, T);
+                bf16x4 ah, al, th, tl;
+                hl(At, ah, al);
+                hl(T, th, tl);
+                Wbuf[b * 64 + ln] = prod3(ah, al, th, tl, zero);
                 __hip_atomic_store(flag + b, c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
             __builtin_amdgcn_s_setprio(0);
@@ -896,7 +916,10 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             }
             const f32x4 W = Wbuf[b * 64 + ln];
             // T_10^T = -(T_11 W)^T = -W^T T_11^T
-            const f32x4 T10t = -tprod16(W, Tt);
+            bf16x4 wh, wl, th, tl;
+            hl(W, wh, wl);
+            hl(Tt, th, tl);
+            const f32x4 T10t = -prod3(wh, wl, th, tl, zero);
             put_t(1, T10t, Tt);
             __builtin_amdgcn_s_setprio(0);
         }

@@ -252,3 +252,29 @@ def test_device_seqlens_out_of_range_are_clamped(dtype, d):
     for a, b in zip(r1, r2):
         assert torch.equal(a, b)
     assert torch.equal(so1, so2)
+
+
+@pytest.mark.parametrize("structure", ["identical", "alternating", "near_parallel"])
+def test_prefill_structured_keys(structure):
+    """Keys that stress the chunk's triangular solve, every write at full strength (b = 1):
+    one key repeated by every token with no decay (each write overwrites the last), a key and
+    its negation alternating, and keys within a few degrees of one common direction."""
+    _say(f"prefill structured keys: {structure}")
+    inp = W.random_small(61, [200, 130], 1, 2, 128, 128)
+    rng = np.random.default_rng(62)
+    T = inp.total_T
+    u = rng.standard_normal(128)
+    u /= np.linalg.norm(u)
+    if structure == "identical":
+        keys = np.tile(u, (T, 1))
+        inp.g[:] = 0.0
+    elif structure == "alternating":
+        keys = np.outer((-1.0) ** np.arange(T), u)
+    else:
+        keys = u + 0.05 * rng.standard_normal((T, 128)) / np.sqrt(128)
+        keys /= np.linalg.norm(keys, axis=1, keepdims=True)
+    inp.k[:, 0, :] = W.f32_to_bf16_bits(keys.astype(np.float32))
+    inp.beta[:] = 1.0
+    _, o, S = _prefill(inp)
+    o_ref, S_ref = oracle.run_inputs(inp)
+    assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), "bf16", f"keys {structure}")
