@@ -98,3 +98,55 @@ def test_prefill_graph_replays():
         assert torch.equal(ST_static, S_e), f"replay {i}: tables differ from the eager call"
         # some eager work of the program between replays
         _ = (o_e.float() * 2).sum().item()
+
+
+def test_block_parts_graph_replays():
+    """The causal convolution + SiLU (carried state in and out) and the gated RMS norm of its v
+    channels, captured together."""
+    _say("graph: conv + SiLU and gated norm, 3 replays")
+    HQK, HV, d = 2, 4, 64
+    lens = [40, 3, 90]
+    T = sum(lens)
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda")
+        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+    blocks = [W.block_inputs(120 + i, lens, HQK, HV, d, d) for i in range(3)]
+    devs = [dict(x=up(b.x), w=up(b.conv_w), st=up(b.conv_state), z=up(b.z), nw=up(b.norm_w),
+                 cu=up(b.cu_seqlens)) for b in blocks]
+    static = {k: v.clone() for k, v in devs[0].items()}
+    q = torch.empty((T, HQK, d), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty_like(q)
+    v = torch.empty((T, HV, d), dtype=torch.bfloat16, device="cuda")
+    st_out = torch.empty_like(static["st"])
+    y = torch.empty_like(v)
+
+    def call():
+        binding.conv_silu(static["x"], static["w"], HQK=HQK, HV=HV, dk=d, dv=d, cu_seqlens=static["cu"],
+                          state_in=static["st"], state_out=st_out, q=q, k=k, v=v)
+        binding.gated_rmsnorm(v, static["z"], static["nw"], 1e-6, y=y)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for i, dv_ in enumerate(devs):
+        for key in ("x", "w", "st", "z", "nw"):
+            static[key].copy_(dv_[key])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        st_e = torch.empty_like(dv_["st"])
+        qe, ke, ve = binding.conv_silu(dv_["x"], dv_["w"], HQK=HQK, HV=HV, dk=d, dv=d, cu_seqlens=dv_["cu"],
+                                       state_in=dv_["st"], state_out=st_e)
+        ye = binding.gated_rmsnorm(ve, dv_["z"], dv_["nw"], 1e-6)
+        torch.cuda.synchronize()
+        for got, want, what in ((q, qe, "q"), (k, ke, "k"), (v, ve, "v"), (st_out, st_e, "state"), (y, ye, "norm")):
+            assert torch.equal(got, want), f"replay {i}: {what} differs from the eager call"
+        _ = (ye.float() * 2).sum().item()
