@@ -278,3 +278,45 @@ def test_prefill_structured_keys(structure):
     _, o, S = _prefill(inp)
     o_ref, S_ref = oracle.run_inputs(inp)
     assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), "bf16", f"keys {structure}")
+
+
+def test_nan_propagates_and_stays_in_its_unit():
+    """A NaN in one element of v (sequence 0, V head 1, column 5, token 100) propagates, as the
+    interface states, and stays in its (sequence, V head) unit: every other unit, and the
+    unit's chunks before the one holding that token, match a clean run bit for bit.  (Inside
+    the chunk the triangular products multiply their structural zeros by the NaN, so earlier
+    tokens of that chunk may read NaN too; no data value steers control flow.)"""
+    _say("prefill: NaN in one element of v")
+    inp = W.random_small(71, [150, 90], 2, 4, 128, 128)
+    _, o_c, S_c = _prefill(inp)
+    inp.v[100, 1, 5] = 0x7FC0  # bf16 quiet NaN
+    _, o_n, S_n = _prefill(inp)
+    o_c, o_n, S_c, S_n = o_c.float().cpu(), o_n.float().cpu(), S_c.cpu(), S_n.cpu()
+    others = [h for h in range(4) if h != 1]
+    assert torch.equal(o_n[:150, others], o_c[:150, others]) and torch.equal(o_n[150:], o_c[150:])
+    assert torch.equal(S_n[0, others], S_c[0, others]) and torch.equal(S_n[1], S_c[1])
+    assert torch.equal(o_n[:64, 1], o_c[:64, 1]), "chunks before the NaN's changed"
+    assert torch.isnan(o_n[100, 1, 5]) and torch.isnan(S_n[0, 1, :, 5]).any()
+
+
+def test_decode_nan_stays_in_its_table_column():
+    """Decode: a NaN in v of one sequence and V head reaches that head's read and that column of
+    its table only."""
+    _say("decode: NaN in one element of v")
+    inp = W.decode(seed=72, N=8)
+    d = to_device(inp)
+    S_c = d["S0"].clone()
+    o_c = binding.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], S_c)
+    v_bad = d["v"].clone()
+    v_bad[3, 7, 9] = float("nan")
+    S_n = d["S0"].clone()
+    o_n = binding.decode_step(d["q"], d["k"], v_bad, d["g"], d["beta"], S_n)
+    torch.cuda.synchronize()
+    mask = torch.ones(8, dtype=torch.bool)
+    mask[3] = False
+    assert torch.equal(o_n[mask], o_c[mask]) and torch.equal(S_n[mask], S_c[mask])
+    heads = [h for h in range(inp.HV) if h != 7]
+    assert torch.equal(o_n[3, heads], o_c[3, heads]) and torch.equal(S_n[3, heads], S_c[3, heads])
+    cols = [c for c in range(128) if c != 9]
+    assert torch.equal(S_n[3, 7][:, cols], S_c[3, 7][:, cols])
+    assert torch.isnan(o_n[3, 7, 9]) and torch.isnan(S_n[3, 7, :, 9]).all()
