@@ -84,7 +84,7 @@ def sq_summary(dirs, frag: str, n_waves: int, n_chunks: int, sum_cmd: str) -> li
            "MI355X (gfx950), one GPU.  Per-dispatch SQ counters (summed over the shader engines by rocprofv3),",
            f"averaged over the kernel's dispatches in each pass and divided by {n_waves} waves x {n_chunks} chunks.",
            "Counters marked (q) count quad-cycles (4 clocks).",
-           "Commands (run from the repository root on the GPU host; one pass per line):", *lines,
+           "Commands (run from the repository root on a machine with an MI355X; one pass per line):", *lines,
            f"  this summary: {sum_cmd}", "",
            f"{'counter':34s} {'per dispatch':>16s} {'per wave per chunk':>20s}  dispatches"]
     for n, mean, cnt in table:
@@ -202,7 +202,7 @@ def main(argv=None):
         lines = [
             f"Workload: {workload}.",
             f"Algorithmic HBM bytes per call: {alg[key]:,} (every input read once, every output written once).",
-            "MI355X (gfx950), one GPU.  Commands (run from the repository root on the GPU host):",
+            "MI355X (gfx950), one GPU.  Commands (run from the repository root on a machine with an MI355X):",
             f"  kernel times:  {cmds[0]}",
             f"  HBM fetch:     {cmds[1]}",
             f"  HBM write:     {cmds[2]}",
