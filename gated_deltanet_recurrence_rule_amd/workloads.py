@@ -155,6 +155,30 @@ def _unit_rows(rng: np.random.Generator, shape) -> np.ndarray:
     return x
 
 
+@dataclasses.dataclass(frozen=True)
+class NormSpread:
+    """How q and k rows are scaled after being drawn unit-norm: each (token, head) row gets
+    a norm log-uniform in [lo, hi]; a fraction p_zero of the rows is set to zero, and a
+    fraction p_tiny is given the norm `tiny` (below the library's 1e-12 floor)."""
+    lo: float = 1e-2
+    hi: float = 1e2
+    p_zero: float = 0.05
+    p_tiny: float = 0.02
+    tiny: float = 1e-13
+
+
+def _spread_rows(rng: np.random.Generator, shape, spread: NormSpread) -> np.ndarray:
+    """Unit rows (see _unit_rows) times random per-row norms drawn as `spread` says."""
+    x = _unit_rows(rng, shape)
+    rows = int(np.prod(shape[:-1], dtype=np.int64))
+    norm = np.exp(rng.uniform(math.log(spread.lo), math.log(spread.hi), size=rows)).astype(np.float32)
+    u = rng.random(rows)
+    norm[u < spread.p_zero] = 0.0
+    norm[(u >= spread.p_zero) & (u < spread.p_zero + spread.p_tiny)] = np.float32(spread.tiny)
+    x.reshape(rows, shape[-1])[:] *= norm[:, None]
+    return x
+
+
 def _log_sigmoid(x: np.ndarray) -> np.ndarray:
     # log(sigmoid(x)) = -log1p(exp(-x)), written to stay finite for any x
     x = x.astype(np.float64)
@@ -171,8 +195,12 @@ def _pack(x: np.ndarray, dtype: str) -> np.ndarray:
 
 def make_inputs(name: str, seed: int, seqlens, HQK: int, HV: int, dk: int, dv: int, dtype: str,
                 g_mu: float, g_sd: float, s0_sd: Optional[float], p_g0: float = 0.0,
-                p_beta1: float = 0.0, scale: float = 1.0) -> Inputs:
-    """Draw one packed batch with the shared recipe (see the module docstring)."""
+                p_beta1: float = 0.0, scale: float = 1.0,
+                qk_spread: Optional[NormSpread] = None) -> Inputs:
+    """Draw one packed batch with the shared recipe (see the module docstring).
+
+    qk_spread: None keeps q and k unit-norm (the workloads' statement); a NormSpread
+    scales their rows instead, for tests of the library's own normalisation."""
     seqlens = np.asarray(seqlens, dtype=np.int64)
     cu = np.zeros(len(seqlens) + 1, dtype=np.int64)
     np.cumsum(seqlens, out=cu[1:])
@@ -180,8 +208,9 @@ def make_inputs(name: str, seed: int, seqlens, HQK: int, HV: int, dk: int, dv: i
         raise ValueError("total length exceeds int32 cu_seqlens")
     T = int(cu[-1])
     io = np.uint16 if dtype == BF16 else np.float32
-    q = _fill_blocks(seed, 0, (T, HQK, dk), io, lambda r, s: _pack(_unit_rows(r, s), dtype))
-    k = _fill_blocks(seed, 1, (T, HQK, dk), io, lambda r, s: _pack(_unit_rows(r, s), dtype))
+    rows = _unit_rows if qk_spread is None else (lambda r, s: _spread_rows(r, s, qk_spread))
+    q = _fill_blocks(seed, 0, (T, HQK, dk), io, lambda r, s: _pack(rows(r, s), dtype))
+    k = _fill_blocks(seed, 1, (T, HQK, dk), io, lambda r, s: _pack(rows(r, s), dtype))
     v = _fill_blocks(seed, 2, (T, HV, dv), io,
                      lambda r, s: _pack(r.standard_normal(s, dtype=np.float32), dtype))
     g = _fill_blocks(seed, 3, (T, HV), np.float32,
@@ -241,10 +270,12 @@ def varlen(seed: int = 5, n: int = 64, lo: int = 128, hi: int = 32768, tail: int
 
 def random_small(seed: int, seqlens, HQK: int, HV: int, dk: int, dv: int, dtype: str = BF16,
                  s0: bool = True, g_mu: float = 2.0, g_sd: float = 1.5, p_g0: float = 0.0,
-                 p_beta1: float = 0.0) -> Inputs:
+                 p_beta1: float = 0.0, qk_spread: Optional[NormSpread] = None,
+                 scale: float = 1.0) -> Inputs:
     """Small random batch for parity tests (any lengths, including zero)."""
     return make_inputs("random", seed, seqlens, HQK, HV, dk, dv, dtype, g_mu, g_sd,
-                       0.05 if s0 else None, p_g0=p_g0, p_beta1=p_beta1)
+                       0.05 if s0 else None, p_g0=p_g0, p_beta1=p_beta1, qk_spread=qk_spread,
+                       scale=scale)
 
 
 # ---------------------------------------------------------------- the block around the scan

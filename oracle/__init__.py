@@ -11,8 +11,9 @@ Three statements of the method live here, all float64:
 
 * ``run`` -- the C token loop in ``gdn_oracle.c`` (OpenMP over independent
   (sequence, V head) units).  This is THE oracle.
-* ``delta_rule_np`` -- a short numpy twin of the same token loop, used to catch
-  mistakes in the C code.
+* ``delta_rule_np`` -- the same rule stated a second way, in [LLV]'s transposed
+  form (the table multiplied by alpha (I - beta k k^T) each token), used to
+  catch mistakes in the C code.
 * ``chunked_np`` -- the chunk-parallel rewriting of the same recurrence, used
   only to pin the algebra that the GPU prefill implements (the handbook page
   says that real implementations split the sequence into chunks and are
@@ -136,24 +137,40 @@ def _unit(x, normalize):
 def delta_rule_np(q, k, v, g, beta, S0=None, *, scale=1.0, delta=True, normalize=True):
     """One sequence, numpy float64: q, k [T, HQK, dk]; v [T, HV, dv]; g, beta [T, HV].
 
-    The four steps of [HB7]'s figure "one step of the delta rule" on every head at
-    once; V head h reads QK head h // (HV // HQK) ([HB7] qwen/deltanet.py,
-    repeat_interleave).  Returns (o [T, HV, dv], S [HV, dk, dv]).
+    A second, independent statement of the rule, checked against the C token loop: the
+    transposed form that [LLV] gives in its update-rule table (Gated DeltaNet row), where
+    the table is M = S^T [dv, dk] and every token multiplies it on the right by the matrix
+    alpha (I - beta k k^T) -- a decay together with a projection away from k -- before
+    adding the new association beta v k^T:
+
+        M_t = M_{t-1} (alpha_t (I - beta_t k_t k_t^T)) + beta_t v_t k_t^T,   o_t = M_t q_t.
+
+    Without the look-up (delta=False) the projection drops out: M_t = alpha_t M_{t-1} +
+    beta_t v_t k_t^T.  V head h reads QK head h // (HV // HQK).  Each head runs its own
+    explicit loop over tokens.  Returns (o [T, HV, dv], S [HV, dk, dv]) in [HB7]'s
+    orientation (S = M^T).
     """
     q, k, v, g, beta = (np.asarray(x, dtype=np.float64) for x in (q, k, v, g, beta))
     T, HQK, dk = q.shape
     HV, dv = v.shape[1:]
-    rep = HV // HQK
-    kh = np.repeat(_unit(k, normalize), rep, axis=1)
-    qh = np.repeat(_unit(q, normalize) * scale, rep, axis=1)
-    S = np.zeros((HV, dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    group = HV // HQK
     o = np.zeros((T, HV, dv))
-    for t in range(T):
-        S = S * np.exp(g[t])[:, None, None]                               # 1. decay
-        pred = np.einsum("hk,hkv->hv", kh[t], S) if delta else 0.0        # 2. look up
-        S = S + np.einsum("hk,hv->hkv", kh[t], beta[t][:, None] * (v[t] - pred))  # 3. write
-        o[t] = np.einsum("hk,hkv->hv", qh[t], S)                          # 4. read
-    return o, S
+    S_out = np.zeros((HV, dk, dv))
+    eye = np.eye(dk)
+    for h in range(HV):
+        hq = h // group
+        M = np.zeros((dv, dk)) if S0 is None else np.array(S0[h], dtype=np.float64).T
+        for t in range(T):
+            key = _unit(k[t, hq], normalize)
+            query = scale * _unit(q[t, hq], normalize)
+            alpha = np.exp(g[t, h])
+            if delta:
+                M = M @ (alpha * (eye - beta[t, h] * np.outer(key, key))) + beta[t, h] * np.outer(v[t, h], key)
+            else:
+                M = alpha * M + beta[t, h] * np.outer(v[t, h], key)
+            o[t, h] = M @ query
+        S_out[h] = M.T
+    return o, S_out
 
 
 # --------------------------------------------------------------------------- chunked form

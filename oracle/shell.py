@@ -132,12 +132,28 @@ def gated_rmsnorm_np(o, z, w, eps):
     return w * (o / np.sqrt(ms + eps)) * silu(z)
 
 
-def round_bf16(x):
-    """Round float64 values to the nearest bfloat16 (8 significant bits), ties to even.
+BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127  # largest finite bfloat16
 
-    Normal range only (|x| >= 2^-126); values are returned as float64.
+
+def round_bf16(x):
+    """Round float64 values to the nearest bfloat16, ties to even; returned as float64.
+
+    bfloat16 keeps 8 significant bits over float32's exponent range.  A value x with
+    x = m 2^e, 0.5 <= |m| < 1, lies among bfloat16 numbers spaced 2^(e - 8) apart; below
+    the normal range (e <= -126) the spacing stays at that of the subnormals, 2^-133.  So
+    x rounds to rint(x / s) s with s = 2^(max(e, -125) - 8), rint taking halves to even
+    (the parity of the count of steps is the parity of the last stored bit).  A result
+    beyond the largest finite bfloat16 -- which happens from the midpoint
+    (2 - 2^-8) 2^127 up, ties going to the even neighbour 2^128 -- is an infinity of the
+    same sign.  NaN and infinities pass through.
     """
     x = np.asarray(x, dtype=np.float64)
-    m, e = np.frexp(x)                # x = m * 2^e, 0.5 <= |m| < 1
-    r = np.rint(m * 256.0) / 256.0    # rint rounds halves to even
-    return np.ldexp(r, e)
+    out = np.array(x, dtype=np.float64, copy=True)
+    fin = np.isfinite(x)
+    xf = x[fin]
+    _, e = np.frexp(xf)
+    step = np.ldexp(1.0, np.maximum(e, -125) - 8)
+    r = np.rint(xf / step) * step
+    r = np.where(np.abs(r) > BF16_MAX, np.copysign(np.inf, xf), r)
+    out[fin] = r
+    return out if out.ndim else out[()]

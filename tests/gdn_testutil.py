@@ -101,6 +101,15 @@ def assert_parity(o, S, o_ref, S_ref, v_ref, dtype, what="", grows=False):
         assert err_s <= fs, f"{what}: state relative Frobenius error {err_s:.3e} > {fs:.1e}"
 
 
+def rows_f64(a):
+    """Exact float64 values of raw bf16 bits (uint16) or float32 rows."""
+    from gated_deltanet_recurrence_rule_amd.workloads import bf16_bits_to_f32
+
+    if a.dtype == np.uint16:
+        a = bf16_bits_to_f32(a)
+    return a.astype(np.float64)
+
+
 def oracle_units(inp, seqs, heads):
     """Oracle on a subset of (sequence, V head) units of a batch.
 
@@ -116,9 +125,9 @@ def oracle_units(inp, seqs, heads):
     S0 = inp.S0
     for n in seqs:
         t0, t1 = int(inp.cu_seqlens[n]), int(inp.cu_seqlens[n + 1])
-        q = inp.as_f64_rows("q", t0, t1)[:, qk_idx]
-        k = inp.as_f64_rows("k", t0, t1)[:, qk_idx]
-        v = inp.as_f64_rows("v", t0, t1)[:, heads]
+        q = rows_f64(inp.q[t0:t1][:, qk_idx])
+        k = rows_f64(inp.k[t0:t1][:, qk_idx])
+        v = rows_f64(inp.v[t0:t1][:, heads])
         g = inp.g[t0:t1][:, heads].astype(np.float64)
         b = inp.beta[t0:t1][:, heads].astype(np.float64)
         s0 = None if S0 is None else S0[n][heads].astype(np.float64)[None]

@@ -35,6 +35,22 @@ def test_c_oracle_equals_numpy_twin(seed, lens, HQK, HV, d):
         np.testing.assert_allclose(S[n], S2, atol=1e-13)
 
 
+@pytest.mark.parametrize("delta,normalize,scale", [(False, True, 1.0), (True, False, 1.0), (True, True, 0.25),
+                                                   (False, False, 0.5)])
+def test_c_oracle_equals_numpy_twin_modes(delta, normalize, scale):
+    """The two statements agree without the look-up, without normalisation (q, k rows of any
+    norm, zero rows and rows below the 1e-12 floor included) and with a scale."""
+    spread = W.NormSpread(lo=0.1, hi=3.0, p_zero=0.1, p_tiny=0.05, tiny=1e-13)
+    inp = W.random_small(9, [40, 0, 23], 2, 4, 16, 8, dtype=W.F32, qk_spread=spread)
+    o, S = oracle.run_inputs(inp, delta=delta, normalize=normalize, scale=scale)
+    for n in range(inp.N):
+        t0, t1, f, s0 = _seq(inp, n)
+        o2, S2 = oracle.delta_rule_np(f["q"], f["k"], f["v"], f["g"], f["beta"], s0, scale=scale, delta=delta,
+                                      normalize=normalize)
+        np.testing.assert_allclose(o[t0:t1], o2, atol=1e-12, rtol=1e-12)
+        np.testing.assert_allclose(S[n], S2, atol=1e-12, rtol=1e-12)
+
+
 @pytest.mark.parametrize("C", [1, 4, 16, 64])
 @pytest.mark.parametrize("lens", [[64], [63], [65], [130, 7, 0, 1]])
 def test_chunked_form_equals_token_loop(C, lens):

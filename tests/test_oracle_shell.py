@@ -180,3 +180,37 @@ def test_round_bf16_ties_to_even_and_matches_generator():
     x = (rng.normal(size=4096) * np.exp(rng.uniform(-20, 20, 4096))).astype(np.float32)
     ref = W.bf16_bits_to_f32(W.f32_to_bf16_bits(x)).astype(np.float64)
     np.testing.assert_array_equal(shell.round_bf16(x.astype(np.float64)), ref)
+
+
+def test_round_bf16_subnormals_and_overflow():
+    """bfloat16's subnormals are multiples of 2^-133 below 2^-126, and its largest finite value is
+    (2 - 2^-7) 2^127; rounding to nearest even sends the midpoint above it to infinity."""
+    t = 2.0 ** -133                                                  # smallest subnormal
+    assert shell.round_bf16(2.0 ** -130) == 2.0 ** -130               # 8 steps: exact
+    assert shell.round_bf16(0.5 * t) == 0.0                           # tie between 0 and 1 step -> 0
+    assert shell.round_bf16(1.5 * t) == 2 * t                         # tie between 1 and 2 steps -> 2
+    assert shell.round_bf16(0.75 * t) == t
+    assert shell.round_bf16(-2.5 * t) == -2 * t
+    assert shell.round_bf16(5.3 * t) == 5 * t
+    assert shell.round_bf16((1 - 2.0 ** -9) * 2.0 ** -126) == 2.0 ** -126  # rounds up into the normal range
+    assert shell.round_bf16(2.0 ** -126) == 2.0 ** -126
+    assert shell.round_bf16(1e-300) == 0.0
+    M = (2 - 2.0 ** -7) * 2.0 ** 127
+    assert shell.round_bf16(M) == M
+    assert shell.round_bf16((2 - 2.0 ** -8) * 2.0 ** 127 * (1 - 2.0 ** -40)) == M   # just below the midpoint
+    assert shell.round_bf16((2 - 2.0 ** -8) * 2.0 ** 127) == np.inf                # the midpoint itself
+    assert shell.round_bf16(-1e39) == -np.inf
+    assert shell.round_bf16(np.inf) == np.inf and np.isnan(shell.round_bf16(np.nan))
+    # whole ranges against two independent roundings: the input generator's integer
+    # float32 -> bf16 rounding and torch's float32 -> bfloat16 conversion on the CPU
+    import torch
+    rng = np.random.default_rng(11)
+    sub = (rng.uniform(-1, 1, 4096) * 2.0 ** -126).astype(np.float32)           # float32 subnormals
+    top = (rng.uniform(-1, 1, 4096) * 3.4e38).astype(np.float32)                # near overflow
+    edge = np.array([3.3895e38, 3.3896e38, 3.39e38, 3.4e38, -3.3955e38, 1e-45, -1e-45, 2e-45], np.float32)
+    for x in (sub, top, edge):
+        ref = W.bf16_bits_to_f32(W.f32_to_bf16_bits(x)).astype(np.float64)
+        got = shell.round_bf16(x.astype(np.float64))
+        np.testing.assert_array_equal(got, ref)
+        tref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+        np.testing.assert_array_equal(got, tref)
