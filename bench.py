@@ -93,10 +93,10 @@ def main():
                     help="before the warm-up steps, run steps for at least this long so the GPU "
                          "reaches its sustained clock (untimed; 0 disables)")
     ap.add_argument("--no-block", action="store_true", help="skip the block-parts leg")
-    ap.add_argument("--extra-configs", action="store_true",
-                    help="also time the packed variable-length batch with its 262144-token sequence "
-                         "(adds about a minute; the tiny fp32 scan and the single 8192-token sequence are "
-                         "timed in every run, under extra_configs)")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the packed variable-length batch with its 262144-token sequence (by default "
+                         "it is timed under extra_configs with the tiny fp32 scan and the single "
+                         "8192-token sequence; its inputs take about half a minute to draw)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run one 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -190,7 +190,7 @@ def main():
     if not args.no_block:
         block = block_leg(args, binding, W, P, D, pf, dc, o_p, S_T, o_d, ws, up, dev)
 
-    extra = extra_leg(args, binding, W, up, dev, with_varlen=args.extra_configs)
+    extra = extra_leg(args, binding, W, up, dev, with_varlen=not args.no_varlen)
 
     # A plain 1 GiB device copy: the measured copy bandwidth reported beside the peaks, and
     # (one call, --copy-probe) the known-size dispatch that scales the HBM counters.
@@ -216,15 +216,8 @@ def main():
     pb, pf_chunk, pf_rec = prefill_alg(N, T, pf.HQK, pf.HV, pf.dk, pf.dv, e, True)
     db, dflops, dstate = decode_alg(dc.N, dc.HQK, dc.HV, dc.dk, dc.dv, e)
     kname = binding.prefill_kernel_name(pf.N, pf.total_T, pf.HQK, pf.HV, pf.dk, pf.dv, torch.bfloat16)
-    if "chunk" in kname:
-        pre_roof = {"bound": "mfma", "achieved": pf_chunk / (pre_avg * 1e-3) / 1e12,
-                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
-    else:
-        pre_roof = {"bound": "alu", "achieved": pf_rec / (pre_avg * 1e-3) / 1e12,
-                    "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s"}
-    pre_roof["frac"] = pre_roof["achieved"] / pre_roof["peak"]
+    pre_roof = prefill_roofline(pb, pf_chunk, pf_rec, pre_avg, kname)
     pre_roof["traffic"] = recorded_traffic("prefill_chunked") if "chunk" in kname else None
-    pre_roof["kernel"] = kname
     dec_gbps = db / (dec_avg * 1e-3) / 1e9
     dec_roof = {"bound": "hbm", "achieved": dec_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": dec_gbps / PEAK_HBM_GBPS, "traffic": recorded_traffic("decode"), "kernel": "decode"}
@@ -268,6 +261,7 @@ def main():
                    "prefill_tokens": N * T, "decode_sequences": dc.N, "parallelism": "none"},
         "prefill_ms": pre_avg, "prefill_ms_median": pre_calls[len(pre_calls) // 2],
         "prefill_ms_min": pre_calls[0], "prefill_hbm_frac": pre_hbm_frac,
+        "prefill_mfma_frac": pre_roof.get("mfma_frac"),
         "prefill_roofline_frac": max(pf_chunk / (PEAK_BF16_TFLOPS * 1e12), pb / (PEAK_HBM_GBPS * 1e9)) / (pre_avg * 1e-3),
         "prefill_recurrence_TFLOPs": pf_rec / (pre_avg * 1e-3) / 1e12,
         "decode_us": dec_avg * 1e3, "decode_us_median": dec_calls[len(dec_calls) // 2] * 1e3,
@@ -282,6 +276,29 @@ def main():
         "wall_s_timed": wall,
     }
     print(json.dumps(out), flush=True)
+
+
+def prefill_roofline(alg_bytes, flops_chunk, flops_rec, ms, kname):
+    """Roofline of one prefill call.  Its algorithmic arithmetic intensity (flops_chunk /
+    alg_bytes, ~230 flop/B at d = 128) lies below the bf16 ridge (2500 TFLOP/s / 8 TB/s =
+    312 flop/B), so HBM is the binding roof: `frac` = algorithmic bytes / time / 8 TB/s.  The
+    bf16 MFMA fraction (algorithmic chunk-form flops / time / 2500 TFLOP/s) is reported beside
+    it.  The token-serial kernel (fp32 inputs) is bound by fp32 vector arithmetic instead:
+    its recurrence flops (7 dk dv per token and head) against the fp32 vector peak."""
+    t = ms * 1e-3
+    hbm = alg_bytes / t / 1e9
+    out = {"bound": "hbm", "achieved": hbm, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": hbm / PEAK_HBM_GBPS,
+           "alg_bytes": int(alg_bytes), "kernel": kname}
+    if "chunk" in kname:
+        out["mfma_achieved_TFLOPs"] = flops_chunk / t / 1e12
+        out["mfma_frac"] = flops_chunk / t / 1e12 / PEAK_BF16_TFLOPS
+        out["alg_flops"] = int(flops_chunk)
+    else:
+        alu = flops_rec / t / 1e12
+        out.update({"bound": "alu", "achieved": alu, "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+                    "frac": alu / PEAK_FP32_VALU_TFLOPS, "hbm_frac": hbm / PEAK_HBM_GBPS,
+                    "alg_flops": int(flops_rec)})
+    return out
 
 
 def host_cpu():
@@ -333,11 +350,13 @@ def extra_leg(args, binding, W, up, dev, with_varlen=False):
         lens = np.diff(inp.cu_seqlens)
         ab = sum(prefill_alg(1, int(L), inp.HQK, inp.HV, inp.dk, inp.dv, e, inp.S0 is not None)[0] for L in lens)
         fl = sum(prefill_alg(1, int(L), inp.HQK, inp.HV, inp.dk, inp.dv, e, False)[1] for L in lens)
+        fr = sum(prefill_alg(1, int(L), inp.HQK, inp.HV, inp.dk, inp.dv, e, False)[2] for L in lens)
         kname = binding.prefill_kernel_name(inp.N, inp.total_T, inp.HQK, inp.HV, inp.dk, inp.dv, tdt)
+        roof = prefill_roofline(ab, fl, fr, ms, kname)
         out[name] = {"sequences": inp.N, "tokens": inp.total_T, "heads": [inp.HQK, inp.HV], "d": [inp.dk, inp.dv],
                      "dtype": inp.dtype, "kernel": kname, "ms": ms, "Mtok_s": inp.total_T / (ms * 1e-3) / 1e6,
-                     "mfma_frac": fl / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12) if "chunk" in kname else None,
-                     "hbm_frac": ab / (ms * 1e-3) / (PEAK_HBM_GBPS * 1e9)}
+                     "mfma_frac": roof.get("mfma_frac"),
+                     "hbm_frac": ab / (ms * 1e-3) / (PEAK_HBM_GBPS * 1e9), "roofline": roof}
         del d, o, ST, ws, S0, cu
         torch.cuda.empty_cache()
     return out

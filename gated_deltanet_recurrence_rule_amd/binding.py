@@ -123,19 +123,20 @@ def _variant_code(variant) -> int:
     return int(variant)
 
 
-def _need_opt(t: Optional[torch.Tensor], name: str, dtype):
+def _need_opt(t: Optional[torch.Tensor], name: str, dtype, shape=None, device=None):
     if t is not None:
-        _need(t, name, dtype)
+        _need(t, name, dtype, shape, device)
 
 
-def _block_ops(A_log, dt_bias, beta_logits, z, norm_w, norm_eps, io_dtype, alpha_sigmoid=False):
+def _block_ops(A_log, dt_bias, beta_logits, z, norm_w, norm_eps, io_dtype, alpha_sigmoid=False, *,
+               HV, dv, z_shape, device):
     """A BlockOps for the given parts, or None when none is asked for."""
     if A_log is None and dt_bias is None and not beta_logits and z is None and not alpha_sigmoid:
         return None
-    _need_opt(A_log, "A_log", torch.float32)
-    _need_opt(dt_bias, "dt_bias", torch.float32)
-    _need_opt(z, "z", io_dtype)
-    _need_opt(norm_w, "norm_w", torch.float32)
+    _need_opt(A_log, "A_log", torch.float32, (HV,), device)
+    _need_opt(dt_bias, "dt_bias", torch.float32, (HV,), device)
+    _need_opt(z, "z", io_dtype, z_shape, device)
+    _need_opt(norm_w, "norm_w", torch.float32, (dv,), device)
     if dt_bias is not None and A_log is None and not alpha_sigmoid:
         raise ValueError("dt_bias is only used with A_log or alpha_sigmoid")
     return BlockOps(None if A_log is None else A_log.data_ptr(),
@@ -144,13 +145,26 @@ def _block_ops(A_log, dt_bias, beta_logits, z, norm_w, norm_eps, io_dtype, alpha
                     float(norm_eps), 1 if alpha_sigmoid else 0)
 
 
-def _need(t: torch.Tensor, name: str, dtype=None):
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None, device=None):
+    """t must be a contiguous device tensor of the given dtype, shape and device: the C ABI sees
+    only pointers, so a tensor smaller than its sizes imply would be read or written past its
+    end by the kernels."""
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call runs on {device}")
+
+
+def _dims(t: torch.Tensor, name: str, n: int):
+    if t.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions, got shape {tuple(t.shape)}")
+    return tuple(int(x) for x in t.shape)
 
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch.Tensor],
@@ -168,19 +182,22 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[t
     norm_w [dv] and norm_eps applies the gated RMS norm to o; alpha_sigmoid (with dt_bias as
     the bias) makes g the raw a of alpha = sigmoid(a + bias) instead.
     """
-    N, HQK, dk = q.shape
-    HV, dv = v.shape[1], v.shape[2]
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, q.dtype)
-    _need_opt(g, "g", torch.float32)
-    _need_opt(beta, "beta", torch.float32)
-    _need(S, "S", torch.float32)
+    N, HQK, dk = _dims(q, "q", 3)
+    _, HV, dv = _dims(v, "v", 3)
+    dev = q.device
+    _need(q, "q", q.dtype, device=dev)
+    _need(k, "k", q.dtype, (N, HQK, dk), dev)
+    _need(v, "v", q.dtype, (N, HV, dv), dev)
+    _need_opt(g, "g", torch.float32, (N, HV), dev)
+    _need_opt(beta, "beta", torch.float32, (N, HV), dev)
+    _need(S, "S", torch.float32, (N, HV, dk, dv), dev)
     if o is None:
-        o = torch.empty((N, HV, dv), dtype=v.dtype, device=v.device)
-    _need(o, "o", v.dtype)
+        o = torch.empty((N, HV, dv), dtype=v.dtype, device=dev)
+    _need(o, "o", v.dtype, (N, HV, dv), dev)
     var = _variant_code(variant)
     lib = load()
-    ops = _block_ops(A_log, dt_bias, beta_logits, z, norm_w, norm_eps, v.dtype, alpha_sigmoid)
+    ops = _block_ops(A_log, dt_bias, beta_logits, z, norm_w, norm_eps, v.dtype, alpha_sigmoid,
+                     HV=HV, dv=dv, z_shape=(N, HV, dv), device=dev)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(o), N, HQK, HV, dk, dv,
             _dtype_code(q), float(scale))
     if ops is not None:
@@ -215,15 +232,27 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch
     S0 [N, HV, dk, dv] fp32 or None.  Returns (o [total_T, HV, dv], S_T or None).
     variant and the block parts: as for decode_step (z is [total_T, HV, dv]).
     """
-    total_T, HQK, dk = q.shape
-    HV, dv = v.shape[1], v.shape[2]
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, q.dtype)
-    _need_opt(g, "g", torch.float32)
-    _need_opt(beta, "beta", torch.float32)
+    return _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, N, S0, scale, o, S_T, output_state, workspace,
+                    variant, A_log, dt_bias, beta_logits, z, norm_w, norm_eps, alpha_sigmoid)
+
+
+def _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, N, S0, scale, o, S_T, output_state, workspace,
+             variant, A_log, dt_bias, beta_logits, z, norm_w, norm_eps, alpha_sigmoid):
+    total_T, HQK, dk = _dims(q, "q", 3)
+    _, HV, dv = _dims(v, "v", 3)
+    dev = q.device
+    _need(q, "q", q.dtype, device=dev)
+    _need(k, "k", q.dtype, (total_T, HQK, dk), dev)
+    _need(v, "v", q.dtype, (total_T, HV, dv), dev)
+    _need_opt(g, "g", torch.float32, (total_T, HV), dev)
+    _need_opt(beta, "beta", torch.float32, (total_T, HV), dev)
     if cu_seqlens is not None:
-        _need(cu_seqlens, "cu_seqlens", torch.int32)
+        _need(cu_seqlens, "cu_seqlens", torch.int32, device=dev)
+        if cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 1:
+            raise ValueError("cu_seqlens must be a 1-D tensor of N + 1 entries")
         n_seq = int(cu_seqlens.shape[0] - 1)
+        if N is not None and int(N) != n_seq:
+            raise ValueError(f"N = {N} but cu_seqlens has {n_seq + 1} entries")
     else:
         if N is None:
             raise ValueError("give cu_seqlens or N")
@@ -232,28 +261,29 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch
     if cu_seqlens_host is not None:
         import numpy as np
         host = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
-        if host.shape[0] != n_seq + 1:
+        if host.shape != (n_seq + 1,):
             raise ValueError("cu_seqlens_host must have N + 1 entries")
-    if S0 is not None:
-        _need(S0, "S0", torch.float32)
+    _need_opt(S0, "S0", torch.float32, (n_seq, HV, dk, dv), dev)
     if o is None:
-        o = torch.empty((total_T, HV, dv), dtype=v.dtype, device=v.device)
-    _need(o, "o", v.dtype)
+        o = torch.empty((total_T, HV, dv), dtype=v.dtype, device=dev)
+    _need(o, "o", v.dtype, (total_T, HV, dv), dev)
     if S_T is None and output_state:
-        S_T = torch.empty((n_seq, HV, dk, dv), dtype=torch.float32, device=v.device)
-    if S_T is not None:
-        _need(S_T, "S_T", torch.float32)
+        S_T = torch.empty((n_seq, HV, dk, dv), dtype=torch.float32, device=dev)
+    _need_opt(S_T, "S_T", torch.float32, (n_seq, HV, dk, dv), dev)
     lib = load()
     code = _dtype_code(q)
     need = int(lib.gdn_prefill_workspace_size(n_seq, total_T, HQK, HV, dk, dv, code))
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=v.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _need(workspace, "workspace", device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     host_ptr = None if host is None else host.ctypes.data_as(ctypes.c_void_p)
     var = _variant_code(variant)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), host_ptr, n_seq, total_T,
             _ptr(S0), _ptr(o), _ptr(S_T), HQK, HV, dk, dv, code, float(scale))
-    ops = _block_ops(A_log, dt_bias, beta_logits, z, norm_w, norm_eps, v.dtype, alpha_sigmoid)
+    ops = _block_ops(A_log, dt_bias, beta_logits, z, norm_w, norm_eps, v.dtype, alpha_sigmoid,
+                     HV=HV, dv=dv, z_shape=(total_T, HV, dv), device=dev)
     if ops is not None:
         _check(lib.gdn_prefill_ex(*args, var, ctypes.byref(ops), _ptr(workspace), ws_bytes,
                                   _stream(q.device)))
@@ -285,27 +315,29 @@ def conv_silu(x: torch.Tensor, w: torch.Tensor, *, HQK: int, HV: int, dk: int, d
     [N, 3, Ctot] in x's dtype (None: zeros / not written; they may be the same tensor).
     Returns (q [total_T, HQK, dk], k, v [total_T, HV, dv]) in x's dtype.
     """
-    total_T, Ct = x.shape
+    total_T, Ct = _dims(x, "x", 2)
     if Ct != 2 * HQK * dk + HV * dv:
         raise ValueError("x's width must be 2 HQK dk + HV dv")
-    _need(x, "x")
+    dev = x.device
+    _need(x, "x", device=dev)
     code = _dtype_code(x)
-    _need(w, "w", torch.float32)
+    _need(w, "w", torch.float32, (Ct, 4), dev)
     if cu_seqlens is not None:
-        _need(cu_seqlens, "cu_seqlens", torch.int32)
+        _need(cu_seqlens, "cu_seqlens", torch.int32, device=dev)
+        if cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 1:
+            raise ValueError("cu_seqlens must be a 1-D tensor of N + 1 entries")
         n_seq = int(cu_seqlens.shape[0] - 1)
     else:
         if N is None:
             raise ValueError("give cu_seqlens or N")
         n_seq = int(N)
-    _need_opt(state_in, "state_in", x.dtype)
-    _need_opt(state_out, "state_out", x.dtype)
-    dev = x.device
+    _need_opt(state_in, "state_in", x.dtype, (n_seq, 3, Ct), dev)
+    _need_opt(state_out, "state_out", x.dtype, (n_seq, 3, Ct), dev)
     q = torch.empty((total_T, HQK, dk), dtype=x.dtype, device=dev) if q is None else q
     k = torch.empty((total_T, HQK, dk), dtype=x.dtype, device=dev) if k is None else k
     v = torch.empty((total_T, HV, dv), dtype=x.dtype, device=dev) if v is None else v
-    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, nm, x.dtype)
+    for t, nm, shp in ((q, "q", (total_T, HQK, dk)), (k, "k", (total_T, HQK, dk)), (v, "v", (total_T, HV, dv))):
+        _need(t, nm, x.dtype, shp, dev)
     host, host_ptr = _host_seqlens(cu_seqlens_host, n_seq)
     _check(load().gdn_conv_silu(_ptr(x), _ptr(w), _ptr(cu_seqlens), host_ptr, n_seq, total_T, _ptr(state_in),
                                 _ptr(state_out), _ptr(q), _ptr(k), _ptr(v), HQK, HV, dk, dv, code,
@@ -316,14 +348,15 @@ def conv_silu(x: torch.Tensor, w: torch.Tensor, *, HQK: int, HV: int, dk: int, d
 def gated_rmsnorm(x: torch.Tensor, z: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
                   y: Optional[torch.Tensor] = None) -> torch.Tensor:
     """y = w * x / sqrt(mean(x^2) + eps) * silu(z) over the last dimension (dv); y may be x."""
-    _need(x, "x")
-    _need(z, "z", x.dtype)
-    _need(w, "w", torch.float32)
-    if z.shape != x.shape:
-        raise ValueError("z must have x's shape")
+    dev = x.device
+    _need(x, "x", device=dev)
+    if x.dim() < 1:
+        raise ValueError("x must have a last dimension (dv)")
     dv = x.shape[-1]
+    _need(z, "z", x.dtype, tuple(x.shape), dev)
+    _need(w, "w", torch.float32, (dv,), dev)
     y = torch.empty_like(x) if y is None else y
-    _need(y, "y", x.dtype)
+    _need(y, "y", x.dtype, tuple(x.shape), dev)
     _check(load().gdn_gated_rmsnorm(_ptr(x), _ptr(z), _ptr(w), float(eps), _ptr(y), x.numel() // max(dv, 1), dv,
                                     _dtype_code(x), _stream(x.device)))
     return y

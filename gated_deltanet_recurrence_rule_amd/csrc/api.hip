@@ -107,6 +107,39 @@ bool partial_overlap(const void *a, size_t na, const void *b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
+// A buffer a call reads or writes: its first byte and length (a NULL or empty one is skipped).
+struct Span {
+    const void *p;
+    size_t n;
+    const char *name;
+};
+
+bool overlaps(const Span &a, const Span &b) {
+    if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+    const uintptr_t x = (uintptr_t)a.p, y = (uintptr_t)b.p;
+    return x < y + b.n && y < x + a.n;
+}
+
+// Every output must be disjoint from every input and from every other output; the one
+// exception allowed is an output that is exactly the input named `same_ok_in` (same first
+// byte and length), for the outputs listed as updating that input in place.
+gdn_status check_disjoint(const Span *outs, int no, const Span *ins, int ni, const char *same_ok_out = nullptr,
+                          const char *same_ok_in = nullptr) {
+    for (int i = 0; i < no; ++i) {
+        for (int j = 0; j < ni; ++j) {
+            if (!overlaps(outs[i], ins[j])) continue;
+            const bool exact = outs[i].p == ins[j].p && outs[i].n == ins[j].n;
+            if (exact && same_ok_out && same_ok_in && strcmp(outs[i].name, same_ok_out) == 0 &&
+                strcmp(ins[j].name, same_ok_in) == 0)
+                continue;
+            return fail(GDN_ERR_ALIAS, "%s overlaps %s", outs[i].name, ins[j].name);
+        }
+        for (int j = 0; j < i; ++j)
+            if (overlaps(outs[i], outs[j])) return fail(GDN_ERR_ALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
+    }
+    return GDN_OK;
+}
+
 gdn::GateArgs gate_args(const gdn_block_ops *ops, gdn_variant variant) {
     gdn::GateArgs ga;
     if (ops) {
@@ -173,127 +206,43 @@ gdn_status hip_status(hipError_t e, const char *what) {
     return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-}  // namespace
-
-extern "C" {
-
-const char *gdn_status_str(gdn_status s) {
-    switch (s) {
-        case GDN_OK: return "ok";
-        case GDN_ERR_NULL: return "null pointer";
-        case GDN_ERR_SHAPE: return "bad shape";
-        case GDN_ERR_DTYPE: return "bad dtype";
-        case GDN_ERR_UNSUPPORTED: return "unsupported configuration";
-        case GDN_ERR_ALIGN: return "misaligned pointer";
-        case GDN_ERR_SEQLENS: return "bad sequence lengths";
-        case GDN_ERR_WORKSPACE: return "workspace too small";
-        case GDN_ERR_HIP: return "HIP runtime error";
-        case GDN_ERR_ALIAS: return "overlapping buffers";
-        case GDN_ERR_VALUE: return "argument out of range";
-    }
-    return "unknown status";
-}
-
-const char *gdn_last_error(void) { return g_last_error; }
-
-int32_t gdn_version(void) { return 200; /* 0.2.0 */ }
-
-gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
-                           const float *beta, float *S, void *o, int32_t N, int32_t HQK,
-                           int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype, float scale,
-                           hipStream_t stream) {
-    return gdn_decode_step_v(q, k, v, g, beta, S, o, N, HQK, HV, dk, dv, dtype, scale, GDN_GATED_DELTA,
-                             stream);
-}
-
-gdn_status gdn_decode_step_v(const void *q, const void *k, const void *v, const float *g,
-                             const float *beta, float *S, void *o, int32_t N, int32_t HQK,
-                             int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype, float scale,
-                             gdn_variant variant, hipStream_t stream) {
-    return gdn_decode_step_ex(q, k, v, g, beta, S, o, N, HQK, HV, dk, dv, dtype, scale, variant, nullptr,
-                              stream);
-}
-
-gdn_status gdn_decode_step_ex(const void *q, const void *k, const void *v, const float *g,
-                              const float *beta, float *S, void *o, int32_t N, int32_t HQK,
-                              int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype, float scale,
-                              gdn_variant variant, const gdn_block_ops *ops, hipStream_t stream) {
-    g_last_error[0] = 0;
-    gdn_status st = check_common(q, k, v, g, beta, o, N, HQK, HV, dk, dv, dtype, N, variant);
-    if (st != GDN_OK) return st;
-    st = check_ops(ops, variant, beta, N);
-    if (st != GDN_OK) return st;
-    if (ops && ops->z) {
-        const size_t ob = (size_t)N * HV * dv * (dtype == GDN_BF16 ? 2 : 4);
-        if (partial_overlap(ops->z, ob, o, ob)) return fail(GDN_ERR_ALIAS, "z partly overlaps o");
-    }
-    if (N == 0) return GDN_OK;
-    if (!S) return fail(GDN_ERR_NULL, "S must be non-NULL");
-    if (!aligned(S, 16)) return fail(GDN_ERR_ALIGN, "S must be 16-byte aligned");
-    if ((int64_t)N * HV > 0x7fffffffLL) return fail(GDN_ERR_SHAPE, "N * HV exceeds the grid limit");
-    gdn::DecodeArgs a{q, k, v, variant_gated(variant) ? g : nullptr, beta, S, o, N, HQK, HV, dk, dv, scale,
-                      variant_delta(variant) ? 1 : 0};
-    a.gate = gate_args(ops, variant);
-    if (ops && ops->z) {
-        a.z = ops->z;
-        a.norm_w = ops->norm_w;
-        a.norm_eps = ops->norm_eps;
-    }
-    a.max_wgs = 4 * device_cus();
-    return hip_status(gdn::launch_decode(a, dtype == GDN_BF16, stream), "decode launch");
-}
-
-size_t gdn_prefill_workspace_size(int32_t N, int64_t total_T, int32_t HQK, int32_t HV,
-                                  int32_t dk, int32_t dv, gdn_dtype dtype) {
-    (void)HQK;
-    if (N < 0 || total_T < 0 || HV <= 0) return 0;
-    return workspace_plan(N, total_T, HV, dk, dv, dtype).total();
-}
-
-gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float *g,
-                       const float *beta, const int32_t *cu_seqlens,
-                       const int32_t *cu_seqlens_host, int32_t N, int64_t total_T,
-                       const float *S0, void *o, float *S_T, int32_t HQK, int32_t HV, int32_t dk,
-                       int32_t dv, gdn_dtype dtype, float scale, void *workspace,
-                       size_t workspace_bytes, hipStream_t stream) {
-    return gdn_prefill_v(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, N, total_T, S0, o, S_T, HQK, HV, dk,
-                         dv, dtype, scale, GDN_GATED_DELTA, workspace, workspace_bytes, stream);
-}
-
-gdn_status gdn_prefill_v(const void *q, const void *k, const void *v, const float *g,
-                         const float *beta, const int32_t *cu_seqlens,
-                         const int32_t *cu_seqlens_host, int32_t N, int64_t total_T,
-                         const float *S0, void *o, float *S_T, int32_t HQK, int32_t HV, int32_t dk,
-                         int32_t dv, gdn_dtype dtype, float scale, gdn_variant variant, void *workspace,
-                         size_t workspace_bytes, hipStream_t stream) {
-    return gdn_prefill_ex(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, N, total_T, S0, o, S_T, HQK, HV, dk, dv,
-                          dtype, scale, variant, nullptr, workspace, workspace_bytes, stream);
-}
-
-gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v, const float *g,
-                          const float *beta, const int32_t *cu_seqlens,
-                          const int32_t *cu_seqlens_host, int32_t N, int64_t total_T,
-                          const float *S0, void *o, float *S_T, int32_t HQK, int32_t HV, int32_t dk,
-                          int32_t dv, gdn_dtype dtype, float scale, gdn_variant variant,
-                          const gdn_block_ops *ops, void *workspace, size_t workspace_bytes,
-                          hipStream_t stream) {
+// The prefill behind gdn_prefill, gdn_prefill_v and gdn_prefill_ex.
+gdn_status run_prefill(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                       const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int32_t N, int64_t total_T,
+                       const float *S0, void *o, float *S_T, int32_t HQK, int32_t HV, int32_t dk, int32_t dv,
+                       gdn_dtype dtype, float scale, gdn_variant variant, const gdn_block_ops *ops,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
     g_last_error[0] = 0;
     if (total_T < 0) return fail(GDN_ERR_SHAPE, "total_T = %lld is negative", (long long)total_T);
     gdn_status st = check_common(q, k, v, g, beta, o, N, HQK, HV, dk, dv, dtype, total_T, variant);
     if (st != GDN_OK) return st;
     st = check_ops(ops, variant, beta, total_T);
     if (st != GDN_OK) return st;
-    if (ops && ops->z) {
-        // the norm runs in place on o after the scan, reading z
-        const size_t ob = (size_t)total_T * HV * dv * (dtype == GDN_BF16 ? 2 : 4);
-        if (ops->z == o || partial_overlap(ops->z, ob, o, ob)) return fail(GDN_ERR_ALIAS, "z overlaps o");
-    }
     if (S0 && !aligned(S0, 16)) return fail(GDN_ERR_ALIGN, "S0 must be 16-byte aligned");
     if (S_T && !aligned(S_T, 16)) return fail(GDN_ERR_ALIGN, "S_T must be 16-byte aligned");
     if ((int64_t)N * HV > 0x7fffffffLL) return fail(GDN_ERR_SHAPE, "N * HV exceeds the grid limit");
     int64_t eq_len = 0;
     st = check_seqlens(cu_seqlens, cu_seqlens_host, N, total_T, &eq_len);
     if (st != GDN_OK) return st;
+    if (N > 0) {
+        const size_t es = dtype == GDN_BF16 ? 2 : 4;
+        const size_t T = (size_t)total_T, nqk = T * HQK * dk * es, nv = T * HV * dv * es, ng = T * HV * 4;
+        const size_t ns = (size_t)N * HV * dk * dv * 4;
+        const Span outs[] = {{o, nv, "o"}, {S_T, ns, "S_T"}, {workspace, workspace_bytes, "workspace"}};
+        const Span ins[] = {{q, nqk, "q"},
+                            {k, nqk, "k"},
+                            {v, nv, "v"},
+                            {variant_gated(variant) ? g : nullptr, ng, "g"},
+                            {beta, ng, "beta"},
+                            {S0, ns, "S0"},
+                            {cu_seqlens, ((size_t)N + 1) * 4, "cu_seqlens"},
+                            {ops ? ops->z : nullptr, nv, "z"},
+                            {ops ? ops->A_log : nullptr, (size_t)HV * 4, "A_log"},
+                            {ops ? ops->dt_bias : nullptr, (size_t)HV * 4, "dt_bias"},
+                            {ops && ops->z ? ops->norm_w : nullptr, (size_t)dv * 4, "norm_w"}};
+        st = check_disjoint(outs, 3, ins, 11, "S_T", "S0");
+        if (st != GDN_OK) return st;
+    }
     const WorkspacePlan plan = workspace_plan(N, total_T, HV, dk, dv, dtype);
     const size_t need = plan.total();
     if (workspace_bytes < need)
@@ -346,6 +295,126 @@ gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v, const flo
     return hip_status(gdn::launch_gated_rmsnorm(na, bf16, stream), "gated norm launch");
 }
 
+}  // namespace
+
+extern "C" {
+
+const char *gdn_status_str(gdn_status s) {
+    switch (s) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_NULL: return "null pointer";
+        case GDN_ERR_SHAPE: return "bad shape";
+        case GDN_ERR_DTYPE: return "bad dtype";
+        case GDN_ERR_UNSUPPORTED: return "unsupported configuration";
+        case GDN_ERR_ALIGN: return "misaligned pointer";
+        case GDN_ERR_SEQLENS: return "bad sequence lengths";
+        case GDN_ERR_WORKSPACE: return "workspace too small";
+        case GDN_ERR_HIP: return "HIP runtime error";
+        case GDN_ERR_ALIAS: return "overlapping buffers";
+        case GDN_ERR_VALUE: return "argument out of range";
+    }
+    return "unknown status";
+}
+
+const char *gdn_last_error(void) { return g_last_error; }
+
+int32_t gdn_version(void) { return 200; /* 0.2.0 */ }
+
+gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, float *S, void *o, int32_t N, int32_t HQK,
+                           int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype, float scale,
+                           hipStream_t stream) {
+    return gdn_decode_step_v(q, k, v, g, beta, S, o, N, HQK, HV, dk, dv, dtype, scale, GDN_GATED_DELTA,
+                             stream);
+}
+
+gdn_status gdn_decode_step_v(const void *q, const void *k, const void *v, const float *g,
+                             const float *beta, float *S, void *o, int32_t N, int32_t HQK,
+                             int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype, float scale,
+                             gdn_variant variant, hipStream_t stream) {
+    return gdn_decode_step_ex(q, k, v, g, beta, S, o, N, HQK, HV, dk, dv, dtype, scale, variant, nullptr,
+                              stream);
+}
+
+gdn_status gdn_decode_step_ex(const void *q, const void *k, const void *v, const float *g,
+                              const float *beta, float *S, void *o, int32_t N, int32_t HQK,
+                              int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype, float scale,
+                              gdn_variant variant, const gdn_block_ops *ops, hipStream_t stream) {
+    g_last_error[0] = 0;
+    gdn_status st = check_common(q, k, v, g, beta, o, N, HQK, HV, dk, dv, dtype, N, variant);
+    if (st != GDN_OK) return st;
+    st = check_ops(ops, variant, beta, N);
+    if (st != GDN_OK) return st;
+    if (N == 0) return GDN_OK;
+    if (!S) return fail(GDN_ERR_NULL, "S must be non-NULL");
+    if (!aligned(S, 16)) return fail(GDN_ERR_ALIGN, "S must be 16-byte aligned");
+    if ((int64_t)N * HV > 0x7fffffffLL) return fail(GDN_ERR_SHAPE, "N * HV exceeds the grid limit");
+    {
+        const size_t es = dtype == GDN_BF16 ? 2 : 4;
+        const size_t nqk = (size_t)N * HQK * dk * es, nv = (size_t)N * HV * dv * es, ng = (size_t)N * HV * 4;
+        const Span outs[] = {{S, (size_t)N * HV * dk * dv * 4, "S"}, {o, nv, "o"}};
+        const Span ins[] = {{q, nqk, "q"},
+                            {k, nqk, "k"},
+                            {v, nv, "v"},
+                            {variant_gated(variant) ? g : nullptr, ng, "g"},
+                            {beta, ng, "beta"},
+                            {ops ? ops->z : nullptr, nv, "z"},
+                            {ops ? ops->A_log : nullptr, (size_t)HV * 4, "A_log"},
+                            {ops ? ops->dt_bias : nullptr, (size_t)HV * 4, "dt_bias"},
+                            {ops && ops->z ? ops->norm_w : nullptr, (size_t)dv * 4, "norm_w"}};
+        st = check_disjoint(outs, 2, ins, 9);
+        if (st != GDN_OK) return st;
+    }
+    gdn::DecodeArgs a{q, k, v, variant_gated(variant) ? g : nullptr, beta, S, o, N, HQK, HV, dk, dv, scale,
+                      variant_delta(variant) ? 1 : 0};
+    a.gate = gate_args(ops, variant);
+    if (ops && ops->z) {
+        a.z = ops->z;
+        a.norm_w = ops->norm_w;
+        a.norm_eps = ops->norm_eps;
+    }
+    a.max_wgs = 4 * device_cus();
+    return hip_status(gdn::launch_decode(a, dtype == GDN_BF16, stream), "decode launch");
+}
+
+size_t gdn_prefill_workspace_size(int32_t N, int64_t total_T, int32_t HQK, int32_t HV,
+                                  int32_t dk, int32_t dv, gdn_dtype dtype) {
+    (void)HQK;
+    if (N < 0 || total_T < 0 || HV <= 0) return 0;
+    return workspace_plan(N, total_T, HV, dk, dv, dtype).total();
+}
+
+gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float *g,
+                       const float *beta, const int32_t *cu_seqlens,
+                       const int32_t *cu_seqlens_host, int32_t N, int64_t total_T,
+                       const float *S0, void *o, float *S_T, int32_t HQK, int32_t HV, int32_t dk,
+                       int32_t dv, gdn_dtype dtype, float scale, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+    return gdn_prefill_v(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, N, total_T, S0, o, S_T, HQK, HV, dk,
+                         dv, dtype, scale, GDN_GATED_DELTA, workspace, workspace_bytes, stream);
+}
+
+gdn_status gdn_prefill_v(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const int32_t *cu_seqlens,
+                         const int32_t *cu_seqlens_host, int32_t N, int64_t total_T,
+                         const float *S0, void *o, float *S_T, int32_t HQK, int32_t HV, int32_t dk,
+                         int32_t dv, gdn_dtype dtype, float scale, gdn_variant variant, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+    return gdn_prefill_ex(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, N, total_T, S0, o, S_T, HQK, HV, dk, dv,
+                          dtype, scale, variant, nullptr, workspace, workspace_bytes, stream);
+}
+
+gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const int32_t *cu_seqlens,
+                          const int32_t *cu_seqlens_host, int32_t N, int64_t total_T,
+                          const float *S0, void *o, float *S_T, int32_t HQK, int32_t HV, int32_t dk,
+                          int32_t dv, gdn_dtype dtype, float scale, gdn_variant variant,
+                          const gdn_block_ops *ops, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+    return run_prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, N, total_T, S0, o, S_T, HQK, HV, dk, dv,
+                       dtype, scale, variant, ops, workspace, workspace_bytes, stream);
+}
+
 gdn_status gdn_conv_silu(const void *x, const float *w, const int32_t *cu_seqlens,
                          const int32_t *cu_seqlens_host, int32_t N, int64_t total_T,
                          const void *state_in, void *state_out, void *q, void *k, void *v,
@@ -369,8 +438,16 @@ gdn_status gdn_conv_silu(const void *x, const float *w, const int32_t *cu_seqlen
         return fail(GDN_ERR_ALIGN, "x, w, q, k, v and the states must be 16-byte aligned");
     const size_t es = dtype == GDN_BF16 ? 2 : 4;
     const size_t sbytes = (size_t)N * 3 * (size_t)Ct * es;
-    if (partial_overlap(state_in, sbytes, state_out, sbytes))
-        return fail(GDN_ERR_ALIAS, "state_out overlaps state_in without being the same buffer");
+    {
+        const size_t T = (size_t)total_T, nq = T * HQK * dk * es, nv = T * HV * dv * es;
+        const Span outs[] = {{q, nq, "q"}, {k, nq, "k"}, {v, nv, "v"}, {state_out, sbytes, "state_out"}};
+        const Span ins[] = {{x, T * (size_t)Ct * es, "x"},
+                            {w, (size_t)Ct * 16, "w"},
+                            {state_in, sbytes, "state_in"},
+                            {cu_seqlens, ((size_t)N + 1) * 4, "cu_seqlens"}};
+        st = check_disjoint(outs, 4, ins, 4, "state_out", "state_in");
+        if (st != GDN_OK) return st;
+    }
     gdn::ConvArgs a{x, w, cu_seqlens, eq_len, N, total_T, state_in, state_out, q, k, v, HQK * dk, HV * dv};
     return hip_status(gdn::launch_conv_silu(a, dtype == GDN_BF16, stream), "conv launch");
 }

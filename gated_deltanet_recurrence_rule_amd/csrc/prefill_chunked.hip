@@ -30,8 +30,9 @@
 // rounded once or carried as hi + lo (hi = bf16(x), lo = bf16(x - hi); two or
 // three MFMAs).  Raw q, k, v rows are exact bf16.  The table path is carried
 // hi + lo: S in K S, T_b, A_10 and Z / Delta in the solve, the scaled Delta in
-// K^T D.  The output path rounds once: S in Q S, P and Delta in P Delta.  All
-// accumulation is fp32.
+// K^T D.  The output path rounds once: S in Q S, P and Delta in P Delta -- except
+// for the rules without the look-up, whose growing table is carried hi + lo in Q S
+// too.  All accumulation is fp32.
 //
 // Mapping.  One workgroup of 8 waves owns one (sequence, V head, 64-column
 // slice of dv) and walks its chunks in order; dv columns of S evolve
@@ -402,6 +403,11 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                 if constexpr (DELTA) {
 #pragma unroll
                     for (int rt = 0; rt < 4; ++rt) y[rt] = mfma32(kk[rt], Sl, y[rt]);
+                } else if (reads) {
+                    // without the look-up the table grows with the sequence and so do the
+                    // reads: carry the table as hi + lo in Q S as well (no K S to pay for)
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt) Ot[rt] = mfma32(Sl, qq[rt], Ot[rt]);
                 }
             }
 #pragma unroll
@@ -909,12 +915,18 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             f32x4 T, Tt;
             bf16x8 kd[4];
             invert_block(T, Tt, kd);
-            // wait for W of this chunk (bounded: the partner wave writes it unconditionally)
+            // wait for W of this chunk (bounded: the partner wave writes it unconditionally).  A
+            // wait that gave up would leave a stale W in the buffer: the block is then poisoned
+            // with NaN, so the failure shows in every read and table it reaches.
+            bool handed = false;
             for (int spin = 0; spin < (1 << 22); ++spin) {
-                if (__hip_atomic_load(flag + b, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) > c) break;
+                if (__hip_atomic_load(flag + b, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) > c) {
+                    handed = true;
+                    break;
+                }
                 __builtin_amdgcn_s_sleep(1);
             }
-            const f32x4 W = Wbuf[b * 64 + ln];
+            const f32x4 W = handed ? Wbuf[b * 64 + ln] : f32x4{NAN, NAN, NAN, NAN};
             // T_10^T = -(T_11 W)^T = -W^T T_11^T
             bf16x4 wh, wl, th, tl;
             hl(W, wh, wl);

@@ -64,7 +64,7 @@ typedef enum {
     GDN_ERR_SEQLENS = -6,     /* cu_seqlens_host malformed, or N does not divide T     */
     GDN_ERR_WORKSPACE = -7,   /* workspace smaller than gdn_prefill_workspace_size()   */
     GDN_ERR_HIP = -8,         /* the HIP runtime reported an error at launch           */
-    GDN_ERR_ALIAS = -9,       /* an output partly overlaps an input it must not        */
+    GDN_ERR_ALIAS = -9,       /* an output overlaps another buffer it must not (below) */
     GDN_ERR_VALUE = -10       /* a scalar argument out of range (e.g. norm_eps < 0)    */
 } gdn_status;
 
@@ -116,7 +116,9 @@ typedef enum {
  *   S      [N, HV, dk, dv]   fp32       in: S_{t-1}; out: S_t (updated in place)
  *   o      [N, HV, dv]       dtype      out: S_t^T (scale * q^)
  *
- * N = 0 is a valid no-op.  o must not overlap any input.
+ * N = 0 is a valid no-op.  S and o are outputs: each must be disjoint from the other and
+ * from every input (q, k, v, g, beta and the gdn_block_ops arrays of the _ex form), else
+ * GDN_ERR_ALIAS.  Inputs may overlap one another (they are only read).
  */
 gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
                            const float *beta, float *S, void *o, int32_t N, int32_t HQK,
@@ -176,10 +178,14 @@ size_t gdn_prefill_workspace_size(int32_t N, int64_t total_T, int32_t HQK, int32
  *   S0          [N, HV, dk, dv] fp32 start tables, or NULL for empty tables
  *   o           [total_T, HV, dv] dtype, out: per-token reads
  *   S_T         [N, HV, dk, dv] fp32, out: final tables, or NULL to skip.
- *               S_T may be the same pointer as S0 (in-place carry); any other
- *               overlap between outputs and inputs is not allowed.
+ *               S_T may be the same pointer as S0 (in-place carry).
  *   workspace   device scratch of at least gdn_prefill_workspace_size() bytes,
  *               16-byte aligned (may be NULL when that size is 0).
+ *
+ * Overlaps: o, S_T and the workspace (all workspace_bytes of it) are written, so each
+ * must be disjoint from the others and from every input (q, k, v, g, beta, S0,
+ * cu_seqlens and the gdn_block_ops arrays of the _ex form) -- except that S_T may be
+ * exactly S0.  Any other overlap is GDN_ERR_ALIAS.  Inputs may overlap one another.
  *
  * N = 0 is a valid no-op.
  */
@@ -277,10 +283,13 @@ gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v, const flo
  *              oldest first.
  *   state_out  [N, 3, Ctot] or NULL (not written): the last three entries of (state ++ x)
  *              for each sequence; an empty sequence passes its state through.  It may be
- *              the same buffer as state_in; a partial overlap is GDN_ERR_ALIAS.
+ *              the same buffer as state_in.
  *   q, k       [total_T, HQK, dk] and v [total_T, HV, dv] in dtype: y split into the
  *              arrays gdn_prefill and gdn_decode_step read.  fp32 arithmetic; bf16 outputs
  *              rounded once to nearest even.
+ * Overlaps: q, k, v and state_out are written: each must be disjoint from the others and
+ * from x, w, state_in and cu_seqlens, except that state_out may be exactly state_in
+ * (GDN_ERR_ALIAS otherwise).
  * Alignment: every array 16 bytes.  Sizes: dk, dv in {32, 64, 128}, HQK, HV > 0.
  */
 gdn_status gdn_conv_silu(const void *x, const float *w, const int32_t *cu_seqlens,

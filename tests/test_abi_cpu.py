@@ -24,6 +24,16 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", src)))
 
 
+@pytest.fixture(scope="module", autouse=True)
+def _no_visible_gpu():
+    """The calls here pass host addresses and must be rejected before any launch; should one be
+    accepted by mistake, it must not reach a real device.  (Counting devices does not
+    initialise the runtime.)"""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("host-pointer ABI checks run only where no GPU is visible")
+
+
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
@@ -397,6 +407,146 @@ def test_split_workspace_too_small_is_rejected(lib):
     B = Bufs(T=8192, N=1, HQK=1, HV=2, dk=128, dv=128)
     need = lib.gdn_prefill_workspace_size(1, 8192, 1, 2, 128, 128, 0)
     assert need > 0
-    ws = np.zeros(16, np.float32)
-    assert _prefill(lib, B, dtype=0, ws=B.p(ws), ws_bytes=need - 1) == E_WS
+    # no pointer: a host array claimed to span need - 1 bytes would overlap the other buffers
+    assert _prefill(lib, B, dtype=0, ws=None, ws_bytes=need - 1) == E_WS
     assert B.untouched()
+
+
+# ------------------------------------------------------------------ overlapping buffers
+# Every call below must fail its checks before any launch (the buffers are host memory).
+@pytest.mark.parametrize("out,into,off", [
+    ("o", "q", 0), ("o", "k", 64), ("o", "v", 16), ("o", "g", 0), ("o", "b", 16),
+    ("S", "q", 0), ("S", "v", 64), ("S", "b", 0), ("S", "o", 16), ("o", "S", 0),
+])
+def test_decode_rejects_overlap(lib, out, into, off):
+    B = Bufs()
+    assert _decode(lib, B, **{out: B.p(getattr(B, into), off)}) == E_ALIAS, lib.gdn_last_error()
+    assert B.untouched()
+
+
+def test_decode_ex_rejects_z_or_weights_inside_outputs(lib):
+    B = Bufs()
+    w = np.ones(B.dv + 4, np.float32)
+    z = np.full_like(B.v, 7.0)
+    assert _decode_ex(lib, B, GATED_DELTA, _ops(B, z=B.p(B.o).value, norm_w=B.p(w).value)) == E_ALIAS
+    assert _decode_ex(lib, B, GATED_DELTA, _ops(B, z=B.p(z).value, norm_w=B.p(B.S, 32).value)) == E_ALIAS
+    assert _decode_ex(lib, B, GATED_DELTA, _ops(B, A_log=B.p(B.o, 16).value)) == E_ALIAS
+    assert B.untouched() and np.all(z == 7.0)
+
+
+@pytest.mark.parametrize("out,into,off", [
+    ("o", "q", 0), ("o", "k", 16), ("o", "v", 0), ("o", "g", 64), ("o", "b", 0), ("o", "S", 0),
+    ("o", "cu", 0), ("ST", "q", 32), ("ST", "v", 0), ("ST", "o", 0), ("ST", "S", 16), ("ST", "cu", 0),
+])
+def test_prefill_rejects_overlap(lib, out, into, off):
+    """o and S_T must be disjoint from every input and from each other; S_T may be exactly S0
+    (covered on the GPU), but not a shifted view of it."""
+    B = Bufs()
+    src = B.cu if into == "cu" else getattr(B, into)
+    key = "S0" if out == "S" else out
+    assert _prefill(lib, B, **{key: B.p(src, off)}) == E_ALIAS, lib.gdn_last_error()
+    assert B.untouched()
+
+
+def test_prefill_rejects_workspace_overlap(lib):
+    B = Bufs()
+    need = lib.gdn_prefill_workspace_size(B.N, B.T, B.HQK, B.HV, B.dk, B.dv, 1)
+    assert need > 0  # the launch-order part of two sequences
+    for name in ("q", "o", "S", "ST"):
+        assert _prefill(lib, B, ws=B.p(getattr(B, name)), ws_bytes=need) == E_ALIAS, name
+    assert B.untouched()
+
+
+def test_conv_rejects_outputs_overlapping(lib):
+    C = ConvBufs()
+    assert _conv(lib, C, q=C.p(C.x)) == E_ALIAS
+    assert _conv(lib, C, k=C.p(C.q, 16)) == E_ALIAS
+    assert _conv(lib, C, v=C.p(C.w)) == E_ALIAS
+    assert _conv(lib, C, so=C.p(C.v)) == E_ALIAS
+    assert C.untouched()
+
+
+# ------------------------------------------------------------------ the Python binding's checks
+class _DevTensor:
+    """Stands in for a contiguous device tensor in the binding's argument checks, which raise
+    before any pointer is taken (so nothing here reaches the library)."""
+
+    def __init__(self, shape, dtype):
+        import torch
+        self.shape = tuple(shape)
+        self.dtype = dtype
+        self.device = torch.device("cuda", 0)
+        self.is_cuda = True
+
+    def is_contiguous(self):
+        return True
+
+    def dim(self):
+        return len(self.shape)
+
+
+def _prefill_args(T=128, N=2, HQK=2, HV=4, dk=64, dv=32):
+    import torch
+    t = lambda *s, dt=torch.bfloat16: _DevTensor(s, dt)
+    return dict(q=t(T, HQK, dk), k=t(T, HQK, dk), v=t(T, HV, dv), g=t(T, HV, dt=torch.float32),
+                beta=t(T, HV, dt=torch.float32), cu_seqlens=t(N + 1, dt=torch.int32),
+                S0=t(N, HV, dk, dv, dt=torch.float32), o=t(T, HV, dv), S_T=t(N, HV, dk, dv, dt=torch.float32))
+
+
+@pytest.mark.parametrize("name,shape", [
+    ("k", (128, 2, 32)), ("k", (127, 2, 64)), ("v", (120, 4, 32)), ("g", (128, 2)), ("beta", (128, 4, 1)),
+    ("S0", (2, 4, 64, 64)), ("S0", (3, 4, 64, 32)), ("o", (128, 4, 64)), ("S_T", (1, 4, 64, 32)),
+])
+def test_binding_prefill_rejects_mis_shaped(name, shape):
+    import torch
+    from gated_deltanet_recurrence_rule_amd import binding
+    a = _prefill_args()
+    a[name] = _DevTensor(shape, a[name].dtype)
+    q, k, v, g, beta = a.pop("q"), a.pop("k"), a.pop("v"), a.pop("g"), a.pop("beta")
+    with pytest.raises(ValueError, match=name):
+        binding.prefill(q, k, v, g, beta, **a)
+
+
+def test_binding_prefill_rejects_seqlens_mismatch():
+    from gated_deltanet_recurrence_rule_amd import binding
+    a = _prefill_args()
+    q, k, v, g, beta = a.pop("q"), a.pop("k"), a.pop("v"), a.pop("g"), a.pop("beta")
+    with pytest.raises(ValueError, match="N = 3"):
+        binding.prefill(q, k, v, g, beta, N=3, **a)
+    with pytest.raises(ValueError, match="cu_seqlens_host"):
+        binding.prefill(q, k, v, g, beta, cu_seqlens_host=[0, 128], **a)
+
+
+@pytest.mark.parametrize("name,shape", [
+    ("k", (5, 2, 32)), ("v", (5, 4, 16)), ("g", (4, 4)), ("beta", (5, 2)), ("S", (5, 4, 64, 16)),
+    ("S", (5, 4, 32, 32)), ("o", (5, 2, 32)), ("z", (5, 4, 64)), ("A_log", (2,)), ("norm_w", (64,)),
+])
+def test_binding_decode_rejects_mis_shaped(name, shape):
+    import torch
+    from gated_deltanet_recurrence_rule_amd import binding
+    t = lambda *s, dt=torch.bfloat16: _DevTensor(s, dt)
+    N, HQK, HV, dk, dv = 5, 2, 4, 64, 32
+    a = dict(q=t(N, HQK, dk), k=t(N, HQK, dk), v=t(N, HV, dv), g=t(N, HV, dt=torch.float32),
+             beta=t(N, HV, dt=torch.float32), S=t(N, HV, dk, dv, dt=torch.float32), o=t(N, HV, dv),
+             z=t(N, HV, dv), A_log=t(HV, dt=torch.float32), norm_w=t(dv, dt=torch.float32))
+    a[name] = _DevTensor(shape, a[name].dtype)
+    with pytest.raises(ValueError, match=name):
+        binding.decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S"], o=a["o"], z=a["z"],
+                            A_log=a["A_log"], norm_w=a["norm_w"])
+
+
+@pytest.mark.parametrize("name,shape", [
+    ("w", (2 * 64 + 4 * 32, 3)), ("state_in", (2, 3, 100)), ("state_out", (3, 3, 256)), ("q", (10, 2, 32)),
+    ("v", (10, 4, 64)),
+])
+def test_binding_conv_rejects_mis_shaped(name, shape):
+    import torch
+    from gated_deltanet_recurrence_rule_amd import binding
+    t = lambda *s, dt=torch.bfloat16: _DevTensor(s, dt)
+    T, N, HQK, HV, dk, dv = 10, 2, 1, 4, 64, 32
+    Ct = 2 * HQK * dk + HV * dv
+    a = dict(w=t(Ct, 4, dt=torch.float32), state_in=t(N, 3, Ct), state_out=t(N, 3, Ct), q=t(T, HQK, dk),
+             k=t(T, HQK, dk), v=t(T, HV, dv))
+    a[name] = _DevTensor(shape, a[name].dtype)
+    with pytest.raises(ValueError, match=name):
+        binding.conv_silu(t(T, Ct), a.pop("w"), HQK=HQK, HV=HV, dk=dk, dv=dv, N=N, **a)

@@ -70,3 +70,18 @@ def test_block_part_counts():
     # the read and z in, the normed read out, the fp32 weight of length dv
     assert bench.norm_alg(rows, 128, 2) == _tensor_bytes(((rows, 128), 2), ((rows, 128), 2),
                                                          ((rows, 128), 2), ((128,), 4)) == 1_610_613_248
+
+
+def test_prefill_roofline_names_the_binding_roof():
+    """The chunked prefill's algorithmic intensity (~230 flop/B) is below the bf16 ridge (312), so its
+    headline roof is HBM, with the MFMA fraction beside it; the token-serial kernel is bound by
+    fp32 vector arithmetic."""
+    nbytes, flops, flops_rec = bench.prefill_alg(4, 16384, 16, 32, 128, 128, 2, True)
+    assert flops / nbytes < bench.PEAK_BF16_TFLOPS * 1e12 / (bench.PEAK_HBM_GBPS * 1e9)
+    r = bench.prefill_roofline(nbytes, flops, flops_rec, 1.0, "prefill_chunked")
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s"
+    assert abs(r["frac"] - nbytes / 1e-3 / 8e12) < 1e-12
+    assert abs(r["mfma_frac"] - flops / 1e-3 / 2.5e15) < 1e-12
+    t = bench.prefill_roofline(nbytes, flops, flops_rec, 2.0, "prefill_recurrent")
+    assert t["bound"] == "alu" and "mfma_frac" not in t
+    assert abs(t["frac"] - flops_rec / 2e-3 / 157.3e12) < 1e-12
