@@ -5,7 +5,7 @@
 Every call goes through libgdn.so (include/gdn.h); there is no CPU fallback.
 """
 from .binding import (VARIANTS, BlockOps, GdnError, conv_silu, decode_step, gated_rmsnorm, load, prefill,
-                      prefill_kernel_name, prefill_workspace_size, version)
+                      prefill_kernel_name, prefill_noalloc, prefill_workspace_size, version)
 
 __all__ = ["VARIANTS", "BlockOps", "GdnError", "conv_silu", "decode_step", "gated_rmsnorm", "load", "prefill",
-           "prefill_kernel_name", "prefill_workspace_size", "version"]
+           "prefill_kernel_name", "prefill_noalloc", "prefill_workspace_size", "version"]

@@ -76,6 +76,9 @@ def load() -> ctypes.CDLL:
     lib.gdn_prefill_ex.argtypes = [vp, vp, vp, fp, fp, vp, vp, i32, i64, fp, vp, fp, i32, i32, i32, i32,
                                    ctypes.c_int, ctypes.c_float, ctypes.c_int, ops_p, vp, sz, vp]
     lib.gdn_prefill_ex.restype = ctypes.c_int
+    lib.gdn_prefill_noalloc.argtypes = [vp, vp, vp, fp, fp, vp, vp, i32, i64, fp, vp, fp, i32, i32, i32, i32,
+                                        ctypes.c_int, ctypes.c_float, ctypes.c_int, ops_p, vp]
+    lib.gdn_prefill_noalloc.restype = ctypes.c_int
     lib.gdn_conv_silu.argtypes = [vp, vp, vp, vp, i32, i64, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                   ctypes.c_int, vp]
     lib.gdn_conv_silu.restype = ctypes.c_int
@@ -233,11 +236,24 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch
     variant and the block parts: as for decode_step (z is [total_T, HV, dv]).
     """
     return _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, N, S0, scale, o, S_T, output_state, workspace,
-                    variant, A_log, dt_bias, beta_logits, z, norm_w, norm_eps, alpha_sigmoid)
+                    variant, A_log, dt_bias, beta_logits, z, norm_w, norm_eps, alpha_sigmoid, noalloc=False)
+
+
+def prefill_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch.Tensor],
+                    beta: Optional[torch.Tensor], *, cu_seqlens: Optional[torch.Tensor] = None,
+                    cu_seqlens_host=None, N: Optional[int] = None, S0: Optional[torch.Tensor] = None,
+                    scale: float = 1.0, o: torch.Tensor, S_T: Optional[torch.Tensor] = None,
+                    variant="gated_delta", A_log=None, dt_bias=None, beta_logits: bool = False, z=None,
+                    norm_w=None, norm_eps: float = 1e-6,
+                    alpha_sigmoid: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """prefill through gdn_prefill_noalloc: the library's static device scratch stands in for
+    the workspace, so nothing is allocated (o and, if wanted, S_T are given by the caller)."""
+    return _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, N, S0, scale, o, S_T, False, None,
+                    variant, A_log, dt_bias, beta_logits, z, norm_w, norm_eps, alpha_sigmoid, noalloc=True)
 
 
 def _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, N, S0, scale, o, S_T, output_state, workspace,
-             variant, A_log, dt_bias, beta_logits, z, norm_w, norm_eps, alpha_sigmoid):
+             variant, A_log, dt_bias, beta_logits, z, norm_w, norm_eps, alpha_sigmoid, *, noalloc):
     total_T, HQK, dk = _dims(q, "q", 3)
     _, HV, dv = _dims(v, "v", 3)
     dev = q.device
@@ -272,7 +288,7 @@ def _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, N, S0, scale, o, S_T
     _need_opt(S_T, "S_T", torch.float32, (n_seq, HV, dk, dv), dev)
     lib = load()
     code = _dtype_code(q)
-    need = int(lib.gdn_prefill_workspace_size(n_seq, total_T, HQK, HV, dk, dv, code))
+    need = 0 if noalloc else int(lib.gdn_prefill_workspace_size(n_seq, total_T, HQK, HV, dk, dv, code))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if workspace is not None:
@@ -284,7 +300,9 @@ def _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, N, S0, scale, o, S_T
             _ptr(S0), _ptr(o), _ptr(S_T), HQK, HV, dk, dv, code, float(scale))
     ops = _block_ops(A_log, dt_bias, beta_logits, z, norm_w, norm_eps, v.dtype, alpha_sigmoid,
                      HV=HV, dv=dv, z_shape=(total_T, HV, dv), device=dev)
-    if ops is not None:
+    if noalloc:
+        _check(lib.gdn_prefill_noalloc(*args, var, None if ops is None else ctypes.byref(ops), _stream(q.device)))
+    elif ops is not None:
         _check(lib.gdn_prefill_ex(*args, var, ctypes.byref(ops), _ptr(workspace), ws_bytes,
                                   _stream(q.device)))
     elif var == GDN_GATED_DELTA:

@@ -7,8 +7,14 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "gdn.h"
 #include "kernels.hpp"
+
+// Maximum workspace of gdn_prefill_noalloc (see static_scratch below).
+static constexpr size_t kStaticScratchBytes = (size_t)24 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -206,13 +212,47 @@ gdn_status hip_status(hipError_t e, const char *what) {
     return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// The prefill behind gdn_prefill, gdn_prefill_v and gdn_prefill_ex.
+// Static scratch of the allocation-free prefill (gdn_prefill_noalloc): one array per device,
+// loaded with the library's code object and kept until the process ends.  In host code the
+// name `scratch` is only a stand-in for the symbol; its device address -- different on every
+// device -- comes from hipGetSymbolAddress, taken once per device at the entry point's first
+// call there, with that device current.  Nothing in the array has to start at zero: every
+// part of the workspace (launch order, segment maps, start tables) is written by an earlier
+// kernel of the same call before it is read.  Calls that overlap in time on one device share
+// the array and race.
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64] = {};
+
+gdn_status static_scratch(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(GDN_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..63", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(GDN_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GDN_OK;
+}
+
+// The prefill behind gdn_prefill_ex (workspace from the caller) and gdn_prefill_noalloc
+// (use_scratch: the workspace is the device's static scratch array, and workspace /
+// workspace_bytes are ignored).
 gdn_status run_prefill(const void *q, const void *k, const void *v, const float *g, const float *beta,
                        const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, int32_t N, int64_t total_T,
                        const float *S0, void *o, float *S_T, int32_t HQK, int32_t HV, int32_t dk, int32_t dv,
                        gdn_dtype dtype, float scale, gdn_variant variant, const gdn_block_ops *ops,
-                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
+                       void *workspace, size_t workspace_bytes, bool use_scratch, hipStream_t stream) {
     g_last_error[0] = 0;
+    if (use_scratch) {
+        workspace = nullptr;
+        workspace_bytes = 0;
+    }
     if (total_T < 0) return fail(GDN_ERR_SHAPE, "total_T = %lld is negative", (long long)total_T);
     gdn_status st = check_common(q, k, v, g, beta, o, N, HQK, HV, dk, dv, dtype, total_T, variant);
     if (st != GDN_OK) return st;
@@ -245,6 +285,19 @@ gdn_status run_prefill(const void *q, const void *k, const void *v, const float 
     }
     const WorkspacePlan plan = workspace_plan(N, total_T, HV, dk, dv, dtype);
     const size_t need = plan.total();
+    if (use_scratch) {
+        if (need > kStaticScratchBytes)
+            return fail(GDN_ERR_WORKSPACE,
+                        "these sizes need %zu bytes of workspace; the static scratch of "
+                        "gdn_prefill_noalloc holds %zu (call gdn_prefill_ex with a workspace instead)",
+                        need, kStaticScratchBytes);
+        if (N == 0) return GDN_OK;
+        if (need > 0) {
+            st = static_scratch(&workspace);
+            if (st != GDN_OK) return st;
+            workspace_bytes = kStaticScratchBytes;
+        }
+    }
     if (workspace_bytes < need)
         return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
     if (need > 0 && !workspace) return fail(GDN_ERR_NULL, "workspace must be non-NULL");
@@ -412,7 +465,17 @@ gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v, const flo
                           const gdn_block_ops *ops, void *workspace, size_t workspace_bytes,
                           hipStream_t stream) {
     return run_prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, N, total_T, S0, o, S_T, HQK, HV, dk, dv,
-                       dtype, scale, variant, ops, workspace, workspace_bytes, stream);
+                       dtype, scale, variant, ops, workspace, workspace_bytes, false, stream);
+}
+
+gdn_status gdn_prefill_noalloc(const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const int32_t *cu_seqlens,
+                               const int32_t *cu_seqlens_host, int32_t N, int64_t total_T,
+                               const float *S0, void *o, float *S_T, int32_t HQK, int32_t HV,
+                               int32_t dk, int32_t dv, gdn_dtype dtype, float scale,
+                               gdn_variant variant, const gdn_block_ops *ops, hipStream_t stream) {
+    return run_prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, N, total_T, S0, o, S_T, HQK, HV, dk, dv,
+                       dtype, scale, variant, ops, nullptr, 0, true, stream);
 }
 
 gdn_status gdn_conv_silu(const void *x, const float *w, const int32_t *cu_seqlens,

@@ -265,6 +265,30 @@ gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v, const flo
                           hipStream_t stream);
 
 /*
+ * gdn_prefill_noalloc -- gdn_prefill_ex without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  It allocates nothing and calls no allocating
+ * routine: the workspace gdn_prefill_ex would take (launch order, and for small batches
+ * the split-sequence maps and start tables) lives in a static device array of 24 MiB,
+ * one per device, held from the library's load on that device until the process ends.
+ * Arguments, checks, results and errors are those of gdn_prefill_ex, bit for bit, plus:
+ *  - GDN_ERR_WORKSPACE when gdn_prefill_workspace_size() of these sizes exceeds 24 MiB
+ *    (on a 256-compute-unit device only some split batches of dv = 64 do: every
+ *    (sequence, head, 64 columns) count times segments is at most 256 there);
+ *  - GDN_ERR_HIP if the device address of the array cannot be obtained (taken once per
+ *    device, at the first call on it, with that device current).
+ * Every call on a device shares that device's array, and calls that overlap in time on
+ * one device (other streams, other host threads) race on it: serialise them.  The array
+ * keeps what the last call wrote; no part of it needs to start at zero.
+ */
+gdn_status gdn_prefill_noalloc(const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const int32_t *cu_seqlens,
+                               const int32_t *cu_seqlens_host, int32_t N, int64_t total_T,
+                               const float *S0, void *o, float *S_T, int32_t HQK, int32_t HV,
+                               int32_t dk, int32_t dv, gdn_dtype dtype, float scale,
+                               gdn_variant variant, const gdn_block_ops *ops, hipStream_t stream);
+
+/*
  * gdn_conv_silu -- the block's causal depthwise short convolution + SiLU, in front of the
  * scan (handbook page "7. Gated DeltaNet: the token-by-token recurrence": the block listing
  * and the parts table, row "in_proj_qkv + conv1d", with the note under the table: the

@@ -550,3 +550,27 @@ def test_binding_conv_rejects_mis_shaped(name, shape):
     a[name] = _DevTensor(shape, a[name].dtype)
     with pytest.raises(ValueError, match=name):
         binding.conv_silu(t(T, Ct), a.pop("w"), HQK=HQK, HV=HV, dk=dk, dv=dv, N=N, **a)
+
+
+# ------------------------------------------------------------------ the allocation-free prefill
+def test_noalloc_rejects_workspace_beyond_its_scratch(lib):
+    """gdn_prefill_noalloc's static scratch holds 24 MiB: a split batch of dv = 64 that needs ~32 MB
+    is rejected with GDN_ERR_WORKSPACE before anything runs (the device count here is taken as 256
+    compute units), and N = 0 is a no-op that touches no device."""
+    T, H, dk, dv = 16384, 16, 128, 64
+    assert lib.gdn_prefill_workspace_size(1, T, H, H, dk, dv, 0) > 24 << 20
+    q = np.full(T * H * dk // 2 + 16, 7.0, np.float32)      # bf16 sizes, in floats
+    k = np.full_like(q, 7.0)
+    v = np.full(T * H * dv // 2 + 16, 7.0, np.float32)
+    o = np.full_like(v, 7.0)
+    g = np.full(T * H + 16, 7.0, np.float32)
+    b = np.full_like(g, 7.0)
+    p = lambda a: ctypes.c_void_p(a.ctypes.data)
+    st = lib.gdn_prefill_noalloc(p(q), p(k), p(v), p(g), p(b), None, None, 1, T, None, p(o), None, H, H, dk, dv,
+                                 0, 1.0, 0, None, None)
+    assert st == E_WS, lib.gdn_last_error()
+    assert b"static scratch" in lib.gdn_last_error()
+    z = np.zeros(1, np.int32)
+    assert lib.gdn_prefill_noalloc(None, None, None, None, None, p(z), p(z), 0, 0, None, None, None, H, H, dk, dv,
+                                   0, 1.0, 0, None, None) == OK
+    assert all(np.all(a == 7.0) for a in (q, k, v, o, g, b))
