@@ -47,11 +47,13 @@
 //    and T_0, T_1 into LDS already in that MFMA operand order (computing a Gram
 //    tile with the two operand roles swapped yields it transposed, which is the
 //    operand order directly).
-// Two workgroup barriers per chunk, a two-stage pipeline: in phase a of chunk c the
-// column waves form K S, Q S and Z while the Gram waves stage chunk c + 1 into LDS; in
-// phase b the column waves solve, write the reads and update the table while the Gram
-// waves build chunk c + 1's operands.  The next chunk's q, k, v, g, beta are fetched into
-// registers one chunk ahead.
+// One workgroup barrier per chunk, a two-stage pipeline: while the column waves run chunk c
+// (K S, Q S and Z, then the solve, the reads and the table update), the Gram waves stage
+// chunk c + 1 into LDS and then build its T (an LDS counter makes the building wait until
+// all four Gram waves have staged); the column waves, done with chunk c, build chunk c + 1's
+// P and -A_10 tiles.  Every buffer the two roles share is doubled by
+// chunk parity.  The next chunk's q, k, v, g, beta are fetched into registers one chunk
+// ahead.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -86,9 +88,12 @@ constexpr int SC_SZ = 10 * C;                              // fp32 per-token sca
 constexpr int OFF_SC = OFF_OP + 2 * OP_SZ;                 // [2]
 constexpr int OFF_FLAG = OFF_SC + 2 * SC_SZ * 4;           // two int hand-over counters
 constexpr int LDS_BYTES = OFF_FLAG + 16;
-// The 16x16 tiles W_b = A_10 T_00 of the two 32-token blocks are handed from one Gram wave
-// to another through the K/Q buffer of the other parity, which nobody reads meanwhile.
-static_assert(2 * 64 * 16 <= KQ_SZ, "hand-over tiles fit in one K/Q buffer");
+// The diagonal 16-blocks of A and of their inverses are handed from one Gram wave to
+// another through the K/Q buffer of the other parity, which nobody reads during phase b:
+// four 16 x 16 fp32 blocks each, at a stride of DSTR floats (272 = 256 + 16, so the blocks'
+// rows fall in different LDS banks).
+constexpr int DSTR = 272;
+static_assert(2 * 4 * DSTR * 4 <= KQ_SZ, "hand-over blocks fit in one K/Q buffer");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -174,6 +179,10 @@ __device__ __forceinline__ float row16_sum(float x) {
     x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
     return x;
 }
+
+// Every lambda of the kernel is inlined: an outlined call would save and restore registers
+// around it and serialise its latency.
+#define GDN_INLINE __attribute__((always_inline))
 
 // A copy of x the compiler cannot see through: lane-dependent addresses derived from
 // it are recomputed inside the chunk loop instead of being hoisted out and spilled.
@@ -288,13 +297,106 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     }
 
     const int nchunks = (int)((t1 - t0 + C - 1) / C);
-    auto chunk_len = [&](int c) { return (int)((t1 - t0 - (int64_t)c * C) < C ? (t1 - t0 - (int64_t)c * C) : C); };
+    if (tid == 0) {
+        int *fl = reinterpret_cast<int *>(lds + OFF_FLAG);
+        fl[0] = 0;
+        fl[1] = 0;
+    }
+    __syncthreads();  // counters cleared before any wave uses them
+    auto chunk_len = [&](int c) GDN_INLINE { return (int)((t1 - t0 - (int64_t)c * C) < C ? (t1 - t0 - (int64_t)c * C) : C); };
 
     // Schedule.  Phase "a" of chunk c: column waves form K S, Q S and Z of chunk c while
     // the Gram waves stage chunk c+1 into LDS.  Phase "b" of chunk c: column waves solve,
     // write the reads and update the table while the Gram waves build T, -A_10 and P of
     // chunk c+1.  One workgroup barrier closes every phase; a prologue stages chunk 0,
     // builds its operands (beside the column waves' phase a of chunk 0) and stages chunk 1.
+    // LDS counters: the last chunk whose T_00, T_11 are in LDS, per 32-token block
+    int *flag = reinterpret_cast<int *>(lds + OFF_FLAG);
+    // The operand tiles of chunk c built from its Gram tiles alone: the read operands P and
+    // the coupling -A_10 of the two 32-token blocks.
+    //
+    // P operand idx = (rt, ks), ks <= rt / 2:  0 (0,0) 1 (1,0) 2 (2,0) 3 (2,1) 4 (3,0) 5 (3,1).
+    // Tile (rt, kt) from MFMA(K block kt, Q block rt): element e at lane is
+    // (Q K^T)[16 rt + lr][16 kt + 4 lq + e], the tile-order operand slot.
+    auto p_operand = [&](int c, int idx) GDN_INLINE {
+        const int ln = opaque(lane);
+        const int lrr = ln & 15, lqq = ln >> 4;
+        GDN_CHUNK(c)
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        auto load_blk = [&](const __bf16 *base, int kb, bf16x8 *dst) GDN_INLINE {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) dst[ks] = ld_std(base, LK, 16 * kb, 32 * ks, ln);
+        };
+        const int rt = idx == 0 ? 0 : (idx == 1 ? 1 : (idx < 4 ? 2 : 3));
+        const int ks = (idx == 3 || idx == 5) ? 1 : 0;
+        const int i = 16 * rt + lrr;
+        const float ci = sRq[i], Gi = sG[i];
+        bf16x8 qq[4];
+        load_blk(sQ, rt, qq);
+        f32x8 x;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int kt = 2 * ks + t;
+            if (kt > rt) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[4 * t + e] = 0.f;
+                continue;
+            }
+            bf16x8 kk[4];
+            load_blk(sK, kt, kk);
+            f32x4 acc = zero;
+#pragma unroll
+            for (int kq = 0; kq < 4; ++kq) acc = mfma32(kk[kq], qq[kq], acc);
+            const int j0 = 16 * kt + 4 * lqq;
+            const f32x4 R4 = *reinterpret_cast<const f32x4 *>(sRk + j0);
+            if (kt < rt) {  // every row after every column: split decays, no mask
+                const float cr = ci * sRF[kt * C + i];
+                const f32x4 CF4 = *reinterpret_cast<const f32x4 *>(sCF + j0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[4 * t + e] = cr * (R4[e] * CF4[e]) * acc[e];
+            } else {
+                const f32x4 G4 = *reinterpret_cast<const f32x4 *>(sG + j0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    x[4 * t + e] = (j0 + e <= i) ? ci * R4[e] * acc[e] * exp2_hw(Gi - G4[e]) : 0.f;
+            }
+        }
+        opP[idx * 64 + ln] = to_bf16(x);
+    };
+    // -A_10 (rows 32 + 16 rt .., columns 0..31) in tile order, from role-swapped Gram tiles
+    auto a_operand = [&](int c, int rt) GDN_INLINE {
+        const int ln = opaque(lane);
+        const int lrr = ln & 15, lqq = ln >> 4;
+        GDN_CHUNK(c)
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        auto load_blk = [&](const __bf16 *base, int kb, bf16x8 *dst) GDN_INLINE {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) dst[ks] = ld_std(base, LK, 16 * kb, 32 * ks, ln);
+        };
+        const int i = 32 + 16 * rt + lrr;
+        const float ci = sB[i] * sRk[i];
+        bf16x8 kr[4];
+        load_blk(sK, 2 + rt, kr);
+        f32x8 x;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            bf16x8 kk[4];
+            load_blk(sK, t, kk);
+            f32x4 acc = zero;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) acc = mfma32(kk[ks], kr[ks], acc);
+            const int j0 = 16 * t + 4 * lqq;
+            const f32x4 R4 = *reinterpret_cast<const f32x4 *>(sRk + j0);
+            const f32x4 CF4 = *reinterpret_cast<const f32x4 *>(sCF + j0);
+            const float cr = -ci * sRF[t * C + i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[4 * t + e] = cr * (R4[e] * CF4[e]) * acc[e];
+        }
+        bf16x8 hi, lo;
+        split(x, hi, lo);
+        opA[(rt * 2 + 0) * 64 + ln] = hi;
+        opA[(rt * 2 + 1) * 64 + ln] = lo;
+    };
     if (colwave) {
         // ====================== column waves: the table and the per-chunk chain ======
         // Element e of S[dt] is S[16 dt + 4 lq + e][col0 + 16 w + lr].
@@ -317,7 +419,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                 const int r = 16 * dt + 4 * lq + e;
                 S[dt][e] = Sin ? Sin[(size_t)r * DW + mycol] : ((SPLIT && mycol - DV == r) ? 1.f : 0.f);
             }
-        auto store_table = [&]() {
+        auto store_table = [&]() GDN_INLINE {
             if (Sout) {
 #pragma unroll
                 for (int dt = 0; dt < 8; ++dt)
@@ -341,7 +443,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         const bool vin = !SPLIT || col0 < DV;
         const bool reads = !SPLIT || mode != 1;  // the map pass forms no reads
         uint16_t *owave = o + (size_t)h * DV + col0 + 16 * wu;
-        auto prefetch_v = [&](int c) {
+        auto prefetch_v = [&](int c) GDN_INLINE {
             const int nn = chunk_len(c);
             const rsrc_t vr = make_rsrc(vwave + (size_t)(t0 + (int64_t)c * C) * vrs, vin ? (uint32_t)nn * rowb : 0u);
             const uint32_t off = 2u * (uint32_t)lr + (uint32_t)(4 * lq) * rowb;
@@ -368,7 +470,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         f32x4 Z[4], Ot[4];
 
         // ---- phase a: Y = K S (hi + lo), Z = beta (v - gamma r_k Y), O^T = S^T Q^T (hi)
-        auto phase_a = [&](int c) {
+        auto phase_a = [&](int c) GDN_INLINE {
             const int ln = opaque(lane);
             const int lqq = ln >> 4;
             GDN_CHUNK(c)
@@ -423,7 +525,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         };
 
         // ---- phase b: solve, reads, table update
-        auto phase_b = [&](int c) {
+        auto phase_b = [&](int c) GDN_INLINE {
             const int ln = opaque(lane);
             const int lrr = ln & 15, lqq = ln >> 4;
             const int64_t c0 = t0 + (int64_t)c * C;
@@ -562,13 +664,13 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     // token row of item (p, u) = 8 gw + 32 p + u (uniform) + 2 lq (lane)
     const int gwu = wu - 4;
     const uint32_t qkrow = 2u * (uint32_t)rs;  // bytes per token row of q and k
-    auto prefetch_qk = [&](int c) {
+    auto prefetch_qk = [&](int c) GDN_INLINE {
         const int nn = chunk_len(c);
         const int64_t cs = t0 + (int64_t)c * C;
         const rsrc_t kr = make_rsrc(k + (size_t)cs * rs + (size_t)hq * DK, (uint32_t)nn * qkrow);
         const rsrc_t qr = make_rsrc(q + (size_t)cs * rs + (size_t)hq * DK, (uint32_t)nn * qkrow);
         const uint32_t off = (uint32_t)(2 * lq) * qkrow + 16u * (uint32_t)lr;
-        auto ld = [&](const rsrc_t &r, int p, int u) {
+        auto ld = [&](const rsrc_t &r, int p, int u) GDN_INLINE {
             return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                                  r, off, (uint32_t)(8 * gwu + 32 * p + u) * qkrow, 0));
         };
@@ -615,7 +717,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     };
 
     // chunk c's q, k, g, beta (already in registers) -> LDS, norms, cumulative decay
-    auto stage_chunk = [&](int c) {
+    auto stage_chunk = [&](int c) GDN_INLINE {
         GDN_CHUNK(c)
         const int ln = opaque(lane);
         const int gtt = opaque(gt);
@@ -713,143 +815,32 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     // index on both sides), so every product below keeps a matrix and its transpose.
     // Waves 0 and 2 also form W = A_10 T_00 of their 32-block and hand it to waves 1 and 3,
     // which finish the block.  The hand-over counter holds the last chunk whose W is in LDS.
-    int *flag = reinterpret_cast<int *>(lds + OFF_FLAG);
-    auto build_operands = [&](int c) {
+    auto build_operands = [&](int c) GDN_INLINE {
         const int ln = opaque(lane);
         const int lrr = ln & 15, lqq = ln >> 4;
         GDN_CHUNK(c)
-        f32x4 *Wbuf = reinterpret_cast<f32x4 *>(lds + OFF_KQ + (par_ ^ 1) * KQ_SZ);  // [2 b][64]
-        const int blk = gwu;
+        // the diagonal 16-blocks of A and of T = (I + A)^{-1}, fp32, handed between Gram waves
+        float *Adiag = reinterpret_cast<float *>(lds + OFF_KQ + (par_ ^ 1) * KQ_SZ);  // [4][DSTR]
+        float *Tdiag = Adiag + 4 * DSTR;                                             // [4][DSTR]
         const int b = gwu >> 1;
-        const bool first = (gwu & 1) == 0;
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        auto load_blk = [&](const __bf16 *base, int kb, bf16x8 *dst) {
+        auto load_blk = [&](const __bf16 *base, int kb, bf16x8 *dst) GDN_INLINE {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) dst[ks] = ld_std(base, LK, 16 * kb, 32 * ks, ln);
-        };
-        // P operand idx = (rt, ks), ks <= rt / 2:  0 (0,0) 1 (1,0) 2 (2,0) 3 (2,1) 4 (3,0) 5 (3,1).
-        // Tile (rt, kt) from MFMA(K block kt, Q block rt): element e at lane is
-        // (Q K^T)[16 rt + lr][16 kt + 4 lq + e], the tile-order operand slot.
-        auto p_operand = [&](int idx) {
-            const int rt = idx == 0 ? 0 : (idx == 1 ? 1 : (idx < 4 ? 2 : 3));
-            const int ks = (idx == 3 || idx == 5) ? 1 : 0;
-            const int i = 16 * rt + lrr;
-            const float ci = sRq[i], Gi = sG[i];
-            bf16x8 qq[4];
-            load_blk(sQ, rt, qq);
-            f32x8 x;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int kt = 2 * ks + t;
-                if (kt > rt) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) x[4 * t + e] = 0.f;
-                    continue;
-                }
-                bf16x8 kk[4];
-                load_blk(sK, kt, kk);
-                f32x4 acc = zero;
-#pragma unroll
-                for (int kq = 0; kq < 4; ++kq) acc = mfma32(kk[kq], qq[kq], acc);
-                const int j0 = 16 * kt + 4 * lqq;
-                const f32x4 R4 = *reinterpret_cast<const f32x4 *>(sRk + j0);
-                if (kt < rt) {  // every row after every column: split decays, no mask
-                    const float cr = ci * sRF[kt * C + i];
-                    const f32x4 CF4 = *reinterpret_cast<const f32x4 *>(sCF + j0);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) x[4 * t + e] = cr * (R4[e] * CF4[e]) * acc[e];
-                } else {
-                    const f32x4 G4 = *reinterpret_cast<const f32x4 *>(sG + j0);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        x[4 * t + e] = (j0 + e <= i) ? ci * R4[e] * acc[e] * exp2_hw(Gi - G4[e]) : 0.f;
-                }
-            }
-            opP[idx * 64 + ln] = to_bf16(x);
-        };
-        // -A_10 (rows 32 + 16 rt .., columns 0..31) in tile order, from role-swapped Gram tiles
-        auto a_operand = [&](int rt) {
-            const int i = 32 + 16 * rt + lrr;
-            const float ci = sB[i] * sRk[i];
-            bf16x8 kr[4];
-            load_blk(sK, 2 + rt, kr);
-            f32x8 x;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                bf16x8 kk[4];
-                load_blk(sK, t, kk);
-                f32x4 acc = zero;
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) acc = mfma32(kk[ks], kr[ks], acc);
-                const int j0 = 16 * t + 4 * lqq;
-                const f32x4 R4 = *reinterpret_cast<const f32x4 *>(sRk + j0);
-                const f32x4 CF4 = *reinterpret_cast<const f32x4 *>(sCF + j0);
-                const float cr = -ci * sRF[t * C + i];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) x[4 * t + e] = cr * (R4[e] * CF4[e]) * acc[e];
-            }
-            bf16x8 hi, lo;
-            split(x, hi, lo);
-            opA[(rt * 2 + 0) * 64 + ln] = hi;
-            opA[(rt * 2 + 1) * 64 + ln] = lo;
         };
         // Products on bf16 MFMA with hi/lo operands.  Y and X in accumulator form split into
         // bf16 (hi, lo); one 16x16x32 MFMA with A = (Yh, Yh) and B = (Xh, Xl) gives
         // Yh^T Xh + Yh^T Xl, a second with A = (Yl, 0) adds Yl^T Xh.
-        auto hl = [&](const f32x4 &x, bf16x4 &h, bf16x4 &l) { split4(x, h, l); };
-        auto prod3 = [&](const bf16x4 &yh, const bf16x4 &yl, const bf16x4 &xh, const bf16x4 &xl, f32x4 acc) {
+        auto hl = [&](const f32x4 &x, bf16x4 &h, bf16x4 &l) GDN_INLINE { split4(x, h, l); };
+        auto prod3 = [&](const bf16x4 &yh, const bf16x4 &yl, const bf16x4 &xh, const bf16x4 &xl, f32x4 acc) GDN_INLINE {
             const bf16x4 z4 = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
             const bf16x8 bx = cat(xh, xl);
             acc = mfma32(cat(yh, yh), bx, acc);
             return mfma32(cat(yl, z4), bx, acc);
         };
-        // Inverse T of the diagonal 16-block and its transpose, as accumulator tiles.
-        auto invert_block = [&](f32x4 &T, f32x4 &Tt, bf16x8 *kd) {
-            load_blk(sK, blk, kd);
-            f32x4 gd = zero;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) gd = mfma32(kd[ks], kd[ks], gd);
-            // A and A^T from the symmetric Gram tile: element e is local row i = 4 lq + e,
-            // column j = lr; exactly one of A[i][j], A[j][i] is nonzero off the diagonal.
-            const int i0 = 16 * blk + 4 * lqq;
-            const int jj = 16 * blk + lrr;
-            const f32x4 G4 = *reinterpret_cast<const f32x4 *>(sG + i0);
-            const f32x4 B4 = *reinterpret_cast<const f32x4 *>(sB + i0);
-            const f32x4 R4 = *reinterpret_cast<const f32x4 *>(sRk + i0);
-            const float Gj = sG[jj], Bj = sB[jj], Rj = sRk[jj];
-            f32x4 Am;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 4 * lqq + e, j = lrr;
-                const float d = G4[e] - Gj;
-                const float f = R4[e] * Rj * gd[e] * exp2_hw(j < i ? d : -d);
-                Am[e] = j < i ? B4[e] * f : 0.f;
-                const float amt = j > i ? Bj * f : 0.f;  // A[j][i]
-                // s = 1: 2x2 blocks [[1, 0], [-a, 1]]
-                T[e] = (i == j) ? 1.f : (((i ^ j) == 1) ? -Am[e] : 0.f);
-                Tt[e] = (i == j) ? 1.f : (((i ^ j) == 1) ? -amt : 0.f);
-            }
-#pragma unroll
-            for (int sl = 2; sl <= 8; sl <<= 1) {
-                f32x4 Ao;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int x = (4 * lqq + e) ^ lrr;
-                    Ao[e] = (x >= sl && x < 2 * sl) ? Am[e] : 0.f;
-                }
-                bf16x4 aoh, aol, tth, ttl, th, tl, uh, ul;
-                hl(Ao, aoh, aol);
-                hl(Tt, tth, ttl);
-                hl(T, th, tl);
-                const f32x4 Ut = prod3(aoh, aol, tth, ttl, zero);  // (T A_s)^T
-                hl(Ut, uh, ul);
-                T = T - prod3(uh, ul, th, tl, zero);    // T - (T A_s) T
-                Tt = Tt - prod3(th, tl, uh, ul, zero);  // its transpose
-            }
-        };
         // Row tile rt of T_b as a tile-order (hi, lo) operand: 8 values at lane (g, i) are
         // T_b[16 rt + i][4 g + e] (first 16 columns) and T_b[16 rt + i][16 + 4 g + e].
-        auto put_t = [&](int rt, const f32x4 &left_t, const f32x4 &right_t) {
+        auto put_t = [&](int rt, const f32x4 &left_t, const f32x4 &right_t) GDN_INLINE {
             bf16x8 hi, lo;
             split(cat(left_t, right_t), hi, lo);
             opT[((2 * b + rt) * 2 + 0) * 64 + ln] = hi;
@@ -858,24 +849,97 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
 
         if constexpr (!DELTA) {
             // no look-up: only P and r_k exp(G_n - G) are needed
-            if (b == 0) {
-                p_operand(first ? 0 : 2);
-                if (first) p_operand(1);
-                else sDn[ln] = sRk[ln] * exp2_hw(sG[C - 1] - sG[ln]);
+            if (gwu == 0) {
+                p_operand(c, 0);
+                p_operand(c, 1);
+            } else if (gwu == 1) {
+                p_operand(c, 2);
+                sDn[ln] = sRk[ln] * exp2_hw(sG[C - 1] - sG[ln]);
+            } else if (gwu == 2) {
+                p_operand(c, 3);
+                p_operand(c, 4);
             } else {
-                p_operand(first ? 3 : 5);
-                if (first) p_operand(4);
+                p_operand(c, 5);
             }
-        } else if (first) {
+        } else if ((gwu & 1) != 0) {
+            // waves 1 and 3: the two diagonal 16-blocks T_00, T_11 of the 32-token block b = gwu / 2
+            // of T = (I + A)^{-1}, by forward substitution in fp32, for wave gwu - 1 to merge; then
+            // one coupling tile -A_10 of the two 32-token blocks.
             __builtin_amdgcn_s_setprio(2);
-            f32x4 T, Tt;
-            bf16x8 kd[4];
-            invert_block(T, Tt, kd);
-            put_t(0, Tt, zero);
-            // W = A_10 T_00 = (A_10^T)^T T_00.  A_10^T from the role-swapped Gram tile of
-            // blocks (blk, blk + 1): element e is A[16 (blk+1) + lr][16 blk + 4 lq + e].
+            const int blk = 2 * b;
+            float *Ad = Adiag + b * 2 * DSTR;  // this block pair of A, then of T
+            float *Td = Tdiag + b * 2 * DSTR;
             {
-                bf16x8 kn[4];
+                // Gram tiles of the two diagonal blocks, written as rows of A: the tile is
+                // symmetric, so lane (g, j) holds row j at columns 4 g .. 4 g + 3, and
+                // A[j][m] = b_j r_k,j r_k,m (K K^T)_jm exp(G_j - G_m) for m < j
+                bf16x8 kd[4], kn[4];
+                load_blk(sK, blk, kd);
+                load_blk(sK, blk + 1, kn);
+                f32x4 g0 = zero, g1 = zero;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    g0 = mfma32(kd[ks], kd[ks], g0);
+                    g1 = mfma32(kn[ks], kn[ks], g1);
+                }
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb) {
+                    const int t0b = 16 * (blk + hb);
+                    const f32x4 gd = hb ? g1 : g0;
+                    const int tj = t0b + lrr;
+                    const float cj = sB[tj] * sRk[tj], Gj = sG[tj];
+                    const f32x4 R4 = *reinterpret_cast<const f32x4 *>(sRk + t0b + 4 * lqq);
+                    const f32x4 G4 = *reinterpret_cast<const f32x4 *>(sG + t0b + 4 * lqq);
+                    f32x4 a;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        a[e] = (4 * lqq + e < lrr) ? cj * R4[e] * gd[e] * exp2_hw(Gj - G4[e]) : 0.f;
+                    *reinterpret_cast<f32x4 *>(Ad + hb * DSTR + 16 * lrr + 4 * lqq) = a;
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            {
+                // Lane (hb, fj) (lanes 32-63 repeat lanes 0-31) solves (I + A_hb) x = e_fj: x is
+                // column fj of T_hb.  The whole block of A is read first, so the reads are in
+                // flight together; row i needs x_m for m < i, the newest, x_{i-1}, last.
+                const int hb = (ln >> 4) & 1, fj = ln & 15;
+                const float *Ab = Ad + hb * DSTR;
+                f32x4 arow[15][4];
+#pragma unroll
+                for (int i = 1; i < 16; ++i)
+#pragma unroll
+                    for (int q4 = 0; q4 < (i + 3) / 4; ++q4)
+                        arow[i - 1][q4] = *reinterpret_cast<const f32x4 *>(Ab + 16 * i + 4 * q4);
+                float x[16];
+#pragma unroll
+                for (int m = 0; m < 16; ++m) x[m] = (m == fj) ? 1.f : 0.f;
+#pragma unroll
+                for (int i = 1; i < 16; ++i) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int m = 0; m < i; ++m) acc = fmaf(arow[i - 1][m >> 2][m & 3], x[m], acc);
+                    x[i] = (i > fj) ? -acc : x[i];
+                }
+                if (ln < 32) {
+                    float *Tb = Td + hb * DSTR;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) Tb[16 * i + fj] = x[i];
+                }
+            }
+            __hip_atomic_store(flag + b, c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __builtin_amdgcn_s_setprio(0);
+            a_operand(c, b);
+        } else {
+            // waves 0 and 2: read operands P and, for the 32-token block b = gwu / 2, the coupling
+            // T_10 = -T_11 A_10 T_00 on MFMA through W = A_10 T_00, once wave gwu + 1 has solved
+            // T_00 and T_11.
+            const int blk = 2 * b;
+            // A_10^T from the role-swapped Gram tile of blocks (2 b, 2 b + 1): element e at lane
+            // (g, j) is A[16 (blk+1) + j][16 blk + 4 g + e]
+            f32x4 At;
+            {
+                bf16x8 kd[4], kn[4];
+                load_blk(sK, blk, kd);
                 load_blk(sK, blk + 1, kn);
                 f32x4 gx = zero;
 #pragma unroll
@@ -885,39 +949,21 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                 const f32x4 R4 = *reinterpret_cast<const f32x4 *>(sRk + i0);
                 const f32x4 CF4 = *reinterpret_cast<const f32x4 *>(sCF + i0);
                 const float cr = sB[r] * sRk[r] * sRF[blk * C + r];
-                f32x4 At;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) At[e] = cr * (R4[e] * CF4[e]) * gx[e];
-                bf16x4 ah, al, th, tl;
-                hl(At, ah, al);
-                hl(T, th, tl);
-                Wbuf[b * 64 + ln] = prod3(ah, al, th, tl, zero);
-                __hip_atomic_store(flag + b, c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
-            __builtin_amdgcn_s_setprio(0);
             if (b == 0) {
-                p_operand(0);
-                p_operand(1);
+                p_operand(c, 0);
+                p_operand(c, 1);
+                p_operand(c, 3);
             } else {
-                p_operand(3);
-                p_operand(4);
-            }
-        } else {
-            if (b == 0) {
-                p_operand(2);
-                a_operand(0);
+                p_operand(c, 2);
+                p_operand(c, 4);
+                p_operand(c, 5);
                 sDn[ln] = sRk[ln] * exp2_hw(sG[C - 1] - sG[ln]);
-            } else {
-                p_operand(5);
-                a_operand(1);
             }
-            __builtin_amdgcn_s_setprio(2);
-            f32x4 T, Tt;
-            bf16x8 kd[4];
-            invert_block(T, Tt, kd);
-            // wait for W of this chunk (bounded: the partner wave writes it unconditionally).  A
-            // wait that gave up would leave a stale W in the buffer: the block is then poisoned
-            // with NaN, so the failure shows in every read and table it reaches.
+            // wait for T_00 and T_11 of this chunk (bounded: the solving wave writes them
+            // unconditionally; a wait that gave up poisons the block with NaN)
             bool handed = false;
             for (int spin = 0; spin < (1 << 22); ++spin) {
                 if (__hip_atomic_load(flag + b, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) > c) {
@@ -926,21 +972,36 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                 }
                 __builtin_amdgcn_s_sleep(1);
             }
-            const f32x4 W = handed ? Wbuf[b * 64 + ln] : f32x4{NAN, NAN, NAN, NAN};
+            // T_00 in accumulator form (element e at lane (g, j) = T[4 g + e][j]) and T_00^T, T_11^T
+            // (element e at lane (g, j) = T[j][4 g + e])
+            const float *T0 = Tdiag + b * 2 * DSTR, *T1 = T0 + DSTR;
+            f32x4 T00, Tt00, Tt11;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) T00[e] = T0[16 * (4 * lqq + e) + lrr];
+            Tt00 = *reinterpret_cast<const f32x4 *>(T0 + 16 * lrr + 4 * lqq);
+            Tt11 = *reinterpret_cast<const f32x4 *>(T1 + 16 * lrr + 4 * lqq);
+            if (!handed) {
+                const f32x4 nan4 = {NAN, NAN, NAN, NAN};
+                T00 = nan4;
+                Tt00 = nan4;
+                Tt11 = nan4;
+            }
+            bf16x4 ah, al, th, tl;
+            hl(At, ah, al);
+            hl(T00, th, tl);
+            const f32x4 W = prod3(ah, al, th, tl, zero);  // A_10 T_00
             // T_10^T = -(T_11 W)^T = -W^T T_11^T
-            bf16x4 wh, wl, th, tl;
+            bf16x4 wh, wl;
             hl(W, wh, wl);
-            hl(Tt, th, tl);
+            hl(Tt11, th, tl);
             const f32x4 T10t = -prod3(wh, wl, th, tl, zero);
-            put_t(1, T10t, Tt);
-            __builtin_amdgcn_s_setprio(0);
+            put_t(0, Tt00, zero);
+            put_t(1, T10t, Tt11);
         }
     };
 
-    if (gt == 0) {
-        flag[0] = 0;
-        flag[1] = 0;
-    }
+    // the Gram waves stage a chunk between them, then build its operands: each counts the
+    // staged chunks in LDS and waits (bounded) until all four have staged this one
     prefetch_qk(0);
     stage_chunk(0);
     if (nchunks > 1) prefetch_qk(1);
