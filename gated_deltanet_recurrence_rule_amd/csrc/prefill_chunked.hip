@@ -72,28 +72,25 @@ constexpr int DVS = 64;     // dv columns per workgroup
 constexpr int NT = 512;     // threads (8 waves)
 
 constexpr int LK = DK + 8;  // row stride (bf16) of K and Q in LDS
-constexpr int LT = C + 8;   // row stride (bf16) of K^T in LDS
 
 // LDS layout (bytes).  Buffers tagged [2] are selected by chunk parity.
 constexpr int KQ_SZ = 2 * C * LK * 2;                      // K then Q, [C][LK] bf16 each, rows = tokens
 constexpr int OFF_KQ = 0;                                  // [2]
-constexpr int KT_SZ = DK * LT * 2;                         // K^T [DK][LT], swizzled
-constexpr int OFF_KT = OFF_KQ + 2 * KQ_SZ;                 // [2]
 constexpr int OPT_SZ = 2 * 2 * 2 * 64 * 16;                // T_b operands [2 b][2 rt][2 hi/lo][64][8]
 constexpr int OPA_SZ = 2 * 2 * 64 * 16;                    // -A_10 operands [2 rt][2 hi/lo][64][8]
 constexpr int OPP_SZ = 6 * 64 * 16;                        // P operands [6 (rt, ks)][64][8]
 constexpr int OP_SZ = OPT_SZ + OPA_SZ + OPP_SZ;
-constexpr int OFF_OP = OFF_KT + 2 * KT_SZ;                 // [2]
+constexpr int OFF_OP = OFF_KQ + 2 * KQ_SZ;                 // [2]
 constexpr int SC_SZ = 10 * C;                              // fp32 per-token scalars of one chunk
 constexpr int OFF_SC = OFF_OP + 2 * OP_SZ;                 // [2]
 constexpr int OFF_FLAG = OFF_SC + 2 * SC_SZ * 4;           // two int hand-over counters
 constexpr int LDS_BYTES = OFF_FLAG + 16;
 // The diagonal 16-blocks of A and of their inverses are handed from one Gram wave to
-// another through the K/Q buffer of the other parity, which nobody reads during phase b:
-// four 16 x 16 fp32 blocks each, at a stride of DSTR floats (272 = 256 + 16, so the blocks'
-// rows fall in different LDS banks).
+// another through the Q rows of the other parity (the column waves read only that
+// parity's K rows during phase b): four 16 x 16 fp32 blocks each, at a stride of DSTR
+// floats (272 = 256 + 16, so the blocks' rows fall in different LDS banks).
 constexpr int DSTR = 272;
-static_assert(2 * 4 * DSTR * 4 <= KQ_SZ, "hand-over blocks fit in one K/Q buffer");
+static_assert(2 * 4 * DSTR * 4 <= KQ_SZ / 2, "hand-over blocks fit in one Q buffer");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -156,17 +153,25 @@ __device__ __forceinline__ bf16x8 ld_std(const __bf16 *base, int stride, int r0,
     return *reinterpret_cast<const bf16x8 *>(base + (r0 + (lane & 15)) * stride + k0 + 8 * (lane >> 4));
 }
 // Tile order inside every 32-element block: stored position 8g + 4t + e holds element
-// 16t + 4g + e.  K and Q rows (over d) and K^T rows (over tokens) are kept in LDS in
-// this order, so the 8 tile-order operand values of lane group g = lane/16 are one
-// contiguous 16-byte read (ld_std at k0 = 32 * block).  Gram products read both
+// 16t + 4g + e.  K and Q rows (over d) are kept in LDS in this order, so the 8 tile-order
+// operand values of lane group g = lane/16 are one contiguous 16-byte read (ld_std at
+// k0 = 32 * block); K^T operands (over tokens) come from the same K rows by two transposed
+// reads (ld_tr), every 4 consecutive d staying contiguous.  Gram products read both
 // operands in the same permuted order, which leaves them unchanged.
 __device__ __forceinline__ int tile_pos(int x) {
     const int r = x & 31;
     return (x & ~31) + 8 * ((r >> 2) & 3) + 4 * (r >> 4) + (r & 3);
 }
-// K^T bank swizzle: 8-element groups are permuted per 8-row band of K^T so that the
-// 16 lanes writing one token hit 16 different banks; groups of 8 stay contiguous.
-__device__ __forceinline__ int kt_col(int d, int pos) { return pos ^ (8 * ((d >> 3) & 7)); }
+// Transposed LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i
+// loads four 16-bit values A_i[0..3] from its own address, and lane j receives
+// A_{j/4}[j%4], A_{4+j/4}[j%4], A_{8+j/4}[j%4], A_{12+j/4}[j%4].  So when lane i points at
+// row r0 + i/4 and the four consecutive columns c0 + 4 (i%4) .. + 3 of a row-major bf16
+// matrix, lane j receives rows r0 .. r0 + 3 of column c0 + j: a column read from rows.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 ld_tr(const __bf16 *p) {
+    return __builtin_bit_cast(
+        bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p)));
+}
 
 // 2^x on the hardware exponential unit (flushes very negative x to zero).
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     const float *__restrict__ S0, uint16_t *__restrict__ o, float *__restrict__ S_T, int HV, int DV,
     int rep, int NG, int M, float scale, GateArgs gate, SplitArgs sp) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
-    // Everything belonging to chunk c lives in the buffers of parity c % 2: K and Q rows, K^T,
+    // Everything belonging to chunk c lives in the buffers of parity c % 2: K and Q rows,
     // the per-token scalars, and the solve / read operands built from them.  Scalars:
     // G (cumulative log-decay times log2 e), gamma = exp(G), r_k = 1/|k|, r_q = scale/|q|,
     // beta, r_k exp(G_n - G), and split decays.  With E_b = G at token 16 b + 15 (the end of
@@ -225,7 +230,6 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     const int par_ = (c) & 1;                                                               \
     __bf16 *sK = reinterpret_cast<__bf16 *>(lds + OFF_KQ + par_ * KQ_SZ);                   \
     __bf16 *sQ = sK + C * LK;                                                               \
-    __bf16 *sKt = reinterpret_cast<__bf16 *>(lds + OFF_KT + par_ * KT_SZ);                  \
     bf16x8 *opT = reinterpret_cast<bf16x8 *>(lds + OFF_OP + par_ * OP_SZ);                  \
     bf16x8 *opA = opT + OPT_SZ / 16;                                                        \
     bf16x8 *opP = opA + OPA_SZ / 16;                                                        \
@@ -233,7 +237,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     float *sG = sc_, *sGam = sc_ + C, *sRk = sc_ + 2 * C;                                   \
     float *sRq = sc_ + 3 * C, *sB = sc_ + 4 * C, *sDn = sc_ + 5 * C;                        \
     float *sCF = sc_ + 6 * C, *sRF = sc_ + 7 * C;                                           \
-    (void)sK; (void)sQ; (void)sKt; (void)opT; (void)opA; (void)opP;                         \
+    (void)sK; (void)sQ; (void)opT; (void)opA; (void)opP;                                    \
     (void)sG; (void)sGam; (void)sRk; (void)sRq; (void)sB; (void)sDn; (void)sCF; (void)sRF;
     // opT [((b*2 + rt)*2 + hl)*64 + lane], opA [(rt*2 + hl)*64 + lane], opP [idx*64 + lane]
 
@@ -611,14 +615,19 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) split(Dx[ks], Dh[ks], Dlo[ks]);
                 const float gam_n = sGam[C - 1];
+                // The A operand K^T (rows d = 16 dt + lr, tokens in tile order) is read from the K
+                // rows by two transposed reads: lane i of a group of 16 points at token row
+                // 32 ks + 16 t + 4 lq + i/4 and the d-quad 16 dt + 4 (i%4) (stored at tile
+                // position 32 (dt/2) + 8 (i%4) + 4 (dt%2)), so lane lr receives tokens
+                // 32 ks + 16 t + 4 lq .. + 3 of d = 16 dt + lr.
+                const __bf16 *ktp = sK + (4 * lqq + (lrr >> 2)) * LK + 8 * (lrr & 3);
 #pragma unroll
                 for (int dt = 0; dt < 8; ++dt) {
                     f32x4 acc = S[dt] * gam_n;
-                    const int d = 16 * dt + lrr;
-                    const __bf16 *rowp = sKt + d * LT;
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks) {
-                        const bf16x8 kt = *reinterpret_cast<const bf16x8 *>(rowp + kt_col(d, 32 * ks + 8 * lqq));
+                        const __bf16 *q0 = ktp + 32 * ks * LK + 32 * (dt >> 1) + 4 * (dt & 1);
+                        const bf16x8 kt = cat(ld_tr(q0), ld_tr(q0 + 16 * LK));
                         acc = mfma32(kt, Dh[ks], acc);
                         acc = mfma32(kt, Dlo[ks], acc);
                     }
@@ -748,17 +757,6 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                 sk[u] = a;
                 sq[u] = bq;
             }
-            // K^T: both tokens of the pair are adjacent in tile order -> one 4-byte write per d
-            const int tp = tile_pos(2 * pr);
-            const uint32_t k0w[4] = {kreg[p][0].x, kreg[p][0].y, kreg[p][0].z, kreg[p][0].w};
-            const uint32_t k1w[4] = {kreg[p][1].x, kreg[p][1].y, kreg[p][1].z, kreg[p][1].w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int d = 8 * sgs + e;
-                // low half: element e of token 2 pr, high half: element e of token 2 pr + 1
-                const uint32_t pair = __builtin_amdgcn_perm(k1w[e >> 1], k0w[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
-                *reinterpret_cast<uint32_t *>(sKt + d * LT + kt_col(d, tp)) = pair;
-            }
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 sk[u] = row16_sum(sk[u]);
@@ -820,7 +818,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         const int lrr = ln & 15, lqq = ln >> 4;
         GDN_CHUNK(c)
         // the diagonal 16-blocks of A and of T = (I + A)^{-1}, fp32, handed between Gram waves
-        float *Adiag = reinterpret_cast<float *>(lds + OFF_KQ + (par_ ^ 1) * KQ_SZ);  // [4][DSTR]
+        float *Adiag = reinterpret_cast<float *>(lds + OFF_KQ + (par_ ^ 1) * KQ_SZ + KQ_SZ / 2);  // [4][DSTR]
         float *Tdiag = Adiag + 4 * DSTR;                                             // [4][DSTR]
         const int b = gwu >> 1;
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
