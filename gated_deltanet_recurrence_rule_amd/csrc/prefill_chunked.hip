@@ -71,7 +71,10 @@ constexpr int DK = 128;     // key dimension
 constexpr int DVS = 64;     // dv columns per workgroup
 constexpr int NT = 512;     // threads (8 waves)
 
-constexpr int LK = DK + 8;  // row stride (bf16) of K and Q in LDS
+// Row stride (bf16) of K and Q in LDS.  Rows of 288 bytes let the operand reads of 16 rows
+// and the transposed reads of 16 rows run without bank conflicts (272-byte rows cost the
+// operand reads twice and the transposed reads three times as long on gfx950).
+constexpr int LK = DK + 16;
 
 // LDS layout (bytes).  Buffers tagged [2] are selected by chunk parity.
 constexpr int KQ_SZ = 2 * C * LK * 2;                      // K then Q, [C][LK] bf16 each, rows = tokens
@@ -87,9 +90,11 @@ constexpr int OFF_FLAG = OFF_SC + 2 * SC_SZ * 4;           // two int hand-over 
 constexpr int LDS_BYTES = OFF_FLAG + 16;
 // The diagonal 16-blocks of A and of their inverses are handed from one Gram wave to
 // another through the Q rows of the other parity (the column waves read only that
-// parity's K rows during phase b): four 16 x 16 fp32 blocks each, at a stride of DSTR
-// floats (272 = 256 + 16, so the blocks' rows fall in different LDS banks).
-constexpr int DSTR = 272;
+// parity's K rows during phase b): four 16 x 16 fp32 blocks each, rows of BR floats, at a
+// stride of DSTR floats.  With rows of 20, the 16 lanes that write or read 4 floats of 16
+// different rows hit 16 different groups of 4 banks.
+constexpr int BR = 20;
+constexpr int DSTR = 16 * BR + 16;
 static_assert(2 * 4 * DSTR * 4 <= KQ_SZ / 2, "hand-over blocks fit in one Q buffer");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
@@ -892,7 +897,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         a[e] = (4 * lqq + e < lrr) ? cj * R4[e] * gd[e] * exp2_hw(Gj - G4[e]) : 0.f;
-                    *reinterpret_cast<f32x4 *>(Ad + hb * DSTR + 16 * lrr + 4 * lqq) = a;
+                    *reinterpret_cast<f32x4 *>(Ad + hb * DSTR + BR * lrr + 4 * lqq) = a;
                 }
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -907,7 +912,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                 for (int i = 1; i < 16; ++i)
 #pragma unroll
                     for (int q4 = 0; q4 < (i + 3) / 4; ++q4)
-                        arow[i - 1][q4] = *reinterpret_cast<const f32x4 *>(Ab + 16 * i + 4 * q4);
+                        arow[i - 1][q4] = *reinterpret_cast<const f32x4 *>(Ab + BR * i + 4 * q4);
                 float x[16];
 #pragma unroll
                 for (int m = 0; m < 16; ++m) x[m] = (m == fj) ? 1.f : 0.f;
@@ -921,7 +926,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                 if (ln < 32) {
                     float *Tb = Td + hb * DSTR;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) Tb[16 * i + fj] = x[i];
+                    for (int i = 0; i < 16; ++i) Tb[BR * i + fj] = x[i];
                 }
             }
             __hip_atomic_store(flag + b, c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -975,9 +980,9 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             const float *T0 = Tdiag + b * 2 * DSTR, *T1 = T0 + DSTR;
             f32x4 T00, Tt00, Tt11;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) T00[e] = T0[16 * (4 * lqq + e) + lrr];
-            Tt00 = *reinterpret_cast<const f32x4 *>(T0 + 16 * lrr + 4 * lqq);
-            Tt11 = *reinterpret_cast<const f32x4 *>(T1 + 16 * lrr + 4 * lqq);
+            for (int e = 0; e < 4; ++e) T00[e] = T0[BR * (4 * lqq + e) + lrr];
+            Tt00 = *reinterpret_cast<const f32x4 *>(T0 + BR * lrr + 4 * lqq);
+            Tt11 = *reinterpret_cast<const f32x4 *>(T1 + BR * lrr + 4 * lqq);
             if (!handed) {
                 const f32x4 nan4 = {NAN, NAN, NAN, NAN};
                 T00 = nan4;
