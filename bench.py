@@ -97,6 +97,9 @@ def main():
                     help="skip the packed variable-length batch with its 262144-token sequence (by default "
                          "it is timed under extra_configs with the tiny fp32 scan and the single "
                          "8192-token sequence; its inputs take about half a minute to draw)")
+    ap.add_argument("--only", choices=["tiny_fp32", "single_8192", "varlen"], default=None,
+                    help="time only this one of the extra configurations and print its record (for a "
+                         "kernel trace of that workload alone; not the benchmark line)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run one 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -119,6 +122,11 @@ def main():
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    if args.only:
+        rec = extra_leg(args, binding, W, up, dev, legs=[args.only])
+        print(json.dumps({"only": args.only, "steps": args.steps, **rec[args.only]}), flush=True)
+        return
 
     t0 = time.time()
     pf = W.qwen3next()
@@ -311,14 +319,18 @@ def host_cpu():
     return None
 
 
-def extra_leg(args, binding, W, up, dev, with_varlen=False):
-    """The other workloads, each timed over K calls between HIP events after a short settle."""
+def extra_leg(args, binding, W, up, dev, with_varlen=False, legs=None):
+    """The other workloads, each timed over K calls between HIP events after a short settle
+    (all of them, or only those named in `legs`)."""
     import torch
 
     out = {}
     stream = torch.cuda.current_stream(dev)
-    legs = [("tiny_fp32", W.tiny), ("single_8192", W.prefill)] + ([("varlen", W.varlen)] if with_varlen else [])
-    for name, make in legs:
+    makers = {"tiny_fp32": W.tiny, "single_8192": W.prefill, "varlen": W.varlen}
+    if legs is None:
+        legs = ["tiny_fp32", "single_8192"] + (["varlen"] if with_varlen else [])
+    for name in legs:
+        make = makers[name]
         t0 = time.time()
         inp = make()
         log(f"{name}: inputs generated in {time.time() - t0:.1f} s")

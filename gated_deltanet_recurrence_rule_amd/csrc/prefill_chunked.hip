@@ -71,9 +71,9 @@ constexpr int DK = 128;     // key dimension
 constexpr int DVS = 64;     // dv columns per workgroup
 constexpr int NT = 512;     // threads (8 waves)
 
-// Row stride (bf16) of K and Q in LDS.  Rows of 288 bytes let the operand reads of 16 rows
-// and the transposed reads of 16 rows run without bank conflicts (272-byte rows cost the
-// operand reads twice and the transposed reads three times as long on gfx950).
+// Row stride (bf16) of K and Q in LDS.  With rows of 288 bytes the operand reads of 16 rows
+// run without bank conflicts, and the transposed reads at twice the conflict-free time;
+// 272-byte rows double both (measured on gfx950).
 constexpr int LK = DK + 16;
 
 // LDS layout (bytes).  Buffers tagged [2] are selected by chunk parity.
