@@ -641,13 +641,18 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             }
         };
 
+        // Column waves 0 and 2 also form the coupling operand -A_10 of the next chunk (row
+        // tile wu / 2) where they would otherwise wait for the Gram waves.
+        const bool couple = DELTA && (wu & 1) == 0;
         prefetch_v(0);
         __syncthreads();  // chunk 0 staged
         phase_a(0);
+        if (couple) a_operand(0, wu >> 1);
         __syncthreads();  // operands of chunk 0 built
         __syncthreads();  // chunk 1 staged
         for (int c = 0; c + 1 < nchunks; ++c) {
             phase_b(c);
+            if (couple) a_operand(c + 1, wu >> 1);
             __syncthreads();
             phase_a(c + 1);
             __syncthreads();
@@ -866,8 +871,8 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             }
         } else if ((gwu & 1) != 0) {
             // waves 1 and 3: the two diagonal 16-blocks T_00, T_11 of the 32-token block b = gwu / 2
-            // of T = (I + A)^{-1}, by forward substitution in fp32, for wave gwu - 1 to merge; then
-            // one coupling tile -A_10 of the two 32-token blocks.
+            // of T = (I + A)^{-1}, by forward substitution in fp32, for wave gwu - 1 to merge (the
+            // coupling operand -A_10 comes from column waves 0 and 2).
             __builtin_amdgcn_s_setprio(2);
             const int blk = 2 * b;
             float *Ad = Adiag + b * 2 * DSTR;  // this block pair of A, then of T
@@ -931,7 +936,6 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             }
             __hip_atomic_store(flag + b, c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
             __builtin_amdgcn_s_setprio(0);
-            a_operand(c, b);
         } else {
             // waves 0 and 2: read operands P and, for the 32-token block b = gwu / 2, the coupling
             // T_10 = -T_11 A_10 T_00 on MFMA through W = A_10 T_00, once wave gwu + 1 has solved
@@ -940,8 +944,8 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             // A_10^T from the role-swapped Gram tile of blocks (2 b, 2 b + 1): element e at lane
             // (g, j) is A[16 (blk+1) + j][16 blk + 4 g + e]
             f32x4 At;
+            bf16x8 kd[4], kn[4];  // K blocks blk and blk + 1
             {
-                bf16x8 kd[4], kn[4];
                 load_blk(sK, blk, kd);
                 load_blk(sK, blk + 1, kn);
                 f32x4 gx = zero;
@@ -955,15 +959,67 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) At[e] = cr * (R4[e] * CF4[e]) * gx[e];
             }
-            if (b == 0) {
-                p_operand(c, 0);
-                p_operand(c, 1);
-                p_operand(c, 3);
-            } else {
-                p_operand(c, 2);
-                p_operand(c, 4);
-                p_operand(c, 5);
-                sDn[ln] = sRk[ln] * exp2_hw(sG[C - 1] - sG[ln]);
+            // P operands idx = (rt, ks) hold tiles (rt, 2 ks) and (rt, 2 ks + 1): wave 0 forms
+            // idx 0, 1, 5 and wave 2 idx 2, 3, 4 (five nonzero tiles, 20 MFMAs each), every LDS
+            // read before the first store so that the reads are in flight together.  Register
+            // arrays are indexed by constants only (a wave-dependent index would move them to
+            // scratch memory).
+            {
+                auto gram = [&](const bf16x8 *x, const bf16x8 *y) GDN_INLINE {
+                    f32x4 acc = zero;
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) acc = mfma32(x[ks], y[ks], acc);
+                    return acc;
+                };
+                // P[16 rt + j][16 kt + 4 g + e] from (K Q^T) tile (kt, rt)
+                auto scale_p = [&](int rt, int kt, const f32x4 &acc) GDN_INLINE {
+                    const int i = 16 * rt + lrr;
+                    const float ci = sRq[i];
+                    const int j0 = 16 * kt + 4 * lqq;
+                    const f32x4 R4 = *reinterpret_cast<const f32x4 *>(sRk + j0);
+                    f32x4 x;
+                    if (kt < rt) {  // every row after every column: split decays, no mask
+                        const float cr = ci * sRF[kt * C + i];
+                        const f32x4 CF4 = *reinterpret_cast<const f32x4 *>(sCF + j0);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[e] = cr * (R4[e] * CF4[e]) * acc[e];
+                    } else {
+                        const float Gi = sG[i];
+                        const f32x4 G4 = *reinterpret_cast<const f32x4 *>(sG + j0);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            x[e] = (j0 + e <= i) ? ci * R4[e] * acc[e] * exp2_hw(Gi - G4[e]) : 0.f;
+                    }
+                    return x;
+                };
+                f32x8 xp[3];
+                if (b == 0) {
+                    bf16x8 k2[4], k3[4], q0[4], q1[4], q3[4];
+                    load_blk(sK, 2, k2);
+                    load_blk(sK, 3, k3);
+                    load_blk(sQ, 0, q0);
+                    load_blk(sQ, 1, q1);
+                    load_blk(sQ, 3, q3);
+                    xp[0] = cat(scale_p(0, 0, gram(kd, q0)), zero);
+                    xp[1] = cat(scale_p(1, 0, gram(kd, q1)), scale_p(1, 1, gram(kn, q1)));
+                    xp[2] = cat(scale_p(3, 2, gram(k2, q3)), scale_p(3, 3, gram(k3, q3)));
+                } else {
+                    bf16x8 k0[4], k1[4], q2[4], q3[4];
+                    load_blk(sK, 0, k0);
+                    load_blk(sK, 1, k1);
+                    load_blk(sQ, 2, q2);
+                    load_blk(sQ, 3, q3);
+                    xp[0] = cat(scale_p(2, 0, gram(k0, q2)), scale_p(2, 1, gram(k1, q2)));
+                    xp[1] = cat(scale_p(2, 2, gram(kd, q2)), zero);
+                    xp[2] = cat(scale_p(3, 0, gram(k0, q3)), scale_p(3, 1, gram(k1, q3)));
+                }
+                const float dn = sRk[ln] * exp2_hw(sG[C - 1] - sG[ln]);
+#pragma unroll
+                for (int u = 0; u < 3; ++u) {
+                    const int idx = b == 0 ? (u == 2 ? 5 : u) : 2 + u;
+                    opP[idx * 64 + ln] = to_bf16(xp[u]);
+                }
+                if (b == 1) sDn[ln] = dn;
             }
             // wait for T_00 and T_11 of this chunk (bounded: the solving wave writes them
             // unconditionally; a wait that gave up poisons the block with NaN)
