@@ -85,8 +85,8 @@ constexpr int OPP_SZ = 6 * 64 * 16;                        // P operands [6 (rt,
 constexpr int OP_SZ = OPT_SZ + OPA_SZ + OPP_SZ;
 constexpr int OFF_OP = OFF_KQ + 2 * KQ_SZ;                 // [2]
 constexpr int SC_SZ = 10 * C;                              // fp32 per-token scalars of one chunk
-constexpr int OFF_SC = OFF_OP + 2 * OP_SZ;                 // [2]
-constexpr int OFF_FLAG = OFF_SC + 2 * SC_SZ * 4;           // two int hand-over counters
+constexpr int OFF_SC = OFF_OP + 2 * OP_SZ;                 // [3], by chunk index mod 3
+constexpr int OFF_FLAG = OFF_SC + 3 * SC_SZ * 4;           // two int hand-over counters
 constexpr int LDS_BYTES = OFF_FLAG + 16;
 // The diagonal 16-blocks of A and of their inverses are handed from one Gram wave to
 // another through the Q rows of the other parity (the column waves read only that
@@ -224,8 +224,9 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     const float *__restrict__ S0, uint16_t *__restrict__ o, float *__restrict__ S_T, int HV, int DV,
     int rep, int NG, int M, float scale, GateArgs gate, SplitArgs sp) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
-    // Everything belonging to chunk c lives in the buffers of parity c % 2: K and Q rows,
-    // the per-token scalars, and the solve / read operands built from them.  Scalars:
+    // Chunk c's K and Q rows and the solve / read operands built from them live in the
+    // buffers of parity c % 2, its per-token scalars in buffer c % 3 (their gate part is
+    // formed a phase before the rest of the chunk is staged).  Scalars:
     // G (cumulative log-decay times log2 e), gamma = exp(G), r_k = 1/|k|, r_q = scale/|q|,
     // beta, r_k exp(G_n - G), and split decays.  With E_b = G at token 16 b + 15 (the end of
     // 16-token tile b): CF[t] = exp(E_{t/16} - G_t) and RF[b][t] = exp(G_t - E_b) for t past
@@ -238,7 +239,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     bf16x8 *opT = reinterpret_cast<bf16x8 *>(lds + OFF_OP + par_ * OP_SZ);                  \
     bf16x8 *opA = opT + OPT_SZ / 16;                                                        \
     bf16x8 *opP = opA + OPA_SZ / 16;                                                        \
-    float *sc_ = reinterpret_cast<float *>(lds + OFF_SC) + par_ * SC_SZ;                    \
+    float *sc_ = reinterpret_cast<float *>(lds + OFF_SC) + ((c) % 3) * SC_SZ;               \
     float *sG = sc_, *sGam = sc_ + C, *sRk = sc_ + 2 * C;                                   \
     float *sRq = sc_ + 3 * C, *sB = sc_ + 4 * C, *sDn = sc_ + 5 * C;                        \
     float *sCF = sc_ + 6 * C, *sRF = sc_ + 7 * C;                                           \
@@ -735,7 +736,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         }
     };
 
-    // chunk c's q, k, g, beta (already in registers) -> LDS, norms, cumulative decay
+    // chunk c's q and k (already in registers) -> LDS, and their norms
     auto stage_chunk = [&](int c) GDN_INLINE {
         GDN_CHUNK(c)
         const int ln = opaque(lane);
@@ -779,50 +780,57 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                 sRq[2 * pr + 1] = inv_norm(sq[1]) * scale;
             }
         }
-        if (gw == 3) {
-            // inclusive prefix sum over the 64 lanes: within rows of 16 by row shifts, then
-            // across rows by the row-15 and row-31 broadcasts (DPP, no LDS traffic)
-            // raw gates, straight-line so the staging above can hide them: softplus(+-t) =
-            // max(+-t, 0) + ln(1 + e^-|t|), log sigmoid(t) = -softplus(-t), and sigmoid(b) =
-            // 1 / (1 + e^-b) on the hardware exp2, log2 and reciprocal (when 1 + e^-|t| rounds
-            // to 1 the term dropped is < 6e-8)
-            const float tt = greg + g_dtb;
-            const float lt = 0.69314718055994531f * __builtin_amdgcn_logf(1.f + exp2_hw(-1.44269504088896341f * fabsf(tt)));
-            const float gl = g_raw ? (g_sig ? -(fmaxf(-tt, 0.f) + lt) : -g_ea * (fmaxf(tt, 0.f) + lt)) : greg;
-            breg = b_raw ? __builtin_amdgcn_rcpf(1.f + exp2_hw(-1.44269504088896341f * breg)) : breg;
-            float x = gl * 1.44269504088896341f;  // log2(e)
+    };
+
+    // Gram wave 3: chunk c's gates (already in registers, one token per lane) -> the
+    // cumulative log-decay G and the decay scalars derived from it, and beta.  Formed in the
+    // phase before chunk c is staged, where wave 3 has finished its own work early.
+    auto chunk_scalars = [&](int c) GDN_INLINE {
+        GDN_CHUNK(c)
+        const int ln = opaque(lane);
+        // raw gates on the hardware exp2, log2 and reciprocal: softplus(+-t) = max(+-t, 0) +
+        // ln(1 + e^-|t|), log sigmoid(t) = -softplus(-t), and sigmoid(b) = 1 / (1 + e^-b) (when
+        // 1 + e^-|t| rounds to 1 the term dropped is < 6e-8); then the inclusive prefix sum
+        // over the 64 lanes: within rows of 16 by row shifts, then across rows by the row-15
+        // and row-31 broadcasts (DPP, no LDS traffic)
+        const float tt = greg + g_dtb;
+        const float lt = 0.69314718055994531f * __builtin_amdgcn_logf(1.f + exp2_hw(-1.44269504088896341f * fabsf(tt)));
+        const float gl = g_raw ? (g_sig ? -(fmaxf(-tt, 0.f) + lt) : -g_ea * (fmaxf(tt, 0.f) + lt)) : greg;
+        breg = b_raw ? __builtin_amdgcn_rcpf(1.f + exp2_hw(-1.44269504088896341f * breg)) : breg;
+        float x = gl * 1.44269504088896341f;  // log2(e)
 #define GDN_DPP_ADD(ctrl, row_mask) \
     x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, row_mask, 0xF, true))
-            GDN_DPP_ADD(0x111, 0xF);  // row_shr:1
-            GDN_DPP_ADD(0x112, 0xF);  // row_shr:2
-            GDN_DPP_ADD(0x114, 0xF);  // row_shr:4
-            GDN_DPP_ADD(0x118, 0xF);  // row_shr:8
-            GDN_DPP_ADD(0x142, 0xA);  // row_bcast:15 into rows 1 and 3
-            GDN_DPP_ADD(0x143, 0xC);  // row_bcast:31 into rows 2 and 3
+        GDN_DPP_ADD(0x111, 0xF);  // row_shr:1
+        GDN_DPP_ADD(0x112, 0xF);  // row_shr:2
+        GDN_DPP_ADD(0x114, 0xF);  // row_shr:4
+        GDN_DPP_ADD(0x118, 0xF);  // row_shr:8
+        GDN_DPP_ADD(0x142, 0xA);  // row_bcast:15 into rows 1 and 3
+        GDN_DPP_ADD(0x143, 0xC);  // row_bcast:31 into rows 2 and 3
 #undef GDN_DPP_ADD
-            sG[ln] = x;
-            sGam[ln] = exp2_hw(x);
-            sB[ln] = breg;
-            const float E0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 15));
-            const float E1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 31));
-            const float E2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 47));
-            const float E3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
-            const int tb = ln >> 4;
-            sCF[ln] = exp2_hw((tb == 0 ? E0 : tb == 1 ? E1 : tb == 2 ? E2 : E3) - x);
-            sRF[ln] = tb > 0 ? exp2_hw(x - E0) : 0.f;
-            sRF[C + ln] = tb > 1 ? exp2_hw(x - E1) : 0.f;
-            sRF[2 * C + ln] = tb > 2 ? exp2_hw(x - E2) : 0.f;
-        }
+        sG[ln] = x;
+        sGam[ln] = exp2_hw(x);
+        sB[ln] = breg;
+        const float E0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 15));
+        const float E1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 31));
+        const float E2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 47));
+        const float E3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+        const int tb = ln >> 4;
+        sCF[ln] = exp2_hw((tb == 0 ? E0 : tb == 1 ? E1 : tb == 2 ? E2 : E3) - x);
+        sRF[ln] = tb > 0 ? exp2_hw(x - E0) : 0.f;
+        sRF[C + ln] = tb > 1 ? exp2_hw(x - E1) : 0.f;
+        sRF[2 * C + ln] = tb > 2 ? exp2_hw(x - E2) : 0.f;
     };
 
     // T_0, T_1, -A_10, P and r_k exp(G_n - G) of chunk c, from its staged K, Q and scalars.
     //
-    // Gram wave gw owns diagonal 16-block gw.  Its matrices live in MFMA accumulator form:
-    // element e at lane (g = lane/16, j = lane%16) is M[4 g + e][j].  With Y and X in that
-    // form, Y^T X needs no data movement (lane group g and element e enumerate the contracted
-    // index on both sides), so every product below keeps a matrix and its transpose.
-    // Waves 0 and 2 also form W = A_10 T_00 of their 32-block and hand it to waves 1 and 3,
-    // which finish the block.  The hand-over counter holds the last chunk whose W is in LDS.
+    // The Gram waves work in pairs, one pair per 32-token block b: waves 1 and 3 solve the two
+    // diagonal 16-blocks of T in block b in fp32 and hand them over through LDS; waves 0 and
+    // 2 form five tiles of P each meanwhile, then merge the two 16-blocks of their block.
+    // Matrices live in MFMA accumulator form: element e at lane (g = lane/16, j = lane%16) is
+    // M[4 g + e][j].  With Y and X in that form, Y^T X needs no data movement (lane group g
+    // and element e enumerate the contracted index on both sides), so every product below
+    // keeps a matrix and its transpose.  The hand-over counter of block b holds the last chunk
+    // whose T_00 and T_11 are in LDS.
     auto build_operands = [&](int c) GDN_INLINE {
         const int ln = opaque(lane);
         const int lrr = ln & 15, lqq = ln >> 4;
@@ -1063,9 +1071,11 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     // staged chunks in LDS and waits (bounded) until all four have staged this one
     prefetch_qk(0);
     stage_chunk(0);
+    if (gwu == 3) chunk_scalars(0);
     if (nchunks > 1) prefetch_qk(1);
     __syncthreads();  // chunk 0 staged
     build_operands(0);
+    if (gwu == 3 && nchunks > 1) chunk_scalars(1);
     __syncthreads();  // operands of chunk 0 built
     if (nchunks > 1) {
         stage_chunk(1);
@@ -1074,6 +1084,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     __syncthreads();  // chunk 1 staged
     for (int c = 0; c < nchunks; ++c) {
         if (c + 1 < nchunks) build_operands(c + 1);
+        if (gwu == 3 && c + 2 < nchunks) chunk_scalars(c + 2);
         __syncthreads();
         if (c + 2 < nchunks) {
             stage_chunk(c + 2);
