@@ -78,20 +78,20 @@ constexpr int LK = DK + 16;
 
 // LDS layout (bytes).  Buffers tagged [2] are selected by chunk parity.
 constexpr int KQ_SZ = 2 * C * LK * 2;                      // K then Q, [C][LK] bf16 each, rows = tokens
-constexpr int OFF_KQ = 0;                                  // [2]
+constexpr int OFF_KQ = 0;                                  // [3], by chunk index mod 3
 constexpr int OPT_SZ = 2 * 2 * 2 * 64 * 16;                // T_b operands [2 b][2 rt][2 hi/lo][64][8]
 constexpr int OPA_SZ = 2 * 2 * 64 * 16;                    // -A_10 operands [2 rt][2 hi/lo][64][8]
 constexpr int OPP_SZ = 6 * 64 * 16;                        // P operands [6 (rt, ks)][64][8]
 constexpr int OP_SZ = OPT_SZ + OPA_SZ + OPP_SZ;
-constexpr int OFF_OP = OFF_KQ + 2 * KQ_SZ;                 // [2]
+constexpr int OFF_OP = OFF_KQ + 3 * KQ_SZ;                 // [2], by chunk parity
 constexpr int SC_SZ = 10 * C;                              // fp32 per-token scalars of one chunk
 constexpr int OFF_SC = OFF_OP + 2 * OP_SZ;                 // [3], by chunk index mod 3
 constexpr int OFF_FLAG = OFF_SC + 3 * SC_SZ * 4;           // two int hand-over counters
 constexpr int LDS_BYTES = OFF_FLAG + 16;
 // The diagonal 16-blocks of A and of their inverses are handed from one Gram wave to
-// another through the Q rows of the other parity (the column waves read only that
-// parity's K rows during phase b): four 16 x 16 fp32 blocks each, rows of BR floats, at a
-// stride of DSTR floats.  With rows of 20, the 16 lanes that write or read 4 floats of 16
+// another through the Q rows of the chunk before the one being built (while chunk c + 1 is
+// built, the column waves read only chunk c's K rows): four 16 x 16 fp32 blocks each, rows
+// of BR floats, at a stride of DSTR floats.  With rows of 20, the 16 lanes that write or read 4 floats of 16
 // different rows hit 16 different groups of 4 banks.
 constexpr int BR = 20;
 constexpr int DSTR = 16 * BR + 16;
@@ -224,9 +224,8 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     const float *__restrict__ S0, uint16_t *__restrict__ o, float *__restrict__ S_T, int HV, int DV,
     int rep, int NG, int M, float scale, GateArgs gate, SplitArgs sp) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
-    // Chunk c's K and Q rows and the solve / read operands built from them live in the
-    // buffers of parity c % 2, its per-token scalars in buffer c % 3 (their gate part is
-    // formed a phase before the rest of the chunk is staged).  Scalars:
+    // Chunk c's K and Q rows and its per-token scalars live in buffers c % 3, the solve /
+    // read operands built from them in the buffers of parity c % 2.  Scalars:
     // G (cumulative log-decay times log2 e), gamma = exp(G), r_k = 1/|k|, r_q = scale/|q|,
     // beta, r_k exp(G_n - G), and split decays.  With E_b = G at token 16 b + 15 (the end of
     // 16-token tile b): CF[t] = exp(E_{t/16} - G_t) and RF[b][t] = exp(G_t - E_b) for t past
@@ -234,7 +233,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     // RF[b][i] CF[j], both factors <= 1.
 #define GDN_CHUNK(c)                                                                        \
     const int par_ = (c) & 1;                                                               \
-    __bf16 *sK = reinterpret_cast<__bf16 *>(lds + OFF_KQ + par_ * KQ_SZ);                   \
+    __bf16 *sK = reinterpret_cast<__bf16 *>(lds + OFF_KQ + ((c) % 3) * KQ_SZ);              \
     __bf16 *sQ = sK + C * LK;                                                               \
     bf16x8 *opT = reinterpret_cast<bf16x8 *>(lds + OFF_OP + par_ * OP_SZ);                  \
     bf16x8 *opA = opT + OPT_SZ / 16;                                                        \
@@ -649,17 +648,14 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         __syncthreads();  // chunk 0 staged
         phase_a(0);
         if (couple) a_operand(0, wu >> 1);
-        __syncthreads();  // operands of chunk 0 built
-        __syncthreads();  // chunk 1 staged
+        __syncthreads();  // operands of chunk 0 built, chunk 1 staged
         for (int c = 0; c + 1 < nchunks; ++c) {
             phase_b(c);
             if (couple) a_operand(c + 1, wu >> 1);
-            __syncthreads();
             phase_a(c + 1);
             __syncthreads();
         }
         phase_b(nchunks - 1);
-        __syncthreads();
         __syncthreads();
         store_table();
         return;
@@ -831,12 +827,14 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     // and element e enumerate the contracted index on both sides), so every product below
     // keeps a matrix and its transpose.  The hand-over counter of block b holds the last chunk
     // whose T_00 and T_11 are in LDS.
-    auto build_operands = [&](int c) GDN_INLINE {
+    f32x4 At;  // waves 0 and 2: A_10^T of their 32-token block, from head to tail
+    // part 0 (the head): everything but the 32-block merge; part 1 (the tail): the merge
+    auto build_operands = [&](int c, int part) GDN_INLINE {
         const int ln = opaque(lane);
         const int lrr = ln & 15, lqq = ln >> 4;
         GDN_CHUNK(c)
         // the diagonal 16-blocks of A and of T = (I + A)^{-1}, fp32, handed between Gram waves
-        float *Adiag = reinterpret_cast<float *>(lds + OFF_KQ + (par_ ^ 1) * KQ_SZ + KQ_SZ / 2);  // [4][DSTR]
+        float *Adiag = reinterpret_cast<float *>(lds + OFF_KQ + (((c) + 2) % 3) * KQ_SZ + KQ_SZ / 2);  // [4][DSTR]
         float *Tdiag = Adiag + 4 * DSTR;                                             // [4][DSTR]
         const int b = gwu >> 1;
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -865,6 +863,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
 
         if constexpr (!DELTA) {
             // no look-up: only P and r_k exp(G_n - G) are needed
+            if (part != 0) return;
             if (gwu == 0) {
                 p_operand(c, 0);
                 p_operand(c, 1);
@@ -878,6 +877,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                 p_operand(c, 5);
             }
         } else if ((gwu & 1) != 0) {
+            if (part != 0) return;
             // waves 1 and 3: the two diagonal 16-blocks T_00, T_11 of the 32-token block b = gwu / 2
             // of T = (I + A)^{-1}, by forward substitution in fp32, for wave gwu - 1 to merge (the
             // coupling operand -A_10 comes from column waves 0 and 2).
@@ -949,9 +949,9 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             // T_10 = -T_11 A_10 T_00 on MFMA through W = A_10 T_00, once wave gwu + 1 has solved
             // T_00 and T_11.
             const int blk = 2 * b;
+            if (part == 0) {
             // A_10^T from the role-swapped Gram tile of blocks (2 b, 2 b + 1): element e at lane
             // (g, j) is A[16 (blk+1) + j][16 blk + 4 g + e]
-            f32x4 At;
             bf16x8 kd[4], kn[4];  // K blocks blk and blk + 1
             {
                 load_blk(sK, blk, kd);
@@ -1029,6 +1029,8 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                 }
                 if (b == 1) sDn[ln] = dn;
             }
+            return;
+            }
             // wait for T_00 and T_11 of this chunk (bounded: the solving wave writes them
             // unconditionally; a wait that gave up poisons the block with NaN)
             bool handed = false;
@@ -1067,29 +1069,30 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         }
     };
 
-    // the Gram waves stage a chunk between them, then build its operands: each counts the
-    // staged chunks in LDS and waits (bounded) until all four have staged this one
+    // One period per chunk, closed by one workgroup barrier: while the column waves finish
+    // chunk c and start chunk c + 1, the Gram waves build the operands of chunk c + 1 and
+    // stage chunk c + 2 (its rows, norms and gates).  The staging sits between the head and
+    // the merge of the build, so the merging waves wait for the solved 16-blocks while doing
+    // useful work.  Wave 3 forms the gates of chunk c + 2 before the prefetch of chunk c + 3
+    // replaces them in its registers.
+    auto period = [&](int x) GDN_INLINE {  // build chunk x, stage chunk x + 1
+        build_operands(x, 0);
+        if (gwu == 3 && x + 1 < nchunks) chunk_scalars(x + 1);
+        if (x + 1 < nchunks) {
+            stage_chunk(x + 1);
+            if (x + 2 < nchunks) prefetch_qk(x + 2);
+        }
+        build_operands(x, 1);
+    };
     prefetch_qk(0);
     stage_chunk(0);
     if (gwu == 3) chunk_scalars(0);
     if (nchunks > 1) prefetch_qk(1);
     __syncthreads();  // chunk 0 staged
-    build_operands(0);
-    if (gwu == 3 && nchunks > 1) chunk_scalars(1);
-    __syncthreads();  // operands of chunk 0 built
-    if (nchunks > 1) {
-        stage_chunk(1);
-        if (nchunks > 2) prefetch_qk(2);
-    }
-    __syncthreads();  // chunk 1 staged
+    period(0);
+    __syncthreads();  // operands of chunk 0 built, chunk 1 staged
     for (int c = 0; c < nchunks; ++c) {
-        if (c + 1 < nchunks) build_operands(c + 1);
-        if (gwu == 3 && c + 2 < nchunks) chunk_scalars(c + 2);
-        __syncthreads();
-        if (c + 2 < nchunks) {
-            stage_chunk(c + 2);
-            if (c + 3 < nchunks) prefetch_qk(c + 3);
-        }
+        if (c + 1 < nchunks) period(c + 1);
         __syncthreads();
     }
 #undef GDN_CHUNK
