@@ -314,11 +314,12 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     __syncthreads();  // counters cleared before any wave uses them
     auto chunk_len = [&](int c) GDN_INLINE { return (int)((t1 - t0 - (int64_t)c * C) < C ? (t1 - t0 - (int64_t)c * C) : C); };
 
-    // Schedule.  Phase "a" of chunk c: column waves form K S, Q S and Z of chunk c while
-    // the Gram waves stage chunk c+1 into LDS.  Phase "b" of chunk c: column waves solve,
-    // write the reads and update the table while the Gram waves build T, -A_10 and P of
-    // chunk c+1.  One workgroup barrier closes every phase; a prologue stages chunk 0,
-    // builds its operands (beside the column waves' phase a of chunk 0) and stages chunk 1.
+    // Schedule.  For chunk c the column waves run phase "a" (K S, Q S and Z) and then phase
+    // "b" (the solve, the reads, the table update).  One period per chunk, closed by one
+    // workgroup barrier: the column waves run phase b of chunk c and phase a of chunk c+1
+    // while the Gram waves build T, P (and with column waves 0 and 2, -A_10) of chunk c+1
+    // and stage chunk c+2 into LDS.  A prologue stages chunk 0, then builds its operands and
+    // stages chunk 1 beside the column waves' phase a of chunk 0.
     // LDS counters: the last chunk whose T_00, T_11 are in LDS, per 32-token block
     int *flag = reinterpret_cast<int *>(lds + OFF_FLAG);
     // The operand tiles of chunk c built from its Gram tiles alone: the read operands P and
@@ -779,8 +780,8 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     };
 
     // Gram wave 3: chunk c's gates (already in registers, one token per lane) -> the
-    // cumulative log-decay G and the decay scalars derived from it, and beta.  Formed in the
-    // phase before chunk c is staged, where wave 3 has finished its own work early.
+    // cumulative log-decay G and the decay scalars derived from it, and beta.  Formed right
+    // after wave 3's own solve, where it would otherwise wait.
     auto chunk_scalars = [&](int c) GDN_INLINE {
         GDN_CHUNK(c)
         const int ln = opaque(lane);
