@@ -882,7 +882,6 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             // waves 1 and 3: the two diagonal 16-blocks T_00, T_11 of the 32-token block b = gwu / 2
             // of T = (I + A)^{-1}, by forward substitution in fp32, for wave gwu - 1 to merge (the
             // coupling operand -A_10 comes from column waves 0 and 2).
-            __builtin_amdgcn_s_setprio(2);
             const int blk = 2 * b;
             float *Ad = Adiag + b * 2 * DSTR;  // this block pair of A, then of T
             float *Td = Tdiag + b * 2 * DSTR;
@@ -944,7 +943,6 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                 }
             }
             __hip_atomic_store(flag + b, c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-            __builtin_amdgcn_s_setprio(0);
         } else {
             // waves 0 and 2: read operands P and, for the 32-token block b = gwu / 2, the coupling
             // T_10 = -T_11 A_10 T_00 on MFMA through W = A_10 T_00, once wave gwu + 1 has solved
