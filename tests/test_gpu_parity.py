@@ -120,6 +120,20 @@ def test_prefill_small(dtype, lens, HQK, HV, dk, dv, s0):
     assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), dtype, "prefill small")
 
 
+def test_prefill_every_chunk_count():
+    """One batch whose sequences span 1 to 8 chunks of 64 tokens, full and ragged: the chunked
+    kernel's pipeline runs its prologue, its per-chunk period and its last period for every
+    count, with the K/Q rows and scalars rotating over three buffers and the operands over two."""
+    lens = [64, 65, 128, 129, 192, 190, 256, 257, 320, 384, 447, 512, 31]
+    _say(f"prefill every chunk count lens={lens}")
+    inp = W.random_small(47, lens, 2, 4, 128, 128, p_g0=0.1, p_beta1=0.1)
+    name = binding.prefill_kernel_name(inp.N, inp.total_T, inp.HQK, inp.HV, inp.dk, inp.dv, torch.bfloat16)
+    assert name == "prefill_chunked", name
+    _, o, S = _prefill(inp)
+    o_ref, S_ref = oracle.run_inputs(inp)
+    assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), "bf16", "every chunk count")
+
+
 def test_prefill_unit_gates_and_extremes():
     """alpha = 1 and beta = 1 tokens mixed in; beta = 0 pure reads; a near-zero decay."""
     inp = W.random_small(42, [300, 77], 2, 4, 128, 128, p_g0=0.2, p_beta1=0.2)
