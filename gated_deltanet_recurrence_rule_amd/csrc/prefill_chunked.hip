@@ -19,12 +19,9 @@
 // Only exp(G_i - G_j) <= 1 and exp(G_n - G_i) <= 1 are formed, never 1/gamma.
 // The triangular system is split into two 32-token blocks:
 //   Delta_0 = T_0 Z_0,   Delta_1 = T_1 (Z_1 - A_10 Delta_0),   T_b = (I + A_bb)^{-1},
-// with T_b built on MFMA by blocked recursion.  If T holds the inverses of the diagonal
-// s x s blocks of a unit lower triangular I + A, and A_s is the part of A coupling the two
-// s-halves of each 2s-block, the inverses of the 2s x 2s blocks are
-//   T - T A_s T   (for two blocks: [[T_a, 0], [-T_b A_ba T_a, T_b]]),
-// applied for s = 1, 2, 4, 8 inside a 16-block (all factors stay as small as T itself);
-// the last step, s = 16, merges the two 16-blocks of a 32-block through W = A_10 T_00.
+// and inside a 32-token block T_b = [[T_00, 0], [T_10, T_11]] from the inverses T_00, T_11
+// of its two diagonal 16-blocks (forward substitution in fp32, one column per lane) and
+// the coupling T_10 = -T_11 A_10 T_00, formed on MFMA through W = A_10 T_00.
 //
 // Precision.  MFMA operands are bf16; a value that is not exactly bf16 is either
 // rounded once or carried as hi + lo (hi = bf16(x), lo = bf16(x - hi); two or
@@ -43,17 +40,16 @@
 //    stacked 16-row accumulator tiles takes them as they are, provided the A
 //    operand enumerates its 32 k-values in the same order (tile t, row 4*(lane/16)+e);
 //    all such products here use that order.
-//  * Waves 4-7 ("Gram waves") compute the chunk's Gram tiles and write P, -A_10
-//    and T_0, T_1 into LDS already in that MFMA operand order (computing a Gram
-//    tile with the two operand roles swapped yields it transposed, which is the
-//    operand order directly).
-// One workgroup barrier per chunk, a two-stage pipeline: while the column waves run chunk c
-// (K S, Q S and Z, then the solve, the reads and the table update), the Gram waves stage
-// chunk c + 1 into LDS and then build its T (an LDS counter makes the building wait until
-// all four Gram waves have staged); the column waves, done with chunk c, build chunk c + 1's
-// P and -A_10 tiles.  Every buffer the two roles share is doubled by
-// chunk parity.  The next chunk's q, k, v, g, beta are fetched into registers one chunk
-// ahead.
+//  * Waves 4-7 ("Gram waves") stage the chunks' q, k rows into LDS, form the gates'
+//    cumulative decays, and compute the chunk's Gram tiles, writing T_0, T_1 and P into
+//    LDS already in that MFMA operand order (computing a Gram tile with the two operand
+//    roles swapped yields it transposed, which is the operand order directly); column
+//    waves 0 and 2 write the -A_10 tiles.
+// One workgroup barrier per chunk: in one period the column waves finish chunk c (the
+// solve, the reads, the table update) and start chunk c + 1 (K S, Q S, Z), while the Gram
+// waves build the operands of chunk c + 1 and stage chunk c + 2.  K and Q rows and the
+// per-token scalars rotate over three buffers, the operands over two.  q, k, g and beta are
+// fetched into registers a period before they are staged, v a period before it is used.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -76,7 +72,7 @@ constexpr int NT = 512;     // threads (8 waves)
 // 272-byte rows double both (measured on gfx950).
 constexpr int LK = DK + 16;
 
-// LDS layout (bytes).  Buffers tagged [2] are selected by chunk parity.
+// LDS layout (bytes).  Buffers tagged [3] are selected by chunk index mod 3, [2] by parity.
 constexpr int KQ_SZ = 2 * C * LK * 2;                      // K then Q, [C][LK] bf16 each, rows = tokens
 constexpr int OFF_KQ = 0;                                  // [3], by chunk index mod 3
 constexpr int OPT_SZ = 2 * 2 * 2 * 64 * 16;                // T_b operands [2 b][2 rt][2 hi/lo][64][8]
@@ -86,13 +82,13 @@ constexpr int OP_SZ = OPT_SZ + OPA_SZ + OPP_SZ;
 constexpr int OFF_OP = OFF_KQ + 3 * KQ_SZ;                 // [2], by chunk parity
 constexpr int SC_SZ = 10 * C;                              // fp32 per-token scalars of one chunk
 constexpr int OFF_SC = OFF_OP + 2 * OP_SZ;                 // [3], by chunk index mod 3
-constexpr int OFF_FLAG = OFF_SC + 3 * SC_SZ * 4;           // two int hand-over counters
+constexpr int OFF_FLAG = OFF_SC + 3 * SC_SZ * 4;           // two int hand-over counters (T_00, T_11 of each 32-block)
 constexpr int LDS_BYTES = OFF_FLAG + 16;
 // The diagonal 16-blocks of A and of their inverses are handed from one Gram wave to
 // another through the Q rows of the chunk before the one being built (while chunk c + 1 is
 // built, the column waves read only chunk c's K rows): four 16 x 16 fp32 blocks each, rows
-// of BR floats, at a stride of DSTR floats.  With rows of 20, the 16 lanes that write or read 4 floats of 16
-// different rows hit 16 different groups of 4 banks.
+// of BR floats, at a stride of DSTR floats.  With rows of 20, the 16 lanes that write or
+// read 4 floats of 16 different rows hit 16 different groups of 4 banks.
 constexpr int BR = 20;
 constexpr int DSTR = 16 * BR + 16;
 static_assert(2 * 4 * DSTR * 4 <= KQ_SZ / 2, "hand-over blocks fit in one Q buffer");
