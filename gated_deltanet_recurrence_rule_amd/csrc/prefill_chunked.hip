@@ -449,31 +449,32 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         const bool vin = !SPLIT || col0 < DV;
         const bool reads = !SPLIT || mode != 1;  // the map pass forms no reads
         uint16_t *owave = o + (size_t)h * DV + col0 + 16 * wu;
+        // Row 16 rt + 4 lq + e of the chunk is read through a descriptor based at row 16 rt whose
+        // range ends at the chunk's last valid row, with the lane's byte offset (4 lq + e rows, lr
+        // columns) in the vector offset, which is what the hardware range check covers: rows
+        // past the chunk, and every row of a chunk past the sequence, read zero without a memory
+        // access.  The loads are therefore unconditional, with no zero-filling branch.
+        uint32_t voff[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) voff[e] = 2u * (uint32_t)lr + (uint32_t)(4 * lq + e) * rowb;
         auto prefetch_v = [&](int c) GDN_INLINE {
             const int nn = chunk_len(c);
-            const rsrc_t vr = make_rsrc(vwave + (size_t)(t0 + (int64_t)c * C) * vrs, vin ? (uint32_t)nn * rowb : 0u);
-            const uint32_t off = 2u * (uint32_t)lr + (uint32_t)(4 * lq) * rowb;
-            if (nn == C) {
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
+            for (int rt = 0; rt < 4; ++rt) {
+                const int rem = nn - 16 * rt;
+                const uint32_t bytes = (vin && rem > 0) ? (uint32_t)rem * rowb : 0u;
+                const rsrc_t vr = make_rsrc(vwave + (size_t)(t0 + (int64_t)c * C + 16 * rt) * vrs, bytes);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        vreg[rt][e] = __builtin_amdgcn_raw_buffer_load_b16(vr, off, (uint32_t)(16 * rt + e) * rowb, 0);
-            } else {
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        vreg[rt][e] = (16 * rt + 4 * lq + e < nn)
-                                          ? __builtin_amdgcn_raw_buffer_load_b16(vr, off, (uint32_t)(16 * rt + e) * rowb, 0)
-                                          : (uint16_t)0;
+                for (int e = 0; e < 4; ++e) vreg[rt][e] = __builtin_amdgcn_raw_buffer_load_b16(vr, voff[e], 0, 0);
             }
         };
 
         // Carried from phase a to phase b of a chunk.  Swapping the operands of a product
         // transposes its accumulator tile: element e of Ot[rt] at this lane is
-        // (Q S)[16 rt + lr][16 w + 4 lq + e].
-        f32x4 Z[4], Ot[4];
+        // (Q S)[16 rt + lr][16 w + 4 lq + e].  Sg = gamma_n S, the decayed start table that
+        // the update adds K^T D to, is formed in phase a before the hi / lo split, so the
+        // split may overwrite S's registers (the split's dot product accumulates in place).
+        f32x4 Z[4], Ot[4], Sg[8];
 
         // ---- phase a: Y = K S (hi + lo), Z = beta (v - gamma r_k Y), O^T = S^T Q^T (hi)
         auto phase_a = [&](int c) GDN_INLINE {
@@ -485,7 +486,10 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) vcur[rt][e] = bf16_to_f32(vreg[rt][e]);
-            if (c + 1 < nchunks) prefetch_v(c + 1);
+            prefetch_v(c + 1);  // past the last chunk: no bytes in range, the loads read zero
+            const float gam_n = sGam[C - 1];
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) Sg[dt] = S[dt] * gam_n;
             // contraction block ks outermost: eight independent accumulator chains in flight
             f32x4 y[4];
 #pragma unroll
@@ -611,12 +615,11 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ob), orr, off, 0, 0);
                 }
             }
-            // S <- gamma_n S + K^T D
+            // S <- Sg + K^T D
             {
                 bf16x8 Dh[2], Dlo[2];
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) split(Dx[ks], Dh[ks], Dlo[ks]);
-                const float gam_n = sGam[C - 1];
                 // The A operand K^T (rows d = 16 dt + lr, tokens in tile order) is read from the K
                 // rows by two transposed reads: lane i of a group of 16 points at token row
                 // 32 ks + 16 t + 4 lq + i/4 and the d-quad 16 dt + 4 (i%4) (stored at tile
@@ -625,7 +628,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                 const __bf16 *ktp = sK + (4 * lqq + (lrr >> 2)) * LK + 8 * (lrr & 3);
 #pragma unroll
                 for (int dt = 0; dt < 8; ++dt) {
-                    f32x4 acc = S[dt] * gam_n;
+                    f32x4 acc = Sg[dt];
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks) {
                         const __bf16 *q0 = ktp + 32 * ks * LK + 32 * (dt >> 1) + 4 * (dt & 1);
@@ -677,42 +680,29 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     // token row of item (p, u) = 8 gw + 32 p + u (uniform) + 2 lq (lane)
     const int gwu = wu - 4;
     const uint32_t qkrow = 2u * (uint32_t)rs;  // bytes per token row of q and k
+    // Token row 8 gw + 32 p + u + 2 lq: read through a descriptor based at row 8 gw + 32 p whose
+    // range ends at the chunk's last valid row, with the lane's part (2 lq + u rows, 16-byte
+    // segment lr) in the vector offset, which the hardware range check covers: rows past the
+    // chunk read zero, so the loads need no branch and no zero-filling.
+    const uint32_t qoff0 = (uint32_t)(2 * lq) * qkrow + 16u * (uint32_t)lr, qoff1 = qoff0 + qkrow;
     auto prefetch_qk = [&](int c) GDN_INLINE {
         const int nn = chunk_len(c);
         const int64_t cs = t0 + (int64_t)c * C;
-        const rsrc_t kr = make_rsrc(k + (size_t)cs * rs + (size_t)hq * DK, (uint32_t)nn * qkrow);
-        const rsrc_t qr = make_rsrc(q + (size_t)cs * rs + (size_t)hq * DK, (uint32_t)nn * qkrow);
-        const uint32_t off = (uint32_t)(2 * lq) * qkrow + 16u * (uint32_t)lr;
-        auto ld = [&](const rsrc_t &r, int p, int u) GDN_INLINE {
-            return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 r, off, (uint32_t)(8 * gwu + 32 * p + u) * qkrow, 0));
-        };
-        if (nn == C) {
 #pragma unroll
-            for (int p = 0; p < 2; ++p)
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    kreg[p][u] = ld(kr, p, u);
-                    qreg[p][u] = ld(qr, p, u);
-                }
-        } else {
-#pragma unroll
-            for (int p = 0; p < 2; ++p)
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int r = 2 * ((gt >> 4) + 16 * p) + u;
-                    kreg[p][u] = make_uint4(0, 0, 0, 0);
-                    qreg[p][u] = make_uint4(0, 0, 0, 0);
-                    if (r < nn) {
-                        kreg[p][u] = ld(kr, p, u);
-                        qreg[p][u] = ld(qr, p, u);
-                    }
-                }
+        for (int p = 0; p < 2; ++p) {
+            const int r0 = 8 * gwu + 32 * p;
+            const uint32_t bytes = nn > r0 ? (uint32_t)(nn - r0) * qkrow : 0u;
+            const size_t base = (size_t)(cs + r0) * rs + (size_t)hq * DK;
+            const rsrc_t kr = make_rsrc(k + base, bytes), qr = make_rsrc(q + base, bytes);
+            kreg[p][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, qoff0, 0, 0));
+            kreg[p][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, qoff1, 0, 0));
+            qreg[p][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qr, qoff0, 0, 0));
+            qreg[p][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qr, qoff1, 0, 0));
         }
         if (gwu == 3) {
             const bool ok = lane < nn;
             const uint32_t goff = 4u * (uint32_t)lane * (uint32_t)HV;
-            const uint32_t gbytes = 4u * (uint32_t)nn * (uint32_t)HV;
+            const uint32_t gbytes = nn > 0 ? 4u * (uint32_t)nn * (uint32_t)HV : 0u;
             // no g: a = 1 (G = 0); no beta: b = 1 (padding tokens keep b = 0)
             greg = 0.f;
             breg = ok ? 1.f : 0.f;
