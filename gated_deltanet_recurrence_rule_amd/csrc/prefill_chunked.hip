@@ -112,7 +112,7 @@ __device__ __forceinline__ float dot2(bf16x2 a, bf16x2 b, float c) {
 // (-1, 0) is emitted as the inline constant -1.0, which packed bf16 operands read as (0, -1).)
 __device__ __forceinline__ bf16x2 pair_const(uint32_t bits) {
     uint32_t r;
-    asm volatile("s_mov_b32 %0, %1" : "=s"(r) : "i"(bits));
+    asm("s_mov_b32 %0, %1" : "=s"(r) : "i"(bits));
     return __builtin_bit_cast(bf16x2, r);
 }
 // hi = bf16(x), lo = bf16(x - hi).  x - hi is exact in fp32; it is formed by a dot product
@@ -177,12 +177,13 @@ __device__ __forceinline__ bf16x4 ld_tr(const __bf16 *p) {
 // 2^x on the hardware exponential unit (flushes very negative x to zero).
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Sum over each row of 16 lanes, result in every lane of the row (DPP, no LDS traffic).
+// Sum over each row of 16 lanes, result in every lane of the row (DPP, no LDS traffic).  Every
+// source lane of these patterns lies in the row, so no lane takes the bound-control zero.
 __device__ __forceinline__ float row16_sum(float x) {
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x124, 0xF, 0xF, true));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, true));
     return x;
 }
 
@@ -207,6 +208,32 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// acc + a * x in one instruction, with a taken from lane M of this lane's row of 16 (DPP row
+// broadcast; the compiler does not fold a broadcast into a multiply-add by itself).  A DPP
+// source needs two wait states after a vector write to it, which are not inserted around
+// inline asm: a must come straight from a memory load, as it does at every use below.
+template <int M>
+__device__ __forceinline__ float fma_row_bcast(float a, float x, float acc) {
+    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "+v"(acc) : "v"(a), "v"(x), "i"(M));
+    return acc;
+}
+// acc + sum_{m < I} a(lane m) x_m, the newest term x_{I-1} last
+template <int I, int M = 0>
+__device__ __forceinline__ float row_bcast_dot(float a, const float *x, float acc) {
+    if constexpr (M < I) return row_bcast_dot<I, M + 1>(a, x, fma_row_bcast<M>(a, x[M], acc));
+    else return acc;
+}
+// Forward substitution for column fj of (I + A)^{-1}, one column per lane of a row of 16: the lane
+// holding column m of -A supplies -A_im by broadcast.  x_i = [i == fj] - sum_{m < i} A_im x_m for
+// every i: rows above fj see only zeros and stay 0, row fj gets 1, so no row needs a mask.
+template <int I>
+__device__ __forceinline__ void solve_rows(float *x, const f32x4 *acol, int fj) {
+    if constexpr (I < 16) {
+        x[I] = row_bcast_dot<I>(acol[I >> 2][I & 3], x, (I == fj) ? 1.f : 0.f);
+        solve_rows<I + 1>(x, acol, fj);
+    }
 }
 
 // DELTA = false drops the look-up (A = 0, so T = I and Delta = Z = diag(b) V): the decayed
@@ -872,9 +899,10 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             float *Ad = Adiag + b * 2 * DSTR;  // this block pair of A, then of T
             float *Td = Tdiag + b * 2 * DSTR;
             {
-                // Gram tiles of the two diagonal blocks, written as rows of A: the tile is
-                // symmetric, so lane (g, j) holds row j at columns 4 g .. 4 g + 3, and
-                // A[j][m] = b_j r_k,j r_k,m (K K^T)_jm exp(G_j - G_m) for m < j
+                // Gram tiles of the two diagonal blocks, stored as rows of -A^T: the tile is
+                // symmetric, so element e at lane (g, j) is also row i = 4 g + e, column j, and
+                // lane (g, j) writes -A[i][j] = -b_i r_k,i r_k,j (K K^T)_ij exp(G_i - G_j) (i > j)
+                // to row j, columns 4 g .. 4 g + 3
                 bf16x8 kd[4], kn[4];
                 load_blk(sK, blk, kd);
                 load_blk(sK, blk + 1, kn);
@@ -889,39 +917,30 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
                     const int t0b = 16 * (blk + hb);
                     const f32x4 gd = hb ? g1 : g0;
                     const int tj = t0b + lrr;
-                    const float cj = sB[tj] * sRk[tj], Gj = sG[tj];
+                    const float rj = sRk[tj], Gj = sG[tj];
+                    const f32x4 B4 = *reinterpret_cast<const f32x4 *>(sB + t0b + 4 * lqq);
                     const f32x4 R4 = *reinterpret_cast<const f32x4 *>(sRk + t0b + 4 * lqq);
                     const f32x4 G4 = *reinterpret_cast<const f32x4 *>(sG + t0b + 4 * lqq);
                     f32x4 a;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        a[e] = (4 * lqq + e < lrr) ? cj * R4[e] * gd[e] * exp2_hw(Gj - G4[e]) : 0.f;
+                        a[e] = (lrr < 4 * lqq + e) ? -((B4[e] * R4[e]) * rj * gd[e] * exp2_hw(G4[e] - Gj)) : 0.f;
                     *reinterpret_cast<f32x4 *>(Ad + hb * DSTR + BR * lrr + 4 * lqq) = a;
                 }
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             {
                 // Lane (hb, fj) (lanes 32-63 repeat lanes 0-31) solves (I + A_hb) x = e_fj: x is
-                // column fj of T_hb.  The whole block of A is read first, so the reads are in
-                // flight together; row i needs x_m for m < i, the newest, x_{i-1}, last.
+                // column fj of T_hb.  It reads column fj of -A_hb (row fj of the stored -A^T) and
+                // takes the other columns from the lanes of its row of 16 by broadcast.
                 const int hb = (ln >> 4) & 1, fj = ln & 15;
                 const float *Ab = Ad + hb * DSTR;
-                f32x4 arow[15][4];
+                f32x4 acol[4];
 #pragma unroll
-                for (int i = 1; i < 16; ++i)
-#pragma unroll
-                    for (int q4 = 0; q4 < (i + 3) / 4; ++q4)
-                        arow[i - 1][q4] = *reinterpret_cast<const f32x4 *>(Ab + BR * i + 4 * q4);
+                for (int q4 = 0; q4 < 4; ++q4) acol[q4] = *reinterpret_cast<const f32x4 *>(Ab + BR * fj + 4 * q4);
                 float x[16];
-#pragma unroll
-                for (int m = 0; m < 16; ++m) x[m] = (m == fj) ? 1.f : 0.f;
-#pragma unroll
-                for (int i = 1; i < 16; ++i) {
-                    float acc = 0.f;
-#pragma unroll
-                    for (int m = 0; m < i; ++m) acc = fmaf(arow[i - 1][m >> 2][m & 3], x[m], acc);
-                    x[i] = (i > fj) ? -acc : x[i];
-                }
+                x[0] = (fj == 0) ? 1.f : 0.f;
+                solve_rows<1>(x, acol, fj);
                 if (ln < 32) {
                     float *Tb = Td + hb * DSTR;
 #pragma unroll
