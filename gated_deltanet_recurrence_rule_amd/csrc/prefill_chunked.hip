@@ -513,6 +513,15 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) vcur[rt][e] = bf16_to_f32(vreg[rt][e]);
+            // The next chunk's loads go after the conversion, into the registers it frees.  Left to
+            // itself the compiler sinks the conversion to its use at the end of the phase, so the
+            // loads land in other registers that are copied back at the end of the period, which
+            // waits for loads issued only a fraction of a period before.
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(vcur[rt][e]));
+            __builtin_amdgcn_sched_barrier(0);
             prefetch_v(c + 1);  // past the last chunk: no bytes in range, the loads read zero
             const float gam_n = sGam[C - 1];
 #pragma unroll
