@@ -199,10 +199,11 @@ __device__ __forceinline__ int opaque(int x) {
 }
 
 // Global traffic goes through raw buffer accesses: a descriptor over a wave-uniform base
-// (re-based every chunk, so 32-bit offsets suffice), a per-lane byte offset in a VGPR and a
-// per-access uniform byte offset in an SGPR.  The 64-bit address arithmetic then stays out
-// of the vector ALU.  The descriptor's byte range is the chunk's valid rows: accesses past
-// it read zero and write nothing (the kernel predicates them as well).
+// (re-based every chunk, so 32-bit offsets suffice) and a per-lane byte offset in a VGPR.
+// The 64-bit address arithmetic then stays out of the vector ALU.  The hardware range check
+// covers the vector offset (not a scalar one), so every access puts its row there against a
+// descriptor whose range ends at the chunk's last valid row: loads past it read zero without
+// a memory access, and stores past it are given an out-of-range offset and dropped.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -840,7 +841,8 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         sRF[2 * C + ln] = tb > 2 ? exp2_hw(x - E2) : 0.f;
     };
 
-    // T_0, T_1, -A_10, P and r_k exp(G_n - G) of chunk c, from its staged K, Q and scalars.
+    // T_0, T_1, P and r_k exp(G_n - G) of chunk c, from its staged K, Q and scalars (the
+    // coupling operand -A_10 comes from column waves 0 and 2).
     //
     // The Gram waves work in pairs, one pair per 32-token block b: waves 1 and 3 solve the two
     // diagonal 16-blocks of T in block b in fp32 and hand them over through LDS; waves 0 and
