@@ -134,6 +134,21 @@ def test_prefill_every_chunk_count():
     assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), "bf16", "every chunk count")
 
 
+def test_prefill_every_tail_length():
+    """Sequences of 64 + t tokens for every t from 1 to 64: the last chunk's valid rows end at
+    every position, so every boundary of the range-checked loads (16-row v tiles, 8-row q / k
+    groups, the per-token gates) and of the dropped output stores is crossed; a row read or
+    written past a sequence's end would land in its neighbour in the packed batch."""
+    lens = [64 + t for t in range(1, 65)]
+    _say(f"prefill every tail length, {len(lens)} sequences")
+    inp = W.random_small(48, lens, 1, 2, 128, 128, p_g0=0.1, p_beta1=0.1)
+    name = binding.prefill_kernel_name(inp.N, inp.total_T, inp.HQK, inp.HV, inp.dk, inp.dv, torch.bfloat16)
+    assert name == "prefill_chunked", name
+    _, o, S = _prefill(inp)
+    o_ref, S_ref = oracle.run_inputs(inp)
+    assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), "bf16", "every tail length")
+
+
 def test_prefill_unit_gates_and_extremes():
     """alpha = 1 and beta = 1 tokens mixed in; beta = 0 pure reads; a near-zero decay."""
     inp = W.random_small(42, [300, 77], 2, 4, 128, 128, p_g0=0.2, p_beta1=0.2)
