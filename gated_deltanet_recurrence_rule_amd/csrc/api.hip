@@ -3,6 +3,7 @@
 // Every check runs before anything is enqueued, so a failing call writes
 // nothing.  The declarations and their contracts are in include/gdn.h.
 #include <stdarg.h>
+#include <algorithm>
 #include <atomic>
 #include <stdio.h>
 #include <string.h>
@@ -186,6 +187,56 @@ int32_t split_segments(int32_t N, int64_t total_T, int32_t HV, int32_t dk, int32
     return P;
 }
 
+// How many of the longest sequences run on 32-column workgroups (chunked prefill without split
+// sequences; host lengths needed).  Such a workgroup has two column waves instead of four and
+// takes ~0.87 of the time per chunk when every compute unit runs the kernel, ~0.95 beside the
+// rest of a packed batch (both measured on MI355X; the model takes 0.95), so a sequence that
+// would outlast the rest of the batch finishes sooner on twice the workgroups while the others
+// share the remaining compute units.  The n longest are narrowed for the n that minimises the
+// modelled time (in chunk periods)
+//   max(0.95 c_0, c_n, rest / (CUs - 2 n u)),  u = HV dv / 64 workgroups per sequence,
+// c_i the chunk counts longest first and rest the 64-column work of the others, provided the
+// narrow workgroups use at most half the units and the model gains at least 3%.
+int32_t narrow_sequences(const int32_t *cu_host, int32_t N, int32_t HV, int32_t dv, int64_t cus) {
+    if (!cu_host || N <= 0 || HV <= 0 || dv < 64 || cus <= 0) return 0;
+    const int64_t u = (int64_t)HV * (dv / 64);
+    // the largest chunk counts, longest first (no heap: the allocation-free entry shares this)
+    constexpr int kTop = 64;
+    int64_t top[kTop + 1];
+    int ntop = 0;
+    double rest = 0.0;
+    for (int32_t i = 0; i < N; ++i) {
+        const int64_t len = (int64_t)cu_host[i + 1] - cu_host[i];
+        const int64_t x = len > 0 ? (len + 63) / 64 : 0;
+        rest += (double)x * (double)u;
+        int j;
+        if (ntop < kTop + 1) {
+            j = ntop++;
+        } else {
+            if (x <= top[kTop]) continue;  // not among the largest
+            j = kTop;
+        }
+        while (j > 0 && top[j - 1] < x) {
+            top[j] = top[j - 1];
+            --j;
+        }
+        top[j] = x;
+    }
+    const double wide = std::max((double)top[0], rest / (double)cus);
+    double best = wide;
+    int32_t n_best = 0;
+    for (int32_t n = 1; n <= N && n <= kTop && 4 * n * u <= cus; ++n) {
+        rest -= (double)top[n - 1] * (double)u;
+        const double longest_wide = n < ntop ? (double)top[n] : 0.0;
+        const double t = std::max(std::max(0.95 * (double)top[0], longest_wide), rest / (double)(cus - 2 * n * u));
+        if (t < best) {
+            best = t;
+            n_best = n;
+        }
+    }
+    return best <= 0.97 * wide ? n_best : 0;
+}
+
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Workspace parts: the longest-first order, then (split sequences) the segment maps and
@@ -307,13 +358,13 @@ gdn_status run_prefill(const void *q, const void *k, const void *v, const float 
     // Launch order: longest sequences first.  Equal lengths (cu_seqlens NULL) and host
     // lengths that are already non-increasing keep the given order.
     const int32_t *order = nullptr;
+    bool sorted = false;
+    if (cu_seqlens && cu_seqlens_host) {
+        sorted = true;
+        for (int32_t i = 1; i < N && sorted; ++i)
+            sorted = cu_seqlens_host[i + 1] - cu_seqlens_host[i] <= cu_seqlens_host[i] - cu_seqlens_host[i - 1];
+    }
     if (cu_seqlens && plan.order > 0) {
-        bool sorted = false;
-        if (cu_seqlens_host) {
-            sorted = true;
-            for (int32_t i = 1; i < N && sorted; ++i)
-                sorted = cu_seqlens_host[i + 1] - cu_seqlens_host[i] <= cu_seqlens_host[i] - cu_seqlens_host[i - 1];
-        }
         if (!sorted) {
             int32_t *ord = static_cast<int32_t *>(workspace);
             gdn_status s2 = hip_status(gdn::launch_longest_first(cu_seqlens, N, ord, stream), "order launch");
@@ -326,6 +377,10 @@ gdn_status run_prefill(const void *q, const void *k, const void *v, const float 
                        variant_delta(variant) ? 1 : 0};
     a.gate = gate_args(ops, variant);
     const bool bf16 = dtype == GDN_BF16;
+    // the longest sequences on 32-column workgroups, when the launch order is longest first
+    if (plan.P == 1 && cu_seqlens && cu_seqlens_host && (order || sorted) &&
+        gdn::prefill_chunked_supported(dk, dv, bf16))
+        a.narrow = narrow_sequences(cu_seqlens_host, N, HV, dv, device_cus());
     if (plan.P > 1) {
         // split sequences: segment maps, their chain, then every segment from its start table
         float *maps = reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.order);
@@ -531,6 +586,15 @@ gdn_status gdn_gated_rmsnorm(const void *x, const void *z, const float *w, float
         return fail(GDN_ERR_ALIAS, "y may be x, but must not otherwise overlap x or z");
     gdn::NormArgs a{x, z, w, y, rows, dv, eps};
     return hip_status(gdn::launch_gated_rmsnorm(a, dtype == GDN_BF16, stream), "gated norm launch");
+}
+
+int32_t gdn_prefill_narrow_count(int32_t N, const int32_t *cu_seqlens_host, int32_t HQK, int32_t HV, int32_t dk,
+                                 int32_t dv, gdn_dtype dtype) {
+    (void)HQK;
+    if (N <= 0 || !cu_seqlens_host || !gdn::prefill_chunked_supported(dk, dv, dtype == GDN_BF16)) return 0;
+    const int64_t total_T = (int64_t)cu_seqlens_host[N] - cu_seqlens_host[0];
+    if (total_T < 0 || split_segments(N, total_T, HV, dk, dv, dtype) > 1) return 0;
+    return narrow_sequences(cu_seqlens_host, N, HV, dv, device_cus());
 }
 
 const char *gdn_prefill_kernel_name(int32_t N, int64_t total_T, int32_t HQK, int32_t HV, int32_t dk,

@@ -66,6 +66,9 @@ struct PrefillArgs {
     int32_t delta;
     GateArgs gate = {};
     SplitArgs split = {};
+    // chunked prefill without split sequences: the first `narrow` launch ranks (the longest
+    // sequences) run on workgroups of 32 columns with two column waves instead of 64 with four
+    int32_t narrow = 0;
 };
 
 // Gated RMS norm over rows of dv values (rows = tokens x heads; z rows alike; w [dv]):

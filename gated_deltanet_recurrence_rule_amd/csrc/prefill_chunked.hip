@@ -246,7 +246,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     const float *__restrict__ g, const float *__restrict__ beta,
     const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ order, int64_t span,
     const float *__restrict__ S0, uint16_t *__restrict__ o, float *__restrict__ S_T, int HV, int DV,
-    int rep, int NG, int M, float scale, GateArgs gate, SplitArgs sp) {
+    int rep, int NG, int M, int nnar, float scale, GateArgs gate, SplitArgs sp) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
     // Chunk c's K and Q rows and its per-token scalars live in buffers c % 3, the solve /
     // read operands built from them in the buffers of parity c % 2.  Scalars:
@@ -277,6 +277,13 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     // numbered in launch order (sequence rank, segment, then QK head); ids past the last
     // group exit.
     //
+    // Narrow workgroups: the first nnar launch ranks (the longest sequences; no split sequences)
+    // run on workgroups of 32 columns in which only column waves 0 and 1 hold columns (a chunk
+    // then takes ~0.87-0.95 of the time: the column waves' LDS reads of K and Q are halved per
+    // CU), so a sequence that would outlast the rest of the batch finishes sooner on twice the
+    // workgroups.  Their groups (rep * (DV / 32) workgroups each) take the first part of the
+    // grid, numbered as above; the groups of 64-column workgroups follow.
+    //
     // Split sequences (P = sp.P > 1 segments of equal whole-chunk length per sequence):
     //  * map pass (sp.mode 1, segments 0 .. P-2): the table is widened to DW = DV + DK
     //    columns, started at [0 | I], and the extra columns read v = 0.  Each column of the
@@ -290,16 +297,23 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     const int mode = SPLIT ? sp.mode : 0;
     const int PS = mode == 1 ? sp.P - 1 : (mode == 2 ? sp.P : 1);  // segments launched
     const int DW = mode == 1 ? DV + DK : DV;                       // table width
-    const int Lid = blockIdx.x;
-    const int G = 8 * ((Lid >> 3) / M) + (Lid & 7);
-    if (G >= NG) return;
-    const int mem = (Lid >> 3) % M;
-    const int rank = G / (PS * HQK);
+    const int nrk = SPLIT ? 0 : nnar;              // launch ranks on narrow workgroups
+    const int NGn = nrk * HQK;                      // their groups
+    const int Mn = rep * (DV / (DVS / 2));          // workgroups per narrow group
+    const int Wn = 8 * Mn * ((NGn + 7) / 8);        // the grid's narrow part (a multiple of 8)
+    const bool narrow = (int)blockIdx.x < Wn;
+    const int Lid = narrow ? (int)blockIdx.x : (int)blockIdx.x - Wn;
+    const int Mg = narrow ? Mn : M;
+    const int G = 8 * ((Lid >> 3) / Mg) + (Lid & 7);
+    if (G >= (narrow ? NGn : NG)) return;
+    const int mem = (Lid >> 3) % Mg;
+    const int rank = (narrow ? 0 : nrk) + G / (PS * HQK);
     const int seg = (G / HQK) % PS;
     const int hq = G % HQK;
     const int nseq = order ? order[rank] : rank;
-    const int h = hq * rep + mem / (DW / DVS);
-    const int col0 = (mem % (DW / DVS)) * DVS;
+    const int slw = narrow ? DVS / 2 : DVS;         // columns per workgroup
+    const int h = hq * rep + mem / (DW / slw);
+    const int col0 = (mem % (DW / slw)) * slw;
     const int unit = nseq * HV + h;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -431,6 +445,13 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         opA[(rt * 2 + 0) * 64 + ln] = hi;
         opA[(rt * 2 + 1) * 64 + ln] = lo;
     };
+    if (colwave && narrow && wu >= 2) {
+        // a narrow workgroup's column waves 2 and 3 hold no columns: they take part in the
+        // workgroup barriers only (two before the chunk loop, one per chunk)
+        if (nchunks > 0)
+            for (int i = 0; i < nchunks + 2; ++i) __syncthreads();
+        return;
+    }
     if (colwave) {
         // ====================== column waves: the table and the per-chunk chain ======
         // Element e of S[dt] is S[16 dt + 4 lq + e][col0 + 16 w + lr].
@@ -678,17 +699,19 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
             }
         };
 
-        // Column waves 0 and 2 also form the coupling operand -A_10 of the next chunk (row
-        // tile wu / 2) where they would otherwise wait for the Gram waves.
-        const bool couple = DELTA && (wu & 1) == 0;
+        // Column waves 0 and 2 (0 and 1 in a narrow workgroup) also form the coupling operand
+        // -A_10 of the next chunk (one row tile each) where they would otherwise wait for the
+        // Gram waves.
+        const bool couple = DELTA && (narrow || (wu & 1) == 0);
+        const int art = narrow ? wu : wu >> 1;  // its row tile of -A_10
         prefetch_v(0);
         __syncthreads();  // chunk 0 staged
         phase_a(0);
-        if (couple) a_operand(0, wu >> 1);
+        if (couple) a_operand(0, art);
         __syncthreads();  // operands of chunk 0 built, chunk 1 staged
         for (int c = 0; c + 1 < nchunks; ++c) {
             phase_b(c);
-            if (couple) a_operand(c + 1, wu >> 1);
+            if (couple) a_operand(c + 1, art);
             phase_a(c + 1);
             __syncthreads();
         }
@@ -1122,9 +1145,13 @@ hipError_t launch_prefill_chunked(const PrefillArgs &a, hipStream_t stream) {
     const int rep = a.HV / a.HQK;
     const int PS = a.split.mode == 1 ? a.split.P - 1 : (a.split.mode == 2 ? a.split.P : 1);
     const int DW = a.split.mode == 1 ? a.dv + DK : a.dv;
-    const int64_t NG = (int64_t)a.N * PS * a.HQK;       // (sequence, segment, QK head) groups
-    const int64_t M = (int64_t)rep * (DW / DVS);        // workgroups per group
-    const int64_t nwg = 8 * M * ((NG + 7) / 8);
+    const int nnar = a.split.mode != 0 ? 0 : a.narrow;
+    if (nnar < 0 || nnar > a.N) return hipErrorInvalidValue;
+    const int64_t NG = (int64_t)(a.N - nnar) * PS * a.HQK;  // (sequence, segment, QK head) groups, 64 columns
+    const int64_t M = (int64_t)rep * (DW / DVS);            // workgroups per group
+    const int64_t NGn = (int64_t)nnar * a.HQK;               // groups on 32-column workgroups
+    const int64_t Mn = (int64_t)rep * (a.dv / (DVS / 2));
+    const int64_t nwg = 8 * Mn * ((NGn + 7) / 8) + 8 * M * ((NG + 7) / 8);
     if (nwg > 0x7fffffffLL || NG > 0x7fffffffLL) return hipErrorInvalidValue;
     auto kern = a.split.mode != 0 ? (a.delta ? prefill_chunked_kernel<true, true> : prefill_chunked_kernel<false, true>)
                                   : (a.delta ? prefill_chunked_kernel<true, false> : prefill_chunked_kernel<false, false>);
@@ -1132,7 +1159,7 @@ hipError_t launch_prefill_chunked(const PrefillArgs &a, hipStream_t stream) {
                        dim3(NT), 0, stream,
                        static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
                        static_cast<const uint16_t *>(a.v), a.g, a.beta, a.cu_seqlens, a.order, a.span(),
-                       a.S0, static_cast<uint16_t *>(a.o), a.S_T, a.HV, a.dv, rep, (int)NG, (int)M, a.scale, a.gate,
+                       a.S0, static_cast<uint16_t *>(a.o), a.S_T, a.HV, a.dv, rep, (int)NG, (int)M, nnar, a.scale, a.gate,
                        a.split);
     return hipGetLastError();
 }

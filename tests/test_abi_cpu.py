@@ -403,6 +403,31 @@ def test_split_workspace_plan(lib):
     assert lib.gdn_prefill_workspace_size(1, 8192, 16, 16, 128, 128, 1) == 0
 
 
+def test_narrow_workgroup_rule(lib):
+    """Host rule for 32-column workgroups (no GPU here: 256 compute units assumed).  The
+    packed batch of 65 sequences with one of 262144 tokens narrows that one; uniform batches,
+    two equally long sequences, split sequences, fp32, and a call without host lengths
+    narrow none."""
+    import ctypes
+
+    def count(lens, HQK=16, HV=32, dk=128, dv=128, dtype=0, host=True):
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        ptr = cu.ctypes.data_as(ctypes.c_void_p) if host else None
+        return lib.gdn_prefill_narrow_count(len(lens), ptr, HQK, HV, dk, dv, dtype)
+
+    from gated_deltanet_recurrence_rule_amd import workloads as W
+    assert count(list(W.varlen_lengths())) == 1
+    assert count([262144] + [1000] * 10) == 1
+    assert count([8192, 1000, 300, 257]) == 1
+    assert count([300, 1000, 8192, 257]) == 1  # the rule does not need sorted lengths
+    assert count([16384] * 4) == 0
+    assert count([16384] * 3) == 0  # a third of the device idle, but no sequence outlasts the others
+    assert count([32768, 32768, 100]) == 0  # the second long sequence would stay on 64 columns
+    assert count([8192, 100]) == 0  # split sequences instead
+    assert count([8192, 1000, 300, 257], dtype=1) == 0  # fp32: token-serial kernel
+    assert count([8192, 1000, 300, 257], host=False) == 0
+
+
 def test_split_workspace_too_small_is_rejected(lib):
     B = Bufs(T=8192, N=1, HQK=1, HV=2, dk=128, dv=128)
     need = lib.gdn_prefill_workspace_size(1, 8192, 1, 2, 128, 128, 0)

@@ -149,6 +149,26 @@ def test_prefill_every_tail_length():
     assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), "bf16", "every tail length")
 
 
+@pytest.mark.parametrize("sorted_lengths", [True, False])
+def test_prefill_narrow_workgroups(sorted_lengths):
+    """A sequence that would outlast the rest of the batch runs on 32-column workgroups (two
+    column waves hold columns, two only keep the barriers): every unit matches the oracle, and
+    the outputs equal bit for bit those of a call without host lengths, which runs every
+    sequence on 64-column workgroups -- each column of the table evolves the same way in both."""
+    lens = [8192, 1000, 300, 257] if sorted_lengths else [300, 1000, 8192, 257]
+    _say(f"prefill narrow workgroups lens={lens}")
+    inp = W.random_small(49, lens, 16, 32, 128, 128, p_g0=0.1, p_beta1=0.1)
+    assert binding.prefill_kernel_name(inp.N, inp.total_T, 16, 32, 128, 128, torch.bfloat16) == "prefill_chunked"
+    assert binding.prefill_narrow_count(inp.cu_seqlens, 16, 32, 128, 128, torch.bfloat16) == 1
+    d, o, S = _prefill(inp)
+    o_ref, S_ref = oracle.run_inputs(inp)
+    assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), "bf16", "narrow workgroups")
+    o2, S2 = binding.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu"], S0=d["S0"],
+                             scale=inp.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(S, S2)
+
+
 def test_prefill_unit_gates_and_extremes():
     """alpha = 1 and beta = 1 tokens mixed in; beta = 0 pure reads; a near-zero decay."""
     inp = W.random_small(42, [300, 77], 2, 4, 128, 128, p_g0=0.2, p_beta1=0.2)
