@@ -149,17 +149,25 @@ def test_prefill_every_tail_length():
     assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), "bf16", "every tail length")
 
 
-@pytest.mark.parametrize("sorted_lengths", [True, False])
-def test_prefill_narrow_workgroups(sorted_lengths):
-    """A sequence that would outlast the rest of the batch runs on 32-column workgroups (two
+_SIX_LONG = [4000] * 6 + [100] * 100
+
+
+@pytest.mark.parametrize("lens,HQK,HV,narrow", [
+    ([8192, 1000, 300, 257], 16, 32, 1),
+    ([300, 1000, 8192, 257], 16, 32, 1),
+    (_SIX_LONG, 2, 4, 6),  # 12 narrow groups: two blocks of eight in the grid's narrow part
+    (list(np.random.default_rng(3).permutation(_SIX_LONG)), 2, 4, 6),
+], ids=["one_sorted", "one_unsorted", "six_sorted", "six_shuffled"])
+def test_prefill_narrow_workgroups(lens, HQK, HV, narrow):
+    """Sequences that would outlast the rest of the batch run on 32-column workgroups (two
     column waves hold columns, two only keep the barriers): every unit matches the oracle, and
     the outputs equal bit for bit those of a call without host lengths, which runs every
     sequence on 64-column workgroups -- each column of the table evolves the same way in both."""
-    lens = [8192, 1000, 300, 257] if sorted_lengths else [300, 1000, 8192, 257]
-    _say(f"prefill narrow workgroups lens={lens}")
-    inp = W.random_small(49, lens, 16, 32, 128, 128, p_g0=0.1, p_beta1=0.1)
-    assert binding.prefill_kernel_name(inp.N, inp.total_T, 16, 32, 128, 128, torch.bfloat16) == "prefill_chunked"
-    assert binding.prefill_narrow_count(inp.cu_seqlens, 16, 32, 128, 128, torch.bfloat16) == 1
+    lens = [int(x) for x in lens]
+    _say(f"prefill narrow workgroups N={len(lens)} HQK={HQK} HV={HV}")
+    inp = W.random_small(49, lens, HQK, HV, 128, 128, p_g0=0.1, p_beta1=0.1)
+    assert binding.prefill_kernel_name(inp.N, inp.total_T, HQK, HV, 128, 128, torch.bfloat16) == "prefill_chunked"
+    assert binding.prefill_narrow_count(inp.cu_seqlens, HQK, HV, 128, 128, torch.bfloat16) == narrow
     d, o, S = _prefill(inp)
     o_ref, S_ref = oracle.run_inputs(inp)
     assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), "bf16", "narrow workgroups")
