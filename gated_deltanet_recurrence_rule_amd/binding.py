@@ -90,7 +90,7 @@ def load() -> ctypes.CDLL:
     lib.gdn_last_error.restype = ctypes.c_char_p
     lib.gdn_prefill_kernel_name.argtypes = [i32, i64, i32, i32, i32, i32, ctypes.c_int]
     lib.gdn_prefill_kernel_name.restype = ctypes.c_char_p
-    lib.gdn_prefill_narrow_count.argtypes = [i32, vp, i32, i32, i32, i32, ctypes.c_int]
+    lib.gdn_prefill_narrow_count.argtypes = [i32, i64, vp, i32, i32, i32, i32, ctypes.c_int]
     lib.gdn_prefill_narrow_count.restype = ctypes.c_int32
     lib.gdn_version.argtypes = []
     lib.gdn_version.restype = ctypes.c_int32
@@ -389,14 +389,15 @@ def prefill_kernel_name(N: int, total_T: int, HQK: int, HV: int, dk: int, dv: in
 
 
 def prefill_narrow_count(cu_seqlens_host, HQK: int, HV: int, dk: int, dv: int, dtype: torch.dtype) -> int:
-    """How many of the longest sequences gdn_prefill runs on 32-column workgroups when it gets
-    these host lengths (N + 1 offsets)."""
+    """How many sequences gdn_prefill runs on 32-column workgroups when it gets these host
+    lengths (N + 1 offsets)."""
     import numpy as np
     host = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
     if host.ndim != 1 or host.size < 2:
         raise ValueError("cu_seqlens_host must hold N + 1 offsets")
     code = GDN_BF16 if dtype == torch.bfloat16 else GDN_F32
-    return int(load().gdn_prefill_narrow_count(host.size - 1, host.ctypes.data, HQK, HV, dk, dv, code))
+    total_T = int(host[-1]) - int(host[0])
+    return int(load().gdn_prefill_narrow_count(host.size - 1, total_T, host.ctypes.data, HQK, HV, dk, dv, code))
 
 
 def version() -> int:

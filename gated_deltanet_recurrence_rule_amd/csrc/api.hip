@@ -176,7 +176,10 @@ int device_cus() {
 // Segments per sequence for the chunked prefill.  A batch whose (sequence, V head, 64-column)
 // workgroups fill at most half the compute units has its sequences cut into P segments
 // (doubling P while P times the workgroups still fits the units, at most 16), provided the
-// average sequence leaves every segment at least 4 chunks.
+// average sequence leaves every segment at least 4 chunks.  Two segments are never used: the
+// map pass and the segment pass then take a chunk period per chunk of a segment each, while
+// the unsplit batch on 32-column workgroups (twice the workgroups, still within the units)
+// takes ~0.87 of one (2 x 16384 tokens, 32 heads: 703 against 782 us).
 int32_t split_segments(int32_t N, int64_t total_T, int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype) {
     if (N <= 0 || !gdn::prefill_chunked_supported(dk, dv, dtype == GDN_BF16)) return 1;
     const int64_t cus = device_cus();
@@ -184,7 +187,7 @@ int32_t split_segments(int32_t N, int64_t total_T, int32_t HV, int32_t dk, int32
     int32_t P = 1;
     while (P < 16 && units * P * 2 <= cus) P *= 2;
     while (P > 1 && total_T < (int64_t)N * P * 4 * 64) P /= 2;
-    return P;
+    return P == 2 ? 1 : P;
 }
 
 // How many of the longest sequences run on 32-column workgroups (chunked prefill without split
@@ -235,6 +238,15 @@ int32_t narrow_sequences(const int32_t *cu_host, int32_t N, int32_t HV, int32_t 
         }
     }
     return best <= 0.97 * wide ? n_best : 0;
+}
+
+// Sequences on 32-column workgroups for an unsplit chunked prefill: all of them when their
+// 64-column workgroups would fill at most half the compute units (twice as many still fit),
+// else the host rule above, which needs the host lengths and a longest-first launch order.
+int32_t narrow_for_batch(int32_t N, int32_t HV, int32_t dv, const int32_t *cu_host, bool longest_first) {
+    const int64_t cus = device_cus();
+    if ((int64_t)N * HV * (dv / 64) * 2 <= cus) return N;
+    return (cu_host && longest_first) ? narrow_sequences(cu_host, N, HV, dv, cus) : 0;
 }
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
@@ -377,10 +389,10 @@ gdn_status run_prefill(const void *q, const void *k, const void *v, const float 
                        variant_delta(variant) ? 1 : 0};
     a.gate = gate_args(ops, variant);
     const bool bf16 = dtype == GDN_BF16;
-    // the longest sequences on 32-column workgroups, when the launch order is longest first
-    if (plan.P == 1 && cu_seqlens && cu_seqlens_host && (order || sorted) &&
-        gdn::prefill_chunked_supported(dk, dv, bf16))
-        a.narrow = narrow_sequences(cu_seqlens_host, N, HV, dv, device_cus());
+    // sequences on 32-column workgroups (all of a batch that fills at most half the units; else
+    // the longest, when the host lengths are known and the launch order is longest first)
+    if (plan.P == 1 && gdn::prefill_chunked_supported(dk, dv, bf16))
+        a.narrow = narrow_for_batch(N, HV, dv, cu_seqlens ? cu_seqlens_host : nullptr, order || sorted);
     if (plan.P > 1) {
         // split sequences: segment maps, their chain, then every segment from its start table
         float *maps = reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.order);
@@ -588,13 +600,18 @@ gdn_status gdn_gated_rmsnorm(const void *x, const void *z, const float *w, float
     return hip_status(gdn::launch_gated_rmsnorm(a, dtype == GDN_BF16, stream), "gated norm launch");
 }
 
-int32_t gdn_prefill_narrow_count(int32_t N, const int32_t *cu_seqlens_host, int32_t HQK, int32_t HV, int32_t dk,
-                                 int32_t dv, gdn_dtype dtype) {
+int32_t gdn_prefill_narrow_count(int32_t N, int64_t total_T, const int32_t *cu_seqlens_host, int32_t HQK,
+                                 int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype) {
     (void)HQK;
-    if (N <= 0 || !cu_seqlens_host || !gdn::prefill_chunked_supported(dk, dv, dtype == GDN_BF16)) return 0;
-    const int64_t total_T = (int64_t)cu_seqlens_host[N] - cu_seqlens_host[0];
-    if (total_T < 0 || split_segments(N, total_T, HV, dk, dv, dtype) > 1) return 0;
-    return narrow_sequences(cu_seqlens_host, N, HV, dv, device_cus());
+    if (N <= 0 || HV <= 0 || total_T < 0 || !gdn::prefill_chunked_supported(dk, dv, dtype == GDN_BF16)) return 0;
+    if (split_segments(N, total_T, HV, dk, dv, dtype) > 1) return 0;
+    // host lengths give the longest-first order the launch uses (sorted on the host or by the
+    // order kernel); a batch too large for the order array keeps the rule off unless sorted
+    bool longest_first = cu_seqlens_host != nullptr;
+    if (longest_first && N > gdn::kMaxOrderedSequences)
+        for (int32_t i = 1; i < N && longest_first; ++i)
+            longest_first = cu_seqlens_host[i + 1] - cu_seqlens_host[i] <= cu_seqlens_host[i] - cu_seqlens_host[i - 1];
+    return narrow_for_batch(N, HV, dv, cu_seqlens_host, longest_first);
 }
 
 const char *gdn_prefill_kernel_name(int32_t N, int64_t total_T, int32_t HQK, int32_t HV, int32_t dk,

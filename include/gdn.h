@@ -346,18 +346,21 @@ const char *gdn_prefill_kernel_name(int32_t N, int64_t total_T, int32_t HQK, int
                                     int32_t dk, int32_t dv, gdn_dtype dtype);
 
 /*
- * gdn_prefill_narrow_count -- how many of the longest sequences gdn_prefill runs on
- * workgroups of 32 value columns instead of 64 (informational, for profiling and tests;
- * the result changes only the speed, never the outputs).  Applies to "prefill_chunked"
- * (not to split sequences) when gdn_prefill receives the host copy of cu_seqlens
- * (cu_seqlens_host, N + 1 int32 entries, read during the call only; NULL => 0): a sequence
- * that would outlast the rest of the batch runs each chunk in ~0.95 of the time on twice
- * the workgroups while the others share the remaining compute units.  The rule models the
- * batch's time in chunk periods on the current device's compute units and narrows the
- * longest sequences only where that gains 3% or more.  Returns 0 for invalid arguments.
+ * gdn_prefill_narrow_count -- how many sequences gdn_prefill runs on workgroups of 32 value
+ * columns instead of 64 (informational, for profiling and tests; it changes only the speed,
+ * never the outputs).  Applies to "prefill_chunked" (not to split sequences):
+ *   - every sequence, when the batch's 64-column workgroups (N x HV x dv / 64) would fill at
+ *     most half the current device's compute units: twice as many still fit, and each chunk
+ *     takes ~0.87 of the time on a workgroup with two column waves;
+ *   - else the longest sequences, when gdn_prefill receives the host copy of cu_seqlens
+ *     (cu_seqlens_host here, N + 1 int32 entries, read during the call only): a sequence that
+ *     would outlast the rest of the batch runs each chunk in ~0.95 of the time on twice the
+ *     workgroups while the others share the remaining units.  The rule models the batch's
+ *     time in chunk periods and narrows only where that gains 3% or more.
+ * total_T is the batch's token count.  Returns 0 for invalid arguments.
  */
-int32_t gdn_prefill_narrow_count(int32_t N, const int32_t *cu_seqlens_host, int32_t HQK, int32_t HV,
-                                 int32_t dk, int32_t dv, gdn_dtype dtype);
+int32_t gdn_prefill_narrow_count(int32_t N, int64_t total_T, const int32_t *cu_seqlens_host, int32_t HQK,
+                                 int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype);
 
 /* Static text for a status code. */
 const char *gdn_status_str(gdn_status s);

@@ -393,9 +393,16 @@ def test_split_workspace_plan(lib):
     need = lib.gdn_prefill_workspace_size(1, 8192, 16, 16, 128, 128, 0)
     assert need == 7 * 16 * 128 * 256 * 4 + 8 * 16 * 128 * 128 * 4
     assert lib.gdn_prefill_kernel_name(1, 8192, 16, 16, 128, 128, 0) == b"prefill_chunked_split"
-    # shorter sequences: segments may not fall under 4 chunks -> fewer segments, or none
-    assert lib.gdn_prefill_workspace_size(1, 1000, 16, 16, 128, 128, 0) == 1 * 16 * 128 * 256 * 4 + 2 * 16 * 128 * 128 * 4
+    # shorter sequences: segments may not fall under 4 chunks -> fewer segments, or none (two
+    # segments are never used: the unsplit batch on 32-column workgroups runs instead)
+    assert lib.gdn_prefill_workspace_size(1, 1500, 16, 16, 128, 128, 0) == 3 * 16 * 128 * 256 * 4 + 4 * 16 * 128 * 128 * 4
+    assert lib.gdn_prefill_workspace_size(1, 1000, 16, 16, 128, 128, 0) == 0
+    assert lib.gdn_prefill_kernel_name(1, 1000, 16, 16, 128, 128, 0) == b"prefill_chunked"
     assert lib.gdn_prefill_workspace_size(1, 400, 16, 16, 128, 128, 0) == 0
+    # 2 x 16384 tokens, 32 heads: 128 workgroups of 64 columns -> unsplit, 256 of 32
+    assert lib.gdn_prefill_workspace_size(2, 32768, 16, 32, 128, 128, 0) == 256
+    assert lib.gdn_prefill_kernel_name(2, 32768, 16, 32, 128, 128, 0) == b"prefill_chunked"
+    assert lib.gdn_prefill_narrow_count(2, 32768, None, 16, 32, 128, 128, 0) == 2
     # the 4 x 16384 batch fills the device (256 workgroups): no split
     assert lib.gdn_prefill_workspace_size(4, 65536, 16, 32, 128, 128, 0) == 256
     assert lib.gdn_prefill_kernel_name(4, 65536, 16, 32, 128, 128, 0) == b"prefill_chunked"
@@ -405,15 +412,16 @@ def test_split_workspace_plan(lib):
 
 def test_narrow_workgroup_rule(lib):
     """Host rule for 32-column workgroups (no GPU here: 256 compute units assumed).  The
-    packed batch of 65 sequences with one of 262144 tokens narrows that one; uniform batches,
-    two equally long sequences, split sequences, fp32, and a call without host lengths
-    narrow none."""
+    packed batch of 65 sequences with one of 262144 tokens narrows that one; a batch whose
+    64-column workgroups fill at most half the units narrows all (host lengths or not);
+    uniform batches that fill more, two equally long sequences, split sequences, fp32, and a
+    large batch without host lengths narrow none."""
     import ctypes
 
     def count(lens, HQK=16, HV=32, dk=128, dv=128, dtype=0, host=True):
         cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
         ptr = cu.ctypes.data_as(ctypes.c_void_p) if host else None
-        return lib.gdn_prefill_narrow_count(len(lens), ptr, HQK, HV, dk, dv, dtype)
+        return lib.gdn_prefill_narrow_count(len(lens), int(cu[-1]), ptr, HQK, HV, dk, dv, dtype)
 
     from gated_deltanet_recurrence_rule_amd import workloads as W
     assert count(list(W.varlen_lengths())) == 1
@@ -423,7 +431,9 @@ def test_narrow_workgroup_rule(lib):
     assert count([16384] * 4) == 0
     assert count([16384] * 3) == 0  # a third of the device idle, but no sequence outlasts the others
     assert count([32768, 32768, 100]) == 0  # the second long sequence would stay on 64 columns
-    assert count([8192, 100]) == 0  # split sequences instead
+    assert count([8192, 100]) == 2  # 128 workgroups of 64 columns: all on 32 (rather than two segments)
+    assert count([8192, 100], host=False) == 2
+    assert count([8192], HQK=16, HV=16) == 0  # 32 workgroups: split into 8 segments instead
     assert count([8192, 1000, 300, 257], dtype=1) == 0  # fp32: token-serial kernel
     assert count([8192, 1000, 300, 257], host=False) == 0
 
