@@ -173,21 +173,48 @@ int device_cus() {
     return cus;
 }
 
-// Segments per sequence for the chunked prefill.  A batch whose (sequence, V head, 64-column)
-// workgroups fill at most half the compute units has its sequences cut into P segments
-// (doubling P while P times the workgroups still fits the units, at most 16), provided the
-// average sequence leaves every segment at least 4 chunks.  Two segments are never used: the
-// map pass and the segment pass then take a chunk period per chunk of a segment each, while
-// the unsplit batch on 32-column workgroups (twice the workgroups, still within the units)
-// takes ~0.87 of one (2 x 16384 tokens, 32 heads: 703 against 782 us).
-int32_t split_segments(int32_t N, int64_t total_T, int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype) {
-    if (N <= 0 || !gdn::prefill_chunked_supported(dk, dv, dtype == GDN_BF16)) return 1;
+// Split plan for the chunked prefill: P segments per sequence (1 = no split), segment 0 w0
+// times as long as each of the others.  Only a batch whose (sequence, V head, 64-column)
+// workgroups, u of them, fill at most half the compute units is considered.  The plan minimises
+// a model of the time in chunk periods, with c the average chunks per sequence:
+//   unsplit, every sequence on 32-column workgroups (section on narrow workgroups): 0.87 c;
+//   split: the map pass scans segment 0 on u workgroups while the maps of segments 1 .. P-2
+//   (um workgroups each, the table widened by dk columns) take rm = ceil((P-2) um / (CUs - u))
+//   rounds of the rest, so segment 0 gets w0 = max(1, rm) units; the segment pass takes
+//   rs = ceil((P-1) u / CUs) rounds; with a = ceil(c / (P - 1 + w0)) chunks per unit the time is
+//   (w0 + rs) a + 1.2 per chain step and round of its workgroups (P - 2 steps) + 3 for the two
+//   extra launches and the second pipeline fill.
+// A split is taken only where the model gains at least 3%.  The plan depends on the sizes only
+// (not the lengths), so the workspace size does too.
+struct SplitPlan {
+    int32_t P = 1, w0 = 1;
+};
+
+SplitPlan split_plan(int32_t N, int64_t total_T, int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype) {
+    SplitPlan best;
+    if (N <= 0 || HV <= 0 || total_T <= 0 || !gdn::prefill_chunked_supported(dk, dv, dtype == GDN_BF16))
+        return best;
     const int64_t cus = device_cus();
-    const int64_t units = (int64_t)N * HV * (dv / 64);
-    int32_t P = 1;
-    while (P < 16 && units * P * 2 <= cus) P *= 2;
-    while (P > 1 && total_T < (int64_t)N * P * 4 * 64) P /= 2;
-    return P == 2 ? 1 : P;
+    const int64_t u = (int64_t)N * HV * (dv / 64), um = (int64_t)N * HV * ((dv + dk) / 64);
+    if (2 * u > cus) return best;
+    const int64_t c = (total_T + 64 * (int64_t)N - 1) / (64 * (int64_t)N);
+    const int64_t chain_wgs = (int64_t)N * HV * (dv / 8);  // two per CU
+    const double chain_step = 1.2 * (double)((chain_wgs + 2 * cus - 1) / (2 * cus));
+    double t_best = 0.97 * 0.87 * (double)c;
+    for (int32_t P = 3; P <= 16; ++P) {
+        const int64_t rm = ((P - 2) * um + (cus - u) - 1) / (cus - u);
+        const int64_t w0 = rm > 1 ? rm : 1;
+        const int64_t rs = ((P - 1) * u + cus - 1) / cus;
+        const int64_t units = P - 1 + w0;
+        const int64_t a = (c + units - 1) / units;
+        const double t = (double)((w0 + rs) * a) + (P - 2) * chain_step + 3.0;
+        if (t < t_best) {
+            t_best = t;
+            best.P = P;
+            best.w0 = (int32_t)w0;
+        }
+    }
+    return best;
 }
 
 // How many of the longest sequences run on 32-column workgroups (chunked prefill without split
@@ -255,17 +282,18 @@ size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 // the segment start tables.
 struct WorkspacePlan {
     size_t order = 0, maps = 0, starts = 0;
-    int32_t P = 1;
+    SplitPlan split;
     size_t total() const { return order + maps + starts; }
 };
 
 WorkspacePlan workspace_plan(int32_t N, int64_t total_T, int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype) {
     WorkspacePlan w;
     if (N > 1 && N <= gdn::kMaxOrderedSequences) w.order = round256((size_t)N * 4);
-    w.P = split_segments(N, total_T, HV, dk, dv, dtype);
-    if (w.P > 1) {
-        w.maps = round256((size_t)N * (w.P - 1) * HV * dk * (dv + dk) * 4);
-        w.starts = round256((size_t)N * w.P * HV * dk * dv * 4);
+    w.split = split_plan(N, total_T, HV, dk, dv, dtype);
+    const int32_t P = w.split.P;
+    if (P > 1) {
+        w.maps = round256((size_t)N * (P - 2) * HV * dk * (dv + dk) * 4);
+        w.starts = round256((size_t)N * (P - 1) * HV * dk * dv * 4);
     }
     return w;
 }
@@ -391,18 +419,20 @@ gdn_status run_prefill(const void *q, const void *k, const void *v, const float 
     const bool bf16 = dtype == GDN_BF16;
     // sequences on 32-column workgroups (all of a batch that fills at most half the units; else
     // the longest, when the host lengths are known and the launch order is longest first)
-    if (plan.P == 1 && gdn::prefill_chunked_supported(dk, dv, bf16))
+    const int32_t P = plan.split.P;
+    if (P == 1 && gdn::prefill_chunked_supported(dk, dv, bf16))
         a.narrow = narrow_for_batch(N, HV, dv, cu_seqlens ? cu_seqlens_host : nullptr, order || sorted);
-    if (plan.P > 1) {
-        // split sequences: segment maps, their chain, then every segment from its start table
+    if (P > 1) {
+        // split sequences: segment 0 and the other segments' maps, their chain, then segments
+        // 1 .. P-1 from their start tables
         float *maps = reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.order);
         float *starts = reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.order + plan.maps);
-        a.split = gdn::SplitArgs{plan.P, 1, maps};
+        a.split = gdn::SplitArgs{P, 1, plan.split.w0, maps, starts};
         st = hip_status(gdn::launch_prefill_chunked(a, stream), "chunked prefill (segment maps) launch");
         if (st == GDN_OK)
-            st = hip_status(gdn::launch_split_chain(maps, S0, starts, N, plan.P, HV, dv, stream), "segment chain launch");
+            st = hip_status(gdn::launch_split_chain(maps, starts, N, P, HV, dv, stream), "segment chain launch");
         if (st == GDN_OK) {
-            a.split = gdn::SplitArgs{plan.P, 2, starts};
+            a.split = gdn::SplitArgs{P, 2, plan.split.w0, maps, starts};
             st = hip_status(gdn::launch_prefill_chunked(a, stream), "chunked prefill (segments) launch");
         }
     } else if (gdn::prefill_chunked_supported(dk, dv, bf16)) {
@@ -604,7 +634,7 @@ int32_t gdn_prefill_narrow_count(int32_t N, int64_t total_T, const int32_t *cu_s
                                  int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype) {
     (void)HQK;
     if (N <= 0 || HV <= 0 || total_T < 0 || !gdn::prefill_chunked_supported(dk, dv, dtype == GDN_BF16)) return 0;
-    if (split_segments(N, total_T, HV, dk, dv, dtype) > 1) return 0;
+    if (split_plan(N, total_T, HV, dk, dv, dtype).P > 1) return 0;
     // host lengths give the longest-first order the launch uses (sorted on the host or by the
     // order kernel); a batch too large for the order array keeps the rule off unless sorted
     bool longest_first = cu_seqlens_host != nullptr;
@@ -618,7 +648,7 @@ const char *gdn_prefill_kernel_name(int32_t N, int64_t total_T, int32_t HQK, int
                                     int32_t dv, gdn_dtype dtype) {
     (void)HQK;
     if (gdn::prefill_chunked_supported(dk, dv, dtype == GDN_BF16))
-        return (N > 0 && HV > 0 && total_T >= 0 && split_segments(N, total_T, HV, dk, dv, dtype) > 1)
+        return (N > 0 && HV > 0 && total_T >= 0 && split_plan(N, total_T, HV, dk, dv, dtype).P > 1)
                    ? "prefill_chunked_split"
                    : "prefill_chunked";
     return "prefill_recurrent";

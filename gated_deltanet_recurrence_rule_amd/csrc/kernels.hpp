@@ -17,13 +17,17 @@ struct GateArgs {
     int32_t alpha_sigmoid = 0;
 };
 
-// Split sequences for the chunked prefill (see prefill_chunked.hip): P segments per sequence;
-// mode 0 = no split, 1 = map pass (state = [N][P - 1][HV][DK][DV + DK] output), 2 = segment
-// pass (state = [N][P][HV][DK][DV] start tables).
+// Split sequences for the chunked prefill (see prefill_chunked.hip): P >= 3 segments per
+// sequence, segment 0 w0 times as long as each of the others; mode 0 = no split, 1 = map pass
+// (segment 0 scanned from S0 into starts, segments 1 .. P-2 into maps), 2 = segment pass
+// (segments 1 .. P-1 from starts).  maps = [N][P - 2][HV][DK][DV + DK], starts =
+// [N][P - 1][HV][DK][DV] (the start tables of segments 1 .. P-1).
 struct SplitArgs {
     int32_t P = 1;
     int32_t mode = 0;
-    float *state = nullptr;
+    int32_t w0 = 1;
+    float *maps = nullptr;
+    float *starts = nullptr;
 };
 
 // Arguments shared by the launchers, already validated by the C-ABI layer.
@@ -112,10 +116,11 @@ constexpr int32_t kMaxOrderedSequences = 16384;
 
 // Chunked MFMA prefill: bf16 I/O, dk = 128, dv a multiple of 64.
 bool prefill_chunked_supported(int dk, int dv, bool bf16);
-// Start tables of every segment of split sequences: S_in[n][0] = S0[n] (or zeros),
-// S_in[n][j + 1] = M_j S_in[n][j] + B_j with [B_j | M_j] = maps[n][j] (dk = 128).
-hipError_t launch_split_chain(const float *maps, const float *S0, float *S_in, int32_t N, int32_t P,
-                              int32_t HV, int32_t dv, hipStream_t stream);
+// Start tables of split sequences: the map pass wrote segment 1's (starts[n][0], the end of
+// segment 0); segment j + 1 starts at M_j S_in(j) + B_j with [B_j | M_j] = maps[n][j - 1],
+// j = 1 .. P-2 (dk = 128).
+hipError_t launch_split_chain(const float *maps, float *starts, int32_t N, int32_t P, int32_t HV, int32_t dv,
+                              hipStream_t stream);
 hipError_t launch_prefill_chunked(const PrefillArgs &a, hipStream_t stream);
 
 }  // namespace gdn

@@ -246,7 +246,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     const float *__restrict__ g, const float *__restrict__ beta,
     const int32_t *__restrict__ cu_seqlens, const int32_t *__restrict__ order, int64_t span,
     const float *__restrict__ S0, uint16_t *__restrict__ o, float *__restrict__ S_T, int HV, int DV,
-    int rep, int NG, int M, int nnar, float scale, GateArgs gate, SplitArgs sp) {
+    int rep, int NG, int M, int nfirst, float scale, GateArgs gate, SplitArgs sp) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
     // Chunk c's K and Q rows and its per-token scalars live in buffers c % 3, the solve /
     // read operands built from them in the buffers of parity c % 2.  Scalars:
@@ -277,38 +277,43 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     // numbered in launch order (sequence rank, segment, then QK head); ids past the last
     // group exit.
     //
-    // Narrow workgroups: the first nnar launch ranks (the longest sequences; no split sequences)
-    // run on workgroups of 32 columns in which only column waves 0 and 1 hold columns (a chunk
-    // then takes ~0.87-0.95 of the time: the column waves' LDS reads of K and Q are halved per
-    // CU), so a sequence that would outlast the rest of the batch finishes sooner on twice the
-    // workgroups.  Their groups (rep * (DV / 32) workgroups each) take the first part of the
-    // grid, numbered as above; the groups of 64-column workgroups follow.
+    // The grid has two parts, each numbered as above.  Unsplit (mode 0), the first part holds the
+    // nfirst longest sequences on narrow workgroups of 32 columns in which only column waves 0
+    // and 1 hold columns (a chunk then takes ~0.87-0.95 of the time: the column waves' LDS
+    // reads of K and Q are halved per CU), so a sequence that would outlast the rest of the
+    // batch finishes sooner on twice the workgroups; the second part holds the other sequences
+    // on 64-column workgroups.
     //
-    // Split sequences (P = sp.P > 1 segments of equal whole-chunk length per sequence):
-    //  * map pass (sp.mode 1, segments 0 .. P-2): the table is widened to DW = DV + DK
-    //    columns, started at [0 | I], and the extra columns read v = 0.  Each column of the
-    //    table evolves on its own and affinely in the start state, so the segment's final
-    //    table is [B | M] with S_out = M S_in + B.  Reads are not stored; the final table
-    //    goes to sp.state, [P - 1 segments][HV][DK][DW] per sequence.
-    //  * segment pass (sp.mode 2): every segment starts from sp.state, [P][HV][DK][DV] per
-    //    sequence (the start tables chained from the maps), writes its reads, and the last
-    //    segment writes S_T.
+    // Split sequences (P = sp.P >= 3 segments of whole chunks per sequence; with cps =
+    // ceil(chunks / (P - 1 + w0)), segment 0 is w0 cps chunks long and segment s >= 1 takes
+    // chunks [(w0 + s - 1) cps, (w0 + s) cps)):
+    //  * map pass (sp.mode 1): the first part scans segment 0 of every sequence (nfirst = N)
+    //    from S0 on 64-column workgroups, writing its reads; its final table, segment 1's start,
+    //    goes to sp.starts.  The second part runs segments 1 .. P-2 with the table widened to
+    //    DW = DV + DK columns, started at [0 | I], the extra columns reading v = 0.  Each column
+    //    of the table evolves on its own and affinely in the start state, so the segment's
+    //    final table is [B | M] with S_out = M S_in + B.  Reads are not stored; the final table
+    //    goes to sp.maps, [P - 2 segments][HV][DK][DW] per sequence.
+    //  * segment pass (sp.mode 2): segments 1 .. P-1 start from sp.starts, [P - 1][HV][DK][DV]
+    //    per sequence (the first written by the map pass, the others chained from the maps),
+    //    write their reads, and the last segment writes S_T.
     const int HQK = HV / rep;
     const int mode = SPLIT ? sp.mode : 0;
-    const int PS = mode == 1 ? sp.P - 1 : (mode == 2 ? sp.P : 1);  // segments launched
-    const int DW = mode == 1 ? DV + DK : DV;                       // table width
-    const int nrk = SPLIT ? 0 : nnar;              // launch ranks on narrow workgroups
-    const int NGn = nrk * HQK;                      // their groups
-    const int Mn = rep * (DV / (DVS / 2));          // workgroups per narrow group
-    const int Wn = 8 * Mn * ((NGn + 7) / 8);        // the grid's narrow part (a multiple of 8)
-    const bool narrow = (int)blockIdx.x < Wn;
-    const int Lid = narrow ? (int)blockIdx.x : (int)blockIdx.x - Wn;
-    const int Mg = narrow ? Mn : M;
+    const int PS = mode == 1 ? sp.P - 2 : (mode == 2 ? sp.P - 1 : 1);  // segments per sequence, second part
+    const int NGa = (mode == 2 ? 0 : nfirst) * HQK;                    // groups in the first part
+    const int Ma = rep * (DV / (SPLIT ? DVS : DVS / 2));               // workgroups per group there
+    const int Wa = 8 * Ma * ((NGa + 7) / 8);                           // its size (a multiple of 8)
+    const bool first = (int)blockIdx.x < Wa;
+    const bool narrow = !SPLIT && first;
+    const bool mapwg = SPLIT && mode == 1 && !first;  // a segment map
+    const int DW = mapwg ? DV + DK : DV;                // table width
+    const int Lid = first ? (int)blockIdx.x : (int)blockIdx.x - Wa;
+    const int Mg = first ? Ma : M;
     const int G = 8 * ((Lid >> 3) / Mg) + (Lid & 7);
-    if (G >= (narrow ? NGn : NG)) return;
+    if (G >= (first ? NGa : NG)) return;
     const int mem = (Lid >> 3) % Mg;
-    const int rank = (narrow ? 0 : nrk) + G / (PS * HQK);
-    const int seg = (G / HQK) % PS;
+    const int rank = first ? G / HQK : (mode == 0 ? nfirst : 0) + G / (PS * HQK);
+    const int seg = (first || mode == 0) ? 0 : 1 + (G / HQK) % PS;
     const int hq = G % HQK;
     const int nseq = order ? order[rank] : rank;
     const int slw = narrow ? DVS / 2 : DVS;         // columns per workgroup
@@ -334,10 +339,13 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         t1 = t0 + span;
     }
     if (mode != 0) {
-        // segment seg: chunks [seg cps, (seg + 1) cps) of the sequence, cps = ceil(chunks / P)
+        // segment seg: units [seg == 0 ? 0 : w0 + seg - 1, w0 + seg) of cps chunks each, cps =
+        // ceil(chunks / (P - 1 + w0))
         const int64_t len = t1 - t0;
-        const int64_t cps = ((len + C - 1) / C + sp.P - 1) / sp.P;
-        const int64_t a = (int64_t)seg * cps * C, bnd = a + cps * C;
+        const int64_t units = sp.P - 1 + sp.w0;
+        const int64_t cps = ((len + C - 1) / C + units - 1) / units;
+        const int64_t a = (seg == 0 ? 0 : (int64_t)(sp.w0 + seg - 1)) * cps * C;
+        const int64_t bnd = (int64_t)(sp.w0 + seg) * cps * C;
         const int64_t s1 = t0 + (bnd < len ? bnd : len);
         t0 += a < len ? a : len;
         t1 = s1;
@@ -460,11 +468,14 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         // start table (row stride DW) and where the final table goes
         const float *Sin = S0 ? S0 + (size_t)unit * DK * DV : nullptr;
         float *Sout = S_T ? S_T + (size_t)unit * DK * DV : nullptr;
-        if (mode == 1) {
+        if (mode == 1 && !mapwg) {
+            // segment 0 from S0; its end is segment 1's start
+            Sout = sp.starts + ((size_t)nseq * (sp.P - 1) * HV + h) * DK * DV;
+        } else if (mode == 1) {
             Sin = nullptr;
-            Sout = sp.state + ((size_t)(nseq * (sp.P - 1) + seg) * HV + h) * DK * DW;
+            Sout = sp.maps + ((size_t)(nseq * (sp.P - 2) + seg - 1) * HV + h) * DK * DW;
         } else if (mode == 2) {
-            Sin = sp.state + ((size_t)(nseq * sp.P + seg) * HV + h) * DK * DV;
+            Sin = sp.starts + ((size_t)(nseq * (sp.P - 1) + seg - 1) * HV + h) * DK * DV;
             if (seg != sp.P - 1) Sout = nullptr;
         }
 #pragma unroll
@@ -492,11 +503,11 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         const size_t vrs = (size_t)HV * DV;  // token stride of v and o
         const uint32_t rowb = 2u * (uint32_t)vrs;  // bytes per token row of v and o
         const uint16_t *vwave = v + (size_t)h * DV + col0 + 16 * wu;
-        // the map pass's identity columns (col0 >= DV) read v = 0 and store no reads: their
-        // buffer descriptors cover no bytes, so the hardware returns zeros and drops stores
-        const bool vio = !SPLIT || (col0 < DV && mode != 1);
+        // a segment map's identity columns (col0 >= DV) read v = 0, and a map stores no reads:
+        // their buffer descriptors cover no bytes, so the hardware returns zeros and drops stores
+        const bool vio = !SPLIT || (col0 < DV && !mapwg);
         const bool vin = !SPLIT || col0 < DV;
-        const bool reads = !SPLIT || mode != 1;  // the map pass forms no reads
+        const bool reads = !SPLIT || !mapwg;  // segment maps form no reads
         uint16_t *owave = o + (size_t)h * DV + col0 + 16 * wu;
         // Row 16 rt + 4 lq + e of the chunk is read through a descriptor based at row 16 rt whose
         // range ends at the chunk's last valid row, with the lane's byte offset (4 lq + e rows, lr
@@ -1143,23 +1154,26 @@ bool prefill_chunked_supported(int dk, int dv, bool bf16) { return bf16 && dk ==
 hipError_t launch_prefill_chunked(const PrefillArgs &a, hipStream_t stream) {
     if (a.N == 0) return hipSuccess;
     const int rep = a.HV / a.HQK;
-    const int PS = a.split.mode == 1 ? a.split.P - 1 : (a.split.mode == 2 ? a.split.P : 1);
-    const int DW = a.split.mode == 1 ? a.dv + DK : a.dv;
-    const int nnar = a.split.mode != 0 ? 0 : a.narrow;
-    if (nnar < 0 || nnar > a.N) return hipErrorInvalidValue;
-    const int64_t NG = (int64_t)(a.N - nnar) * PS * a.HQK;  // (sequence, segment, QK head) groups, 64 columns
-    const int64_t M = (int64_t)rep * (DW / DVS);            // workgroups per group
-    const int64_t NGn = (int64_t)nnar * a.HQK;               // groups on 32-column workgroups
-    const int64_t Mn = (int64_t)rep * (a.dv / (DVS / 2));
-    const int64_t nwg = 8 * Mn * ((NGn + 7) / 8) + 8 * M * ((NG + 7) / 8);
-    if (nwg > 0x7fffffffLL || NG > 0x7fffffffLL) return hipErrorInvalidValue;
+    const int mode = a.split.mode;
+    if (mode != 0 && (a.split.P < 3 || a.split.w0 < 1)) return hipErrorInvalidValue;
+    const int PS = mode == 1 ? a.split.P - 2 : (mode == 2 ? a.split.P - 1 : 1);
+    const int DW = mode == 1 ? a.dv + DK : a.dv;
+    // first part of the grid: the narrow sequences (unsplit) or every sequence's segment 0 (map pass)
+    const int nfirst = mode == 0 ? a.narrow : (mode == 1 ? a.N : 0);
+    if (nfirst < 0 || nfirst > a.N) return hipErrorInvalidValue;
+    const int64_t NG = (int64_t)(mode == 0 ? a.N - nfirst : a.N) * PS * a.HQK;  // second part's groups
+    const int64_t M = (int64_t)rep * (DW / DVS);                                // workgroups per group
+    const int64_t NGa = (int64_t)(mode == 2 ? 0 : nfirst) * a.HQK;              // first part's groups
+    const int64_t Ma = (int64_t)rep * (a.dv / (mode == 0 ? DVS / 2 : DVS));
+    const int64_t nwg = 8 * Ma * ((NGa + 7) / 8) + 8 * M * ((NG + 7) / 8);
+    if (nwg > 0x7fffffffLL || NG > 0x7fffffffLL || NGa > 0x7fffffffLL) return hipErrorInvalidValue;
     auto kern = a.split.mode != 0 ? (a.delta ? prefill_chunked_kernel<true, true> : prefill_chunked_kernel<false, true>)
                                   : (a.delta ? prefill_chunked_kernel<true, false> : prefill_chunked_kernel<false, false>);
     hipLaunchKernelGGL(kern, dim3((unsigned)nwg),
                        dim3(NT), 0, stream,
                        static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
                        static_cast<const uint16_t *>(a.v), a.g, a.beta, a.cu_seqlens, a.order, a.span(),
-                       a.S0, static_cast<uint16_t *>(a.o), a.S_T, a.HV, a.dv, rep, (int)NG, (int)M, nnar, a.scale, a.gate,
+                       a.S0, static_cast<uint16_t *>(a.o), a.S_T, a.HV, a.dv, rep, (int)NG, (int)M, nfirst, a.scale, a.gate,
                        a.split);
     return hipGetLastError();
 }

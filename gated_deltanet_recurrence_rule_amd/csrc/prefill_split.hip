@@ -4,9 +4,10 @@
 // P segments of whole chunks.  The recurrence of the handbook page "7. Gated DeltaNet: the
 // token-by-token recurrence" (section "The formula") is affine in the table it starts
 // from, so a segment that starts from S_in ends at M S_in + B.  The chunked kernel's map
-// pass gives every segment's [B | M] at once; this kernel chains them, one segment after
-// another, into the start table of every segment; the segment pass then runs all segments
-// at once from those tables.
+// pass scans segment 0 from S0 (its final table is segment 1's start) and gives the [B | M]
+// of segments 1 .. P-2 at once; this kernel chains them, one segment after another, into the
+// start tables of segments 2 .. P-1; the segment pass then runs segments 1 .. P-1 at once
+// from their tables.
 //
 // One workgroup per (sequence, V head, 8 columns of dv): columns of the table evolve
 // independently, so a column block chains on its own.  Per step it stages M (128 x 128
@@ -24,8 +25,7 @@ constexpr int SDK = 128;      // dk of the chunked path
 constexpr int SLM = SDK + 4;  // padded LDS row of M
 constexpr int SCB = 8;        // columns per workgroup
 
-__global__ __launch_bounds__(256) void split_chain_kernel(const float *__restrict__ maps,
-                                                          const float *__restrict__ S0, float *__restrict__ S_in,
+__global__ __launch_bounds__(256) void split_chain_kernel(const float *__restrict__ maps, float *__restrict__ starts,
                                                           int P, int HV, int DV) {
     __shared__ __attribute__((aligned(16))) float Ms[SDK * SLM];
     __shared__ __attribute__((aligned(16))) float Sb[SDK * SCB];
@@ -36,18 +36,17 @@ __global__ __launch_bounds__(256) void split_chain_kernel(const float *__restric
     const int tid = threadIdx.x;
     const int c4 = tid & 1, r = tid >> 1;  // columns c0 + 4 c4 .. + 3 of row r
 
-    auto sin_at = [&](int j) { return S_in + ((size_t)(n * P + j) * HV + h) * SDK * DV; };
-    // segment 0 starts from S0 (or zeros)
+    // start table of segment j (1 .. P-1) and map of segment j (1 .. P-2)
+    auto sin_at = [&](int j) { return starts + ((size_t)(n * (P - 1) + j - 1) * HV + h) * SDK * DV; };
+    auto map_at = [&](int j) { return maps + ((size_t)(n * (P - 2) + j - 1) * HV + h) * SDK * DW; };
+    // segment 1 starts where the map pass's scan of segment 0 ended
     for (int idx = tid; idx < SDK * SCB; idx += 256) {
         const int row = idx / SCB, col = idx % SCB;
-        const float x = S0 ? S0[((size_t)unit * SDK + row) * DV + c0 + col] : 0.f;
-        Sb[idx] = x;
-        sin_at(0)[(size_t)row * DV + c0 + col] = x;
+        Sb[idx] = sin_at(1)[(size_t)row * DV + c0 + col];
     }
     // M of the next step is loaded into registers while this step computes (16 float4 per
     // thread), then stored to LDS once every thread is done reading the current one.
     constexpr int NLD = SDK * SDK / 4 / 256;
-    auto map_at = [&](int j) { return maps + ((size_t)(n * (P - 1) + j) * HV + h) * SDK * DW; };
     f32x4 mreg[NLD];
     auto load_m = [&](int j) {
         const float *map = map_at(j);
@@ -66,8 +65,8 @@ __global__ __launch_bounds__(256) void split_chain_kernel(const float *__restric
             *reinterpret_cast<f32x4 *>(&Ms[rr * SLM + 4 * kq]) = mreg[i];
         }
     };
-    if (P > 1) load_m(0);
-    for (int j = 0; j + 1 < P; ++j) {
+    if (P > 2) load_m(1);
+    for (int j = 1; j + 1 < P; ++j) {
         const float *map = map_at(j);
         __syncthreads();  // Sb holds S_in(j); every read of Ms is done
         store_m();
@@ -90,12 +89,12 @@ __global__ __launch_bounds__(256) void split_chain_kernel(const float *__restric
 
 }  // namespace
 
-hipError_t launch_split_chain(const float *maps, const float *S0, float *S_in, int32_t N, int32_t P, int32_t HV,
-                              int32_t dv, hipStream_t stream) {
-    if (N == 0) return hipSuccess;
+hipError_t launch_split_chain(const float *maps, float *starts, int32_t N, int32_t P, int32_t HV, int32_t dv,
+                              hipStream_t stream) {
+    if (N == 0 || P < 3) return hipSuccess;
     if (dv % SCB != 0 || (int64_t)N * HV > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(split_chain_kernel, dim3((unsigned)(N * HV), (unsigned)(dv / SCB)), dim3(256), 0, stream,
-                       maps, S0, S_in, P, HV, dv);
+                       maps, starts, P, HV, dv);
     return hipGetLastError();
 }
 

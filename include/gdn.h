@@ -140,13 +140,15 @@ gdn_status gdn_decode_step_v(const void *q, const void *k, const void *v, const 
  *    N above 16384 (such batches run in the given order);
  *  - for a batch the chunked kernel runs (bf16, dk = 128, dv a multiple of 64) whose
  *    (sequence, V head, 64-column) workgroups fill at most half the device's compute
- *    units: each sequence is cut into P segments (P doubles while P times the
- *    workgroups still fits the units, at most 16, and halves until total_T >= N P 256).
- *    The recurrence is affine in the table a segment starts from, S_out = M S_in + B
- *    (handbook page "7. Gated DeltaNet: the token-by-token recurrence", section "The
- *    formula"): the library forms every segment's [B | M] at once, chains them into
- *    each segment's start table, then runs all segments at once.  This part holds
- *    N (P-1) HV dk (dv + dk) + N P HV dk dv floats.
+ *    units, and where a model of the time in chunk periods says it pays (by 3% or more):
+ *    each sequence is cut into P segments, 3 <= P <= 16, the first w0 times as long as
+ *    each of the others.  The recurrence is affine in the table a segment starts from,
+ *    S_out = M S_in + B (handbook page "7. Gated DeltaNet: the token-by-token recurrence",
+ *    section "The formula"): the library scans segment 0 from S0 while it forms the
+ *    [B | M] of segments 1 .. P-2, chains them into the start tables of segments 2 .. P-1,
+ *    then runs segments 1 .. P-1 at once.  This part holds
+ *    N (P-2) HV dk (dv + dk) + N (P-1) HV dk dv floats (22 MiB for one 8192-token sequence
+ *    with 16 heads of d = 128 on a 256-compute-unit device, P = 9).
  * The size depends on the current device's compute-unit count: query it with the
  * device current that gdn_prefill will run on.
  */
@@ -273,8 +275,9 @@ gdn_status gdn_prefill_ex(const void *q, const void *k, const void *v, const flo
  * one per device, held from the library's load on that device until the process ends.
  * Arguments, checks, results and errors are those of gdn_prefill_ex, bit for bit, plus:
  *  - GDN_ERR_WORKSPACE when gdn_prefill_workspace_size() of these sizes exceeds 24 MiB
- *    (on a 256-compute-unit device only some split batches of dv = 64 do: every
- *    (sequence, head, 64 columns) count times segments is at most 256 there);
+ *    (only split batches can: e.g. one 4096-token sequence with 32 V heads of dv = 64
+ *    needs 29 MiB on a 256-compute-unit device, one 8192-token sequence with 16 heads of
+ *    d = 128 needs 22 MiB);
  *  - GDN_ERR_HIP if the device address of the array cannot be obtained (taken once per
  *    device, at the first call on it, with that device current).
  * Every call on a device shares that device's array, and calls that overlap in time on

@@ -388,24 +388,39 @@ def test_gated_rmsnorm_rejects(lib, kw, status):
 # ------------------------------------------------------------------ split sequences
 def test_split_workspace_plan(lib):
     """Host planning of split sequences (no GPU here, so the device is taken to have 256
-    compute units): 1 x 8192 tokens, 16 heads, d = 128, bf16 -> 32 workgroups -> P = 8:
-    7 maps of 128 x 256 and 8 start tables of 128 x 128 per head."""
-    need = lib.gdn_prefill_workspace_size(1, 8192, 16, 16, 128, 128, 0)
-    assert need == 7 * 16 * 128 * 256 * 4 + 8 * 16 * 128 * 128 * 4
+    compute units).  The plan minimises the modelled time in chunk periods; the expected plans
+    below are what that model gives, worked out by hand:
+    1 x 8192 tokens, 16 heads, d = 128, bf16: u = 32 workgroups of 64 columns, 128 chunks.
+    P = 9: the maps of segments 1-7 (7 x 64 workgroups) take 2 rounds of the 224 units beside
+    segment 0's scan, so w0 = 2 and a = ceil(128 / 10) = 13 chunks per unit; the segment pass
+    (8 x 32 workgroups) 1 round; 3 x 13 + 7 x 1.2 + 3 = 50.4 periods against 0.87 x 128 unsplit.
+    Workspace: 7 maps of 128 x 256 and 8 start tables of 128 x 128 per head."""
+    def plan_bytes(N, HV, P, dk=128, dv=128):
+        maps = N * (P - 2) * HV * dk * (dv + dk) * 4
+        starts = N * (P - 1) * HV * dk * dv * 4
+        return (maps + 255) // 256 * 256 + (starts + 255) // 256 * 256
+
+    assert lib.gdn_prefill_workspace_size(1, 8192, 16, 16, 128, 128, 0) == plan_bytes(1, 16, 9)
     assert lib.gdn_prefill_kernel_name(1, 8192, 16, 16, 128, 128, 0) == b"prefill_chunked_split"
-    # shorter sequences: segments may not fall under 4 chunks -> fewer segments, or none (two
-    # segments are never used: the unsplit batch on 32-column workgroups runs instead)
-    assert lib.gdn_prefill_workspace_size(1, 1500, 16, 16, 128, 128, 0) == 3 * 16 * 128 * 256 * 4 + 4 * 16 * 128 * 128 * 4
-    assert lib.gdn_prefill_workspace_size(1, 1000, 16, 16, 128, 128, 0) == 0
-    assert lib.gdn_prefill_kernel_name(1, 1000, 16, 16, 128, 128, 0) == b"prefill_chunked"
+    # 24 chunks: P = 5 with w0 = 1 (3 maps fit one round), a = 5: 2 x 5 + 3 x 1.2 + 3 = 16.6
+    # periods against 0.87 x 24 = 20.9
+    assert lib.gdn_prefill_workspace_size(1, 1500, 16, 16, 128, 128, 0) == plan_bytes(1, 16, 5)
+    # 16 chunks: P = 4, w0 = 1, a = 4: 8 + 2.4 + 3 = 13.4 < 0.97 x 13.92
+    assert lib.gdn_prefill_workspace_size(1, 1000, 16, 16, 128, 128, 0) == plan_bytes(1, 16, 4)
+    # 7 chunks: nothing beats 0.87 x 7 once the fixed cost of the two extra launches is paid
     assert lib.gdn_prefill_workspace_size(1, 400, 16, 16, 128, 128, 0) == 0
-    # 2 x 16384 tokens, 32 heads: 128 workgroups of 64 columns -> unsplit, 256 of 32
-    assert lib.gdn_prefill_workspace_size(2, 32768, 16, 32, 128, 128, 0) == 256
-    assert lib.gdn_prefill_kernel_name(2, 32768, 16, 32, 128, 128, 0) == b"prefill_chunked"
-    assert lib.gdn_prefill_narrow_count(2, 32768, None, 16, 32, 128, 128, 0) == 2
+    assert lib.gdn_prefill_kernel_name(1, 400, 16, 16, 128, 128, 0) == b"prefill_chunked"
+    # 2 x 16384 tokens, 32 heads: u = 128, so the maps of one middle segment take 2 rounds of
+    # the other 128 units: P = 3, w0 = 2, a = 64: 3 x 64 + 1.2 x 2 + 3 = 197.4 against 222.7
+    # (the launch order takes the first 256 bytes)
+    assert lib.gdn_prefill_workspace_size(2, 32768, 16, 32, 128, 128, 0) == 256 + plan_bytes(2, 32, 3)
+    assert lib.gdn_prefill_kernel_name(2, 32768, 16, 32, 128, 128, 0) == b"prefill_chunked_split"
+    assert lib.gdn_prefill_narrow_count(2, 32768, None, 16, 32, 128, 128, 0) == 0
     # the 4 x 16384 batch fills the device (256 workgroups): no split
     assert lib.gdn_prefill_workspace_size(4, 65536, 16, 32, 128, 128, 0) == 256
     assert lib.gdn_prefill_kernel_name(4, 65536, 16, 32, 128, 128, 0) == b"prefill_chunked"
+    # a batch of more than half the units (3 x 16384, 32 heads: 192 workgroups) never splits
+    assert lib.gdn_prefill_workspace_size(3, 49152, 16, 32, 128, 128, 0) == 256
     # fp32 runs the token-serial kernel: never split
     assert lib.gdn_prefill_workspace_size(1, 8192, 16, 16, 128, 128, 1) == 0
 
@@ -431,9 +446,9 @@ def test_narrow_workgroup_rule(lib):
     assert count([16384] * 4) == 0
     assert count([16384] * 3) == 0  # a third of the device idle, but no sequence outlasts the others
     assert count([32768, 32768, 100]) == 0  # the second long sequence would stay on 64 columns
-    assert count([8192, 100]) == 2  # 128 workgroups of 64 columns: all on 32 (rather than two segments)
+    assert count([8192, 100]) == 2  # 128 workgroups of 64 columns: all on 32 (a split does not pay)
     assert count([8192, 100], host=False) == 2
-    assert count([8192], HQK=16, HV=16) == 0  # 32 workgroups: split into 8 segments instead
+    assert count([8192], HQK=16, HV=16) == 0  # 32 workgroups: split into 9 segments instead
     assert count([8192, 1000, 300, 257], dtype=1) == 0  # fp32: token-serial kernel
     assert count([8192, 1000, 300, 257], host=False) == 0
 
@@ -589,19 +604,20 @@ def test_binding_conv_rejects_mis_shaped(name, shape):
 
 # ------------------------------------------------------------------ the allocation-free prefill
 def test_noalloc_rejects_workspace_beyond_its_scratch(lib):
-    """gdn_prefill_noalloc's static scratch holds 24 MiB: a split batch of dv = 64 that needs ~32 MB
-    is rejected with GDN_ERR_WORKSPACE before anything runs (the device count here is taken as 256
-    compute units), and N = 0 is a no-op that touches no device."""
-    T, H, dk, dv = 16384, 16, 128, 64
-    assert lib.gdn_prefill_workspace_size(1, T, H, H, dk, dv, 0) > 24 << 20
+    """gdn_prefill_noalloc's static scratch holds 24 MiB: a split batch (4096 tokens, 16 QK / 32 V
+    heads of dv = 64) that needs ~29 MiB is rejected with GDN_ERR_WORKSPACE before anything runs
+    (the device count here is taken as 256 compute units), and N = 0 is a no-op that touches no
+    device."""
+    T, H, HV, dk, dv = 4096, 16, 32, 128, 64
+    assert lib.gdn_prefill_workspace_size(1, T, H, HV, dk, dv, 0) > 24 << 20
     q = np.full(T * H * dk // 2 + 16, 7.0, np.float32)      # bf16 sizes, in floats
     k = np.full_like(q, 7.0)
-    v = np.full(T * H * dv // 2 + 16, 7.0, np.float32)
+    v = np.full(T * HV * dv // 2 + 16, 7.0, np.float32)
     o = np.full_like(v, 7.0)
-    g = np.full(T * H + 16, 7.0, np.float32)
+    g = np.full(T * HV + 16, 7.0, np.float32)
     b = np.full_like(g, 7.0)
     p = lambda a: ctypes.c_void_p(a.ctypes.data)
-    st = lib.gdn_prefill_noalloc(p(q), p(k), p(v), p(g), p(b), None, None, 1, T, None, p(o), None, H, H, dk, dv,
+    st = lib.gdn_prefill_noalloc(p(q), p(k), p(v), p(g), p(b), None, None, 1, T, None, p(o), None, H, HV, dk, dv,
                                  0, 1.0, 0, None, None)
     assert st == E_WS, lib.gdn_last_error()
     assert b"static scratch" in lib.gdn_last_error()

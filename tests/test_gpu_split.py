@@ -63,6 +63,39 @@ def test_split_prefill(lens, HQK, HV, s0, variant):
                   grows=not look)
 
 
+def _split_plan_P(inp):
+    """P of the library's split plan, from the workspace size (maps of P - 2 segments and start
+    tables of P - 1, each part rounded to 256 bytes, after the launch order's 256 bytes)."""
+    need = _split_ws(inp)
+    order = 256 if 1 < inp.N <= 16384 else 0
+    per_map = inp.N * inp.HV * inp.dk * (inp.dv + inp.dk) * 4
+    per_start = inp.N * inp.HV * inp.dk * inp.dv * 4
+    r = lambda x: (x + 255) // 256 * 256
+    for P in range(3, 17):
+        if need == order + r((P - 2) * per_map) + r((P - 1) * per_start):
+            return P
+    return 1
+
+
+@pytest.mark.parametrize("lens,HQK,HV,P", [
+    ([8192] * 16, 2, 4, 3),      # 128 workgroups: one middle segment, its maps two rounds beside segment 0
+    ([8192], 16, 16, 9),         # the 8192-token workload's plan
+])
+def test_split_prefill_weak_decay(lens, HQK, HV, P):
+    """Decay close to 1 (a = sigmoid(N(8, 1))): a segment's map M stays far from zero, so the start
+    tables depend on how the chain applies it to segment 0's final table."""
+    _say(f"split prefill, weak decay: lens={lens[0]} x {len(lens)} HQK={HQK} HV={HV}")
+    inp = W.random_small(85, lens, HQK, HV, 128, 128, dtype="bf16", s0=True, g_mu=8.0, g_sd=1.0)
+    assert _split_plan_P(inp) == P
+    d = to_device(inp)
+    o, S = binding.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu"],
+                           cu_seqlens_host=inp.cu_seqlens, S0=d["S0"], scale=inp.scale)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.run(inp.as_f64("q"), inp.as_f64("k"), inp.as_f64("v"), inp.as_f64("g"),
+                              inp.as_f64("beta"), inp.cu_seqlens, inp.as_f64("S0"), scale=inp.scale)
+    assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), "bf16", f"split weak decay P={P}")
+
+
 def test_split_prefill_equal_lengths_in_place_raw_gates():
     """cu_seqlens NULL (equal lengths), the final table written over the start table, gates from
     raw projections: the split path reads S0 only before its segment pass."""

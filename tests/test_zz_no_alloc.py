@@ -47,7 +47,7 @@ def _both(inp, variant="gated_delta"):
 
 
 def test_noalloc_equals_workspace_entry_on_two_calls():
-    # first call: one 8192-token sequence, 16 heads: split into 8 segments, 22 MiB of maps
+    # first call: one 8192-token sequence, 16 heads: split into 9 segments, 22 MiB of maps
     # and start tables in the scratch
     big = W.prefill()
     need = binding.prefill_workspace_size(big.N, big.total_T, big.HQK, big.HV, big.dk, big.dv, torch.bfloat16)
@@ -75,13 +75,14 @@ def test_noalloc_equals_workspace_entry_on_two_calls():
 
 
 def test_noalloc_rejects_workspace_beyond_the_scratch():
-    # a split batch of dv = 64 whose maps and start tables need ~30 MiB
-    T = 16 * 4 * 64 * 4
-    need = binding.prefill_workspace_size(1, T, 16, 16, 128, 64, torch.bfloat16)
+    # a split batch (4096 tokens, 16 QK / 32 V heads of dv = 64) whose maps and start tables
+    # need ~29 MiB
+    T = 4096
+    need = binding.prefill_workspace_size(1, T, 16, 32, 128, 64, torch.bfloat16)
     assert need > SCRATCH_BYTES
-    inp = W.random_small(79, [T], 16, 16, 128, 64, dtype="bf16", s0=False)
+    inp = W.random_small(79, [T], 16, 32, 128, 64, dtype="bf16", s0=False)
     d = to_device(inp)
-    o = torch.zeros((T, 16, 64), dtype=torch.bfloat16, device="cuda")
+    o = torch.zeros((T, 32, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(binding.GdnError) as e:
         binding.prefill_noalloc(d["q"], d["k"], d["v"], d["g"], d["beta"], N=1, o=o)
     assert e.value.status == -7 and "static scratch" in str(e.value)
