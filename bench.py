@@ -140,7 +140,7 @@ def main():
     S_T = torch.empty((pf.N, pf.HV, pf.dk, pf.dv), dtype=torch.float32, device=dev)
     o_d = torch.empty((dc.N, dc.HV, dc.dv), dtype=torch.bfloat16, device=dev)
     ws_bytes = binding.prefill_workspace_size(pf.N, pf.total_T, pf.HQK, pf.HV, pf.dk, pf.dv,
-                                              torch.bfloat16)
+                                              torch.bfloat16, cu_seqlens_host=pf.cu_seqlens)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
@@ -223,7 +223,8 @@ def main():
     e = 2  # bf16 bytes
     pb, pf_chunk, pf_rec = prefill_alg(N, T, pf.HQK, pf.HV, pf.dk, pf.dv, e, True)
     db, dflops, dstate = decode_alg(dc.N, dc.HQK, dc.HV, dc.dk, dc.dv, e)
-    kname = binding.prefill_kernel_name(pf.N, pf.total_T, pf.HQK, pf.HV, pf.dk, pf.dv, torch.bfloat16)
+    kname = binding.prefill_kernel_name(pf.N, pf.total_T, pf.HQK, pf.HV, pf.dk, pf.dv, torch.bfloat16,
+                                        cu_seqlens_host=pf.cu_seqlens)
     pre_roof = prefill_roofline(pb, pf_chunk, pf_rec, pre_avg, kname)
     pre_roof["traffic"] = recorded_traffic("prefill_chunked") if "chunk" in kname else None
     dec_gbps = db / (dec_avg * 1e-3) / 1e9
@@ -340,7 +341,8 @@ def extra_leg(args, binding, W, up, dev, with_varlen=False, legs=None):
         tdt = torch.bfloat16 if inp.dtype == "bf16" else torch.float32
         o = torch.empty((inp.total_T, inp.HV, inp.dv), dtype=tdt, device=dev)
         ST = torch.empty((inp.N, inp.HV, inp.dk, inp.dv), dtype=torch.float32, device=dev)
-        nws = binding.prefill_workspace_size(inp.N, inp.total_T, inp.HQK, inp.HV, inp.dk, inp.dv, tdt)
+        nws = binding.prefill_workspace_size(inp.N, inp.total_T, inp.HQK, inp.HV, inp.dk, inp.dv, tdt,
+                                             cu_seqlens_host=inp.cu_seqlens)
         ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
 
         def call():
@@ -363,7 +365,8 @@ def extra_leg(args, binding, W, up, dev, with_varlen=False, legs=None):
         ab = sum(prefill_alg(1, int(L), inp.HQK, inp.HV, inp.dk, inp.dv, e, inp.S0 is not None)[0] for L in lens)
         fl = sum(prefill_alg(1, int(L), inp.HQK, inp.HV, inp.dk, inp.dv, e, False)[1] for L in lens)
         fr = sum(prefill_alg(1, int(L), inp.HQK, inp.HV, inp.dk, inp.dv, e, False)[2] for L in lens)
-        kname = binding.prefill_kernel_name(inp.N, inp.total_T, inp.HQK, inp.HV, inp.dk, inp.dv, tdt)
+        kname = binding.prefill_kernel_name(inp.N, inp.total_T, inp.HQK, inp.HV, inp.dk, inp.dv, tdt,
+                                            cu_seqlens_host=inp.cu_seqlens)
         roof = prefill_roofline(ab, fl, fr, ms, kname)
         out[name] = {"sequences": inp.N, "tokens": inp.total_T, "heads": [inp.HQK, inp.HV], "d": [inp.dk, inp.dv],
                      "dtype": inp.dtype, "kernel": kname, "ms": ms, "Mtok_s": inp.total_T / (ms * 1e-3) / 1e6,

@@ -67,6 +67,8 @@ def load() -> ctypes.CDLL:
     lib.gdn_decode_step_ex.restype = ctypes.c_int
     lib.gdn_prefill_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, ctypes.c_int]
     lib.gdn_prefill_workspace_size.restype = sz
+    lib.gdn_prefill_workspace_size_lens.argtypes = [i32, i64, vp, i32, i32, i32, i32, ctypes.c_int]
+    lib.gdn_prefill_workspace_size_lens.restype = sz
     lib.gdn_prefill.argtypes = [vp, vp, vp, fp, fp, vp, vp, i32, i64, fp, vp, fp, i32, i32, i32, i32,
                                 ctypes.c_int, ctypes.c_float, vp, sz, vp]
     lib.gdn_prefill.restype = ctypes.c_int
@@ -88,7 +90,7 @@ def load() -> ctypes.CDLL:
     lib.gdn_status_str.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
     lib.gdn_last_error.restype = ctypes.c_char_p
-    lib.gdn_prefill_kernel_name.argtypes = [i32, i64, i32, i32, i32, i32, ctypes.c_int]
+    lib.gdn_prefill_kernel_name.argtypes = [i32, i64, vp, i32, i32, i32, i32, ctypes.c_int]
     lib.gdn_prefill_kernel_name.restype = ctypes.c_char_p
     lib.gdn_prefill_narrow_count.argtypes = [i32, i64, vp, i32, i32, i32, i32, ctypes.c_int]
     lib.gdn_prefill_narrow_count.restype = ctypes.c_int32
@@ -214,10 +216,23 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[t
     return o
 
 
+def _host_offsets(cu_seqlens_host, N: int):
+    import numpy as np
+    host = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
+    if host.shape != (N + 1,):
+        raise ValueError("cu_seqlens_host must have N + 1 entries")
+    return host
+
+
 def prefill_workspace_size(N: int, total_T: int, HQK: int, HV: int, dk: int, dv: int,
-                           dtype: torch.dtype) -> int:
+                           dtype: torch.dtype, cu_seqlens_host=None) -> int:
+    """Workspace bytes for these sizes; with the host lengths (N + 1 offsets), for the plan
+    gdn_prefill takes given those lengths (gdn_prefill_workspace_size_lens)."""
     code = GDN_BF16 if dtype == torch.bfloat16 else GDN_F32
-    return int(load().gdn_prefill_workspace_size(N, total_T, HQK, HV, dk, dv, code))
+    if cu_seqlens_host is None:
+        return int(load().gdn_prefill_workspace_size(N, total_T, HQK, HV, dk, dv, code))
+    host = _host_offsets(cu_seqlens_host, N)
+    return int(load().gdn_prefill_workspace_size_lens(N, total_T, host.ctypes.data, HQK, HV, dk, dv, code))
 
 
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch.Tensor],
@@ -275,12 +290,7 @@ def _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, N, S0, scale, o, S_T
         if N is None:
             raise ValueError("give cu_seqlens or N")
         n_seq = int(N)
-    host = None
-    if cu_seqlens_host is not None:
-        import numpy as np
-        host = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
-        if host.shape != (n_seq + 1,):
-            raise ValueError("cu_seqlens_host must have N + 1 entries")
+    host = None if cu_seqlens_host is None else _host_offsets(cu_seqlens_host, n_seq)
     _need_opt(S0, "S0", torch.float32, (n_seq, HV, dk, dv), dev)
     if o is None:
         o = torch.empty((total_T, HV, dv), dtype=v.dtype, device=dev)
@@ -290,7 +300,12 @@ def _prefill(q, k, v, g, beta, cu_seqlens, cu_seqlens_host, N, S0, scale, o, S_T
     _need_opt(S_T, "S_T", torch.float32, (n_seq, HV, dk, dv), dev)
     lib = load()
     code = _dtype_code(q)
-    need = 0 if noalloc else int(lib.gdn_prefill_workspace_size(n_seq, total_T, HQK, HV, dk, dv, code))
+    if noalloc:
+        need = 0
+    elif host is not None and cu_seqlens is not None:
+        need = int(lib.gdn_prefill_workspace_size_lens(n_seq, total_T, host.ctypes.data, HQK, HV, dk, dv, code))
+    else:
+        need = int(lib.gdn_prefill_workspace_size(n_seq, total_T, HQK, HV, dk, dv, code))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if workspace is not None:
@@ -383,9 +398,13 @@ def gated_rmsnorm(x: torch.Tensor, z: torch.Tensor, w: torch.Tensor, eps: float 
 
 
 def prefill_kernel_name(N: int, total_T: int, HQK: int, HV: int, dk: int, dv: int,
-                        dtype: torch.dtype) -> str:
+                        dtype: torch.dtype, cu_seqlens_host=None) -> str:
+    """The kernel gdn_prefill runs, with the workspace prefill() allocates for these sizes
+    (and host lengths, if given)."""
     code = GDN_BF16 if dtype == torch.bfloat16 else GDN_F32
-    return load().gdn_prefill_kernel_name(N, total_T, HQK, HV, dk, dv, code).decode()
+    host = None if cu_seqlens_host is None else _host_offsets(cu_seqlens_host, N)
+    ptr = None if host is None else host.ctypes.data
+    return load().gdn_prefill_kernel_name(N, total_T, ptr, HQK, HV, dk, dv, code).decode()
 
 
 def prefill_narrow_count(cu_seqlens_host, HQK: int, HV: int, dk: int, dv: int, dtype: torch.dtype) -> int:

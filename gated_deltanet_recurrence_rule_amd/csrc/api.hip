@@ -173,10 +173,21 @@ int device_cus() {
     return cus;
 }
 
-// Split plan for the chunked prefill: P segments per sequence (1 = no split), segment 0 w0
-// times as long as each of the others.  Only a batch whose (sequence, V head, 64-column)
-// workgroups, u of them, fill at most half the compute units is considered.  The plan minimises
-// a model of the time in chunk periods, with c the average chunks per sequence:
+// Split plan for the chunked prefill: the first ns launch ranks are cut into P segments (P = 1:
+// no split), segment 0 w0 times as long as each of the others.
+struct SplitPlan {
+    int32_t P = 1, w0 = 1, ns = 0;
+};
+
+// Chain steps in chunk periods: one workgroup per (split sequence, V head, 8 columns), two per CU.
+double chain_step(int64_t ns, int32_t HV, int32_t dv, int64_t cus) {
+    const int64_t wgs = ns * HV * (dv / 8);
+    return 1.2 * (double)((wgs + 2 * cus - 1) / (2 * cus));
+}
+
+// The plan from the sizes alone: only a batch whose (sequence, V head, 64-column) workgroups, u
+// of them, fill at most half the compute units is split, every sequence alike.  The plan
+// minimises a model of the time in chunk periods, with c the average chunks per sequence:
 //   unsplit, every sequence on 32-column workgroups (section on narrow workgroups): 0.87 c;
 //   split: the map pass scans segment 0 on u workgroups while the maps of segments 1 .. P-2
 //   (um workgroups each, the table widened by dk columns) take rm = ceil((P-2) um / (CUs - u))
@@ -184,12 +195,7 @@ int device_cus() {
 //   rs = ceil((P-1) u / CUs) rounds; with a = ceil(c / (P - 1 + w0)) chunks per unit the time is
 //   (w0 + rs) a + 1.2 per chain step and round of its workgroups (P - 2 steps) + 3 for the two
 //   extra launches and the second pipeline fill.
-// A split is taken only where the model gains at least 3%.  The plan depends on the sizes only
-// (not the lengths), so the workspace size does too.
-struct SplitPlan {
-    int32_t P = 1, w0 = 1;
-};
-
+// A split is taken only where the model gains at least 3%.
 SplitPlan split_plan(int32_t N, int64_t total_T, int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype) {
     SplitPlan best;
     if (N <= 0 || HV <= 0 || total_T <= 0 || !gdn::prefill_chunked_supported(dk, dv, dtype == GDN_BF16))
@@ -198,8 +204,7 @@ SplitPlan split_plan(int32_t N, int64_t total_T, int32_t HV, int32_t dk, int32_t
     const int64_t u = (int64_t)N * HV * (dv / 64), um = (int64_t)N * HV * ((dv + dk) / 64);
     if (2 * u > cus) return best;
     const int64_t c = (total_T + 64 * (int64_t)N - 1) / (64 * (int64_t)N);
-    const int64_t chain_wgs = (int64_t)N * HV * (dv / 8);  // two per CU
-    const double chain_step = 1.2 * (double)((chain_wgs + 2 * cus - 1) / (2 * cus));
+    const double step = chain_step(N, HV, dv, cus);
     double t_best = 0.97 * 0.87 * (double)c;
     for (int32_t P = 3; P <= 16; ++P) {
         const int64_t rm = ((P - 2) * um + (cus - u) - 1) / (cus - u);
@@ -207,64 +212,78 @@ SplitPlan split_plan(int32_t N, int64_t total_T, int32_t HV, int32_t dk, int32_t
         const int64_t rs = ((P - 1) * u + cus - 1) / cus;
         const int64_t units = P - 1 + w0;
         const int64_t a = (c + units - 1) / units;
-        const double t = (double)((w0 + rs) * a) + (P - 2) * chain_step + 3.0;
+        const double t = (double)((w0 + rs) * a) + (P - 2) * step + 3.0;
         if (t < t_best) {
             t_best = t;
             best.P = P;
             best.w0 = (int32_t)w0;
+            best.ns = N;
         }
     }
     return best;
 }
 
-// How many of the longest sequences run on 32-column workgroups (chunked prefill without split
-// sequences; host lengths needed).  Such a workgroup has two column waves instead of four and
-// takes ~0.87 of the time per chunk when every compute unit runs the kernel, ~0.95 beside the
-// rest of a packed batch (both measured on MI355X; the model takes 0.95), so a sequence that
-// would outlast the rest of the batch finishes sooner on twice the workgroups while the others
-// share the remaining compute units.  The n longest are narrowed for the n that minimises the
-// modelled time (in chunk periods)
-//   max(0.95 c_0, c_n, rest / (CUs - 2 n u)),  u = HV dv / 64 workgroups per sequence,
-// c_i the chunk counts longest first and rest the 64-column work of the others, provided the
-// narrow workgroups use at most half the units and the model gains at least 3%.
-int32_t narrow_sequences(const int32_t *cu_host, int32_t N, int32_t HV, int32_t dv, int64_t cus) {
-    if (!cu_host || N <= 0 || HV <= 0 || dv < 64 || cus <= 0) return 0;
-    const int64_t u = (int64_t)HV * (dv / 64);
-    // the largest chunk counts, longest first (no heap: the allocation-free entry shares this)
-    constexpr int kTop = 64;
+// Chunk counts of a packed batch from its host lengths: the largest (longest first; no heap, the
+// allocation-free entry shares this) and the 64-column work of the whole batch.
+struct LengthStats {
+    static constexpr int kTop = 64;
     int64_t top[kTop + 1];
     int ntop = 0;
-    double rest = 0.0;
+    double work = 0.0;  // sum of chunks x (HV dv / 64) workgroups
+};
+
+LengthStats length_stats(const int32_t *cu_host, int32_t N, int64_t u) {
+    LengthStats ls;
     for (int32_t i = 0; i < N; ++i) {
         const int64_t len = (int64_t)cu_host[i + 1] - cu_host[i];
         const int64_t x = len > 0 ? (len + 63) / 64 : 0;
-        rest += (double)x * (double)u;
+        ls.work += (double)x * (double)u;
         int j;
-        if (ntop < kTop + 1) {
-            j = ntop++;
+        if (ls.ntop < LengthStats::kTop + 1) {
+            j = ls.ntop++;
         } else {
-            if (x <= top[kTop]) continue;  // not among the largest
-            j = kTop;
+            if (x <= ls.top[LengthStats::kTop]) continue;  // not among the largest
+            j = LengthStats::kTop;
         }
-        while (j > 0 && top[j - 1] < x) {
-            top[j] = top[j - 1];
+        while (j > 0 && ls.top[j - 1] < x) {
+            ls.top[j] = ls.top[j - 1];
             --j;
         }
-        top[j] = x;
+        ls.top[j] = x;
     }
-    const double wide = std::max((double)top[0], rest / (double)cus);
-    double best = wide;
+    return ls;
+}
+
+// How many of the longest sequences run on 32-column workgroups (chunked prefill without split
+// sequences; host lengths needed), and the modelled time in chunk periods.  Such a workgroup has
+// two column waves instead of four and takes ~0.87 of the time per chunk when every compute
+// unit runs the kernel, ~0.95 beside the rest of a packed batch (both measured on MI355X; the
+// model takes 0.95), so a sequence that would outlast the rest of the batch finishes sooner on
+// twice the workgroups while the others share the remaining compute units.  The n longest are
+// narrowed for the n that minimises
+//   max(0.95 c_0, c_n, rest / (CUs - 2 n u)),  u = HV dv / 64 workgroups per sequence,
+// c_i the chunk counts longest first and rest the 64-column work of the others, provided the
+// narrow workgroups use at most half the units and the model gains at least 3% over
+// max(c_0, work / CUs).
+int32_t narrow_sequences(const LengthStats &ls, int32_t N, int64_t u, int64_t cus, double *t_out) {
+    const double wide = std::max((double)ls.top[0], ls.work / (double)cus);
+    double best = wide, rest = ls.work;
     int32_t n_best = 0;
-    for (int32_t n = 1; n <= N && n <= kTop && 4 * n * u <= cus; ++n) {
-        rest -= (double)top[n - 1] * (double)u;
-        const double longest_wide = n < ntop ? (double)top[n] : 0.0;
-        const double t = std::max(std::max(0.95 * (double)top[0], longest_wide), rest / (double)(cus - 2 * n * u));
+    for (int32_t n = 1; n <= N && n <= LengthStats::kTop && 4 * n * u <= cus; ++n) {
+        rest -= (double)ls.top[n - 1] * (double)u;
+        const double longest_wide = n < ls.ntop ? (double)ls.top[n] : 0.0;
+        const double t = std::max(std::max(0.95 * (double)ls.top[0], longest_wide), rest / (double)(cus - 2 * n * u));
         if (t < best) {
             best = t;
             n_best = n;
         }
     }
-    return best <= 0.97 * wide ? n_best : 0;
+    if (best > 0.97 * wide) {
+        best = wide;
+        n_best = 0;
+    }
+    if (t_out) *t_out = best;
+    return n_best;
 }
 
 // Sequences on 32-column workgroups for an unsplit chunked prefill: all of them when their
@@ -272,30 +291,109 @@ int32_t narrow_sequences(const int32_t *cu_host, int32_t N, int32_t HV, int32_t 
 // else the host rule above, which needs the host lengths and a longest-first launch order.
 int32_t narrow_for_batch(int32_t N, int32_t HV, int32_t dv, const int32_t *cu_host, bool longest_first) {
     const int64_t cus = device_cus();
-    if ((int64_t)N * HV * (dv / 64) * 2 <= cus) return N;
-    return (cu_host && longest_first) ? narrow_sequences(cu_host, N, HV, dv, cus) : 0;
+    const int64_t u = (int64_t)HV * (dv / 64);
+    if ((int64_t)N * u * 2 <= cus) return N;
+    if (!cu_host || !longest_first || N <= 0 || u <= 0) return 0;
+    return narrow_sequences(length_stats(cu_host, N, u), N, u, cus, nullptr);
+}
+
+// The longest sequence of a packed batch alone cut into segments (ns = 1), for the batch the
+// sizes alone leave unsplit, when its host lengths are known and the launch order is longest
+// first.  With c_0, c_1 the two largest chunk counts, u (um) the sequence's 64-column
+// workgroups (with dk extra columns) and rest the other sequences' work, the model is
+//   map pass:     max(w0 a, c_1, (rest + (P-2) um a) / (CUs - u)), a = ceil(c_0 / (P - 1 + w0))
+//                 (segment 0 on u units; the maps, launched first, and the others on the rest),
+//   segment pass: ceil((P-1) u / CUs) a,
+// plus the chain and the fixed 3 as above.  Taken where it gains 3% over the unsplit plan.
+SplitPlan split_longest(const LengthStats &ls, int32_t HV, int32_t dk, int32_t dv, int64_t cus, double t_unsplit) {
+    SplitPlan best;
+    const int64_t u = (int64_t)HV * (dv / 64), um = (int64_t)HV * ((dv + dk) / 64);
+    if (ls.ntop < 2 || u <= 0 || 2 * u > cus) return best;
+    const int64_t c0 = ls.top[0], c1 = ls.top[1];
+    const double rest = ls.work - (double)c0 * (double)u;
+    const double step = chain_step(1, HV, dv, cus);
+    double t_best = 0.97 * t_unsplit;
+    for (int32_t P = 3; P <= 16; ++P)
+        for (int32_t w0 = 1; w0 <= 16; ++w0) {
+            const int64_t a = (c0 + P - 2 + w0) / (P - 1 + w0);
+            const double pass1 = std::max(std::max((double)(w0 * a), (double)c1),
+                                          (rest + (double)((P - 2) * um * a)) / (double)(cus - u));
+            const double pass2 = (double)((((P - 1) * u + cus - 1) / cus) * a);
+            const double t = pass1 + pass2 + (P - 2) * step + 3.0;
+            if (t < t_best) {
+                t_best = t;
+                best.P = P;
+                best.w0 = w0;
+                best.ns = 1;
+            }
+        }
+    return best;
+}
+
+// The plan for a batch whose host lengths are known and whose launch order is longest first:
+// the sizes' plan where it splits, else the longest sequence split where that pays, else the
+// narrow rule.
+struct LengthPlan {
+    SplitPlan split;
+    int32_t narrow = 0;
+};
+
+LengthPlan plan_for_lengths(int32_t N, int64_t total_T, const int32_t *cu_host, int32_t HV, int32_t dk, int32_t dv,
+                            gdn_dtype dtype) {
+    LengthPlan lp;
+    lp.split = split_plan(N, total_T, HV, dk, dv, dtype);
+    if (lp.split.P > 1 || N <= 0 || HV <= 0 || !gdn::prefill_chunked_supported(dk, dv, dtype == GDN_BF16))
+        return lp;
+    const int64_t cus = device_cus();
+    const int64_t u = (int64_t)HV * (dv / 64);
+    if ((int64_t)N * u * 2 <= cus) {
+        lp.narrow = N;
+        return lp;
+    }
+    const LengthStats ls = length_stats(cu_host, N, u);
+    double t_unsplit = 0.0;
+    lp.narrow = narrow_sequences(ls, N, u, cus, &t_unsplit);
+    const SplitPlan sl = split_longest(ls, HV, dk, dv, cus, t_unsplit);
+    if (sl.P > 1) {
+        lp.split = sl;
+        lp.narrow = 0;
+    }
+    return lp;
 }
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Workspace parts: the longest-first order, then (split sequences) the segment maps and
-// the segment start tables.
+// the segment start tables of the split ranks.
 struct WorkspacePlan {
     size_t order = 0, maps = 0, starts = 0;
     SplitPlan split;
     size_t total() const { return order + maps + starts; }
 };
 
-WorkspacePlan workspace_plan(int32_t N, int64_t total_T, int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype) {
+WorkspacePlan workspace_for(int32_t N, int32_t HV, int32_t dk, int32_t dv, SplitPlan sp) {
     WorkspacePlan w;
     if (N > 1 && N <= gdn::kMaxOrderedSequences) w.order = round256((size_t)N * 4);
-    w.split = split_plan(N, total_T, HV, dk, dv, dtype);
-    const int32_t P = w.split.P;
-    if (P > 1) {
-        w.maps = round256((size_t)N * (P - 2) * HV * dk * (dv + dk) * 4);
-        w.starts = round256((size_t)N * (P - 1) * HV * dk * dv * 4);
+    w.split = sp;
+    if (sp.P > 1) {
+        w.maps = round256((size_t)sp.ns * (sp.P - 2) * HV * dk * (dv + dk) * 4);
+        w.starts = round256((size_t)sp.ns * (sp.P - 1) * HV * dk * dv * 4);
     }
     return w;
+}
+
+WorkspacePlan workspace_plan(int32_t N, int64_t total_T, int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype) {
+    return workspace_for(N, HV, dk, dv, split_plan(N, total_T, HV, dk, dv, dtype));
+}
+
+// Whether the launch order of a batch with these host lengths is longest first: the order
+// kernel sorts batches of up to kMaxOrderedSequences; larger ones run in the given order.
+bool launches_longest_first(const int32_t *cu_host, int32_t N) {
+    if (!cu_host) return false;
+    if (N <= gdn::kMaxOrderedSequences) return true;
+    for (int32_t i = 1; i < N; ++i)
+        if (cu_host[i + 1] - cu_host[i] > cu_host[i] - cu_host[i - 1]) return false;
+    return true;
 }
 
 gdn_status hip_status(hipError_t e, const char *what) {
@@ -374,7 +472,7 @@ gdn_status run_prefill(const void *q, const void *k, const void *v, const float 
         st = check_disjoint(outs, 3, ins, 11, "S_T", "S0");
         if (st != GDN_OK) return st;
     }
-    const WorkspacePlan plan = workspace_plan(N, total_T, HV, dk, dv, dtype);
+    WorkspacePlan plan = workspace_plan(N, total_T, HV, dk, dv, dtype);
     const size_t need = plan.total();
     if (use_scratch) {
         if (need > kStaticScratchBytes)
@@ -417,22 +515,36 @@ gdn_status run_prefill(const void *q, const void *k, const void *v, const float 
                        variant_delta(variant) ? 1 : 0};
     a.gate = gate_args(ops, variant);
     const bool bf16 = dtype == GDN_BF16;
-    // sequences on 32-column workgroups (all of a batch that fills at most half the units; else
-    // the longest, when the host lengths are known and the launch order is longest first)
+    const bool longest_first = order || sorted;
+    if (plan.split.P == 1 && gdn::prefill_chunked_supported(dk, dv, bf16)) {
+        // sequences on 32-column workgroups (all of a batch that fills at most half the units;
+        // else the longest, when the host lengths are known and the launch order is longest first)
+        a.narrow = narrow_for_batch(N, HV, dv, cu_seqlens ? cu_seqlens_host : nullptr, longest_first);
+        // or, where that pays, the longest sequence split, if the workspace holds its maps and
+        // start tables (gdn_prefill_workspace_size_lens)
+        if (cu_seqlens && cu_seqlens_host && longest_first && workspace) {
+            const LengthPlan lp = plan_for_lengths(N, total_T, cu_seqlens_host, HV, dk, dv, dtype);
+            const WorkspacePlan wl = workspace_for(N, HV, dk, dv, lp.split);
+            if (lp.split.P > 1 && wl.total() <= workspace_bytes) {
+                plan = wl;
+                a.narrow = 0;
+            }
+        }
+    }
     const int32_t P = plan.split.P;
-    if (P == 1 && gdn::prefill_chunked_supported(dk, dv, bf16))
-        a.narrow = narrow_for_batch(N, HV, dv, cu_seqlens ? cu_seqlens_host : nullptr, order || sorted);
     if (P > 1) {
-        // split sequences: segment 0 and the other segments' maps, their chain, then segments
-        // 1 .. P-1 from their start tables
+        // split sequences: segment 0 of the split ranks (and the other sequences whole) beside
+        // the maps of their middle segments, the chain, then segments 1 .. P-1 from their start
+        // tables
         float *maps = reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.order);
         float *starts = reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.order + plan.maps);
-        a.split = gdn::SplitArgs{P, 1, plan.split.w0, maps, starts};
+        const int32_t ns = plan.split.ns;
+        a.split = gdn::SplitArgs{P, 1, plan.split.w0, ns, maps, starts};
         st = hip_status(gdn::launch_prefill_chunked(a, stream), "chunked prefill (segment maps) launch");
         if (st == GDN_OK)
-            st = hip_status(gdn::launch_split_chain(maps, starts, N, P, HV, dv, stream), "segment chain launch");
+            st = hip_status(gdn::launch_split_chain(maps, starts, ns, P, HV, dv, stream), "segment chain launch");
         if (st == GDN_OK) {
-            a.split = gdn::SplitArgs{P, 2, plan.split.w0, maps, starts};
+            a.split = gdn::SplitArgs{P, 2, plan.split.w0, ns, maps, starts};
             st = hip_status(gdn::launch_prefill_chunked(a, stream), "chunked prefill (segments) launch");
         }
     } else if (gdn::prefill_chunked_supported(dk, dv, bf16)) {
@@ -635,23 +747,32 @@ int32_t gdn_prefill_narrow_count(int32_t N, int64_t total_T, const int32_t *cu_s
     (void)HQK;
     if (N <= 0 || HV <= 0 || total_T < 0 || !gdn::prefill_chunked_supported(dk, dv, dtype == GDN_BF16)) return 0;
     if (split_plan(N, total_T, HV, dk, dv, dtype).P > 1) return 0;
-    // host lengths give the longest-first order the launch uses (sorted on the host or by the
-    // order kernel); a batch too large for the order array keeps the rule off unless sorted
-    bool longest_first = cu_seqlens_host != nullptr;
-    if (longest_first && N > gdn::kMaxOrderedSequences)
-        for (int32_t i = 1; i < N && longest_first; ++i)
-            longest_first = cu_seqlens_host[i + 1] - cu_seqlens_host[i] <= cu_seqlens_host[i] - cu_seqlens_host[i - 1];
-    return narrow_for_batch(N, HV, dv, cu_seqlens_host, longest_first);
+    if (cu_seqlens_host && launches_longest_first(cu_seqlens_host, N)) {
+        const LengthPlan lp = plan_for_lengths(N, total_T, cu_seqlens_host, HV, dk, dv, dtype);
+        return lp.split.P > 1 ? 0 : lp.narrow;
+    }
+    return narrow_for_batch(N, HV, dv, nullptr, false);
 }
 
-const char *gdn_prefill_kernel_name(int32_t N, int64_t total_T, int32_t HQK, int32_t HV, int32_t dk,
-                                    int32_t dv, gdn_dtype dtype) {
+size_t gdn_prefill_workspace_size_lens(int32_t N, int64_t total_T, const int32_t *cu_seqlens_host, int32_t HQK,
+                                       int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype) {
+    const size_t base = gdn_prefill_workspace_size(N, total_T, HQK, HV, dk, dv, dtype);
+    if (N <= 0 || total_T < 0 || HV <= 0 || !cu_seqlens_host || !launches_longest_first(cu_seqlens_host, N))
+        return base;
+    const LengthPlan lp = plan_for_lengths(N, total_T, cu_seqlens_host, HV, dk, dv, dtype);
+    const size_t with = workspace_for(N, HV, dk, dv, lp.split).total();
+    return with > base ? with : base;
+}
+
+const char *gdn_prefill_kernel_name(int32_t N, int64_t total_T, const int32_t *cu_seqlens_host, int32_t HQK,
+                                    int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype) {
     (void)HQK;
-    if (gdn::prefill_chunked_supported(dk, dv, dtype == GDN_BF16))
-        return (N > 0 && HV > 0 && total_T >= 0 && split_plan(N, total_T, HV, dk, dv, dtype).P > 1)
-                   ? "prefill_chunked_split"
-                   : "prefill_chunked";
-    return "prefill_recurrent";
+    if (!gdn::prefill_chunked_supported(dk, dv, dtype == GDN_BF16)) return "prefill_recurrent";
+    if (N <= 0 || HV <= 0 || total_T < 0) return "prefill_chunked";
+    bool split = split_plan(N, total_T, HV, dk, dv, dtype).P > 1;
+    if (!split && cu_seqlens_host && launches_longest_first(cu_seqlens_host, N))
+        split = plan_for_lengths(N, total_T, cu_seqlens_host, HV, dk, dv, dtype).split.P > 1;
+    return split ? "prefill_chunked_split" : "prefill_chunked";
 }
 
 }  // extern "C"

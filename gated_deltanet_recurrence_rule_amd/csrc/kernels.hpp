@@ -17,15 +17,17 @@ struct GateArgs {
     int32_t alpha_sigmoid = 0;
 };
 
-// Split sequences for the chunked prefill (see prefill_chunked.hip): P >= 3 segments per
-// sequence, segment 0 w0 times as long as each of the others; mode 0 = no split, 1 = map pass
-// (segment 0 scanned from S0 into starts, segments 1 .. P-2 into maps), 2 = segment pass
-// (segments 1 .. P-1 from starts).  maps = [N][P - 2][HV][DK][DV + DK], starts =
-// [N][P - 1][HV][DK][DV] (the start tables of segments 1 .. P-1).
+// Split sequences for the chunked prefill (see prefill_chunked.hip): the first ns launch ranks
+// are cut into P >= 3 segments, segment 0 w0 times as long as each of the others; mode 0 = no
+// split, 1 = map pass (every sequence scanned from S0, a split rank's only through segment 0,
+// whose end goes to starts; segments 1 .. P-2 of the split ranks into maps), 2 = segment pass
+// (segments 1 .. P-1 of the split ranks from starts).  maps = [ns][P - 2][HV][DK][DV + DK],
+// starts = [ns][P - 1][HV][DK][DV] (the start tables of segments 1 .. P-1), both by rank.
 struct SplitArgs {
     int32_t P = 1;
     int32_t mode = 0;
     int32_t w0 = 1;
+    int32_t ns = 0;
     float *maps = nullptr;
     float *starts = nullptr;
 };
@@ -116,10 +118,10 @@ constexpr int32_t kMaxOrderedSequences = 16384;
 
 // Chunked MFMA prefill: bf16 I/O, dk = 128, dv a multiple of 64.
 bool prefill_chunked_supported(int dk, int dv, bool bf16);
-// Start tables of split sequences: the map pass wrote segment 1's (starts[n][0], the end of
-// segment 0); segment j + 1 starts at M_j S_in(j) + B_j with [B_j | M_j] = maps[n][j - 1],
+// Start tables of the ns split ranks: the map pass wrote segment 1's (starts[r][0], the end of
+// segment 0); segment j + 1 starts at M_j S_in(j) + B_j with [B_j | M_j] = maps[r][j - 1],
 // j = 1 .. P-2 (dk = 128).
-hipError_t launch_split_chain(const float *maps, float *starts, int32_t N, int32_t P, int32_t HV, int32_t dv,
+hipError_t launch_split_chain(const float *maps, float *starts, int32_t ns, int32_t P, int32_t HV, int32_t dv,
                               hipStream_t stream);
 hipError_t launch_prefill_chunked(const PrefillArgs &a, hipStream_t stream);
 

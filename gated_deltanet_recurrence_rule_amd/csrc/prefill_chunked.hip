@@ -277,43 +277,49 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     // numbered in launch order (sequence rank, segment, then QK head); ids past the last
     // group exit.
     //
-    // The grid has two parts, each numbered as above.  Unsplit (mode 0), the first part holds the
-    // nfirst longest sequences on narrow workgroups of 32 columns in which only column waves 0
-    // and 1 hold columns (a chunk then takes ~0.87-0.95 of the time: the column waves' LDS
-    // reads of K and Q are halved per CU), so a sequence that would outlast the rest of the
-    // batch finishes sooner on twice the workgroups; the second part holds the other sequences
-    // on 64-column workgroups.
-    //
-    // Split sequences (P = sp.P >= 3 segments of whole chunks per sequence; with cps =
-    // ceil(chunks / (P - 1 + w0)), segment 0 is w0 cps chunks long and segment s >= 1 takes
-    // chunks [(w0 + s - 1) cps, (w0 + s) cps)):
-    //  * map pass (sp.mode 1): the first part scans segment 0 of every sequence (nfirst = N)
-    //    from S0 on 64-column workgroups, writing its reads; its final table, segment 1's start,
-    //    goes to sp.starts.  The second part runs segments 1 .. P-2 with the table widened to
-    //    DW = DV + DK columns, started at [0 | I], the extra columns reading v = 0.  Each column
-    //    of the table evolves on its own and affinely in the start state, so the segment's
-    //    final table is [B | M] with S_out = M S_in + B.  Reads are not stored; the final table
-    //    goes to sp.maps, [P - 2 segments][HV][DK][DW] per sequence.
-    //  * segment pass (sp.mode 2): segments 1 .. P-1 start from sp.starts, [P - 1][HV][DK][DV]
-    //    per sequence (the first written by the map pass, the others chained from the maps),
-    //    write their reads, and the last segment writes S_T.
+    // The grid has up to three parts, each numbered as above, launched in this order.
+    //  * Unsplit (mode 0): part 0 holds the nfirst longest sequences on narrow workgroups of 32
+    //    columns in which only column waves 0 and 1 hold columns (a chunk then takes ~0.87-0.95
+    //    of the time: the column waves' LDS reads of K and Q are halved per CU), so a sequence
+    //    that would outlast the rest of the batch finishes sooner on twice the workgroups; part
+    //    2 holds the other sequences on 64-column workgroups.
+    //  * Split sequences: the first sp.ns launch ranks (every sequence of a small batch, or the
+    //    longest of a packed one) are cut into P = sp.P >= 3 segments of whole chunks; with cps =
+    //    ceil(chunks / (P - 1 + w0)), segment 0 is w0 cps chunks long and segment s >= 1 takes
+    //    chunks [(w0 + s - 1) cps, (w0 + s) cps).
+    //    - map pass (sp.mode 1): part 0 scans segment 0 of the split ranks from S0, writing its
+    //      reads; its final table, segment 1's start, goes to sp.starts.  Part 1 runs segments
+    //      1 .. P-2 of the split ranks with the table widened to DW = DV + DK columns, started at
+    //      [0 | I], the extra columns reading v = 0.  Each column of the table evolves on its own
+    //      and affinely in the start state, so the segment's final table is [B | M] with
+    //      S_out = M S_in + B.  Reads are not stored; the final table goes to sp.maps,
+    //      [P - 2 segments][HV][DK][DW] per split rank.  Part 2 runs the other sequences whole.
+    //      Segment 0 goes first: it is the longest stretch of the pass's critical path.
+    //    - segment pass (sp.mode 2): part 2 runs segments 1 .. P-1 of the split ranks from
+    //      sp.starts, [P - 1][HV][DK][DV] per split rank (the first written by the map pass,
+    //      the others chained from the maps), writing their reads; the last writes S_T.
     const int HQK = HV / rep;
     const int mode = SPLIT ? sp.mode : 0;
-    const int PS = mode == 1 ? sp.P - 2 : (mode == 2 ? sp.P - 1 : 1);  // segments per sequence, second part
-    const int NGa = (mode == 2 ? 0 : nfirst) * HQK;                    // groups in the first part
-    const int Ma = rep * (DV / (SPLIT ? DVS : DVS / 2));               // workgroups per group there
-    const int Wa = 8 * Ma * ((NGa + 7) / 8);                           // its size (a multiple of 8)
-    const bool first = (int)blockIdx.x < Wa;
-    const bool narrow = !SPLIT && first;
-    const bool mapwg = SPLIT && mode == 1 && !first;  // a segment map
-    const int DW = mapwg ? DV + DK : DV;                // table width
-    const int Lid = first ? (int)blockIdx.x : (int)blockIdx.x - Wa;
-    const int Mg = first ? Ma : M;
+    const int ns = SPLIT ? sp.ns : 0;
+    const int PS = mode == 1 ? sp.P - 2 : (mode == 2 ? sp.P - 1 : 1);  // segments per split rank in a segment part
+    const int NG0 = mode == 0 ? nfirst * HQK : (mode == 1 ? ns * HQK : 0);  // groups of part 0
+    const int M0 = rep * (DV / (SPLIT ? DVS : DVS / 2));                     // workgroups per group there
+    const int NG1 = mode == 1 ? ns * PS * HQK : 0;                           // part 1 (segment maps)
+    const int M1 = rep * ((DV + DK) / DVS);
+    const int W0 = 8 * M0 * ((NG0 + 7) / 8), W1 = 8 * M1 * ((NG1 + 7) / 8);  // part sizes (multiples of 8)
+    const int part = (int)blockIdx.x < W0 ? 0 : ((int)blockIdx.x < W0 + W1 ? 1 : 2);
+    const bool narrow = !SPLIT && part == 0;
+    const bool mapwg = part == 1;                   // a segment map
+    const int DW = mapwg ? DV + DK : DV;            // table width
+    const int Lid = (int)blockIdx.x - (part >= 1 ? W0 : 0) - (part == 2 ? W1 : 0);
+    const int Mg = part == 0 ? M0 : (part == 1 ? M1 : M);
     const int G = 8 * ((Lid >> 3) / Mg) + (Lid & 7);
-    if (G >= (first ? NGa : NG)) return;
+    if (G >= (part == 0 ? NG0 : (part == 1 ? NG1 : NG))) return;
     const int mem = (Lid >> 3) % Mg;
-    const int rank = first ? G / HQK : (mode == 0 ? nfirst : 0) + G / (PS * HQK);
-    const int seg = (first || mode == 0) ? 0 : 1 + (G / HQK) % PS;
+    const bool segpart = mapwg || mode == 2;        // groups run segments 1 .. of split ranks
+    const int rank = (part == 2 && mode != 2 ? (mode == 0 ? nfirst : ns) : 0) + G / ((segpart ? PS : 1) * HQK);
+    const int seg = segpart ? 1 + (G / HQK) % PS : 0;
+    const bool splitseq = mode != 0 && rank < ns;    // this sequence is cut into segments
     const int hq = G % HQK;
     const int nseq = order ? order[rank] : rank;
     const int slw = narrow ? DVS / 2 : DVS;         // columns per workgroup
@@ -338,7 +344,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         t0 = (int64_t)nseq * span;
         t1 = t0 + span;
     }
-    if (mode != 0) {
+    if (splitseq) {
         // segment seg: units [seg == 0 ? 0 : w0 + seg - 1, w0 + seg) of cps chunks each, cps =
         // ceil(chunks / (P - 1 + w0))
         const int64_t len = t1 - t0;
@@ -468,14 +474,14 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
         // start table (row stride DW) and where the final table goes
         const float *Sin = S0 ? S0 + (size_t)unit * DK * DV : nullptr;
         float *Sout = S_T ? S_T + (size_t)unit * DK * DV : nullptr;
-        if (mode == 1 && !mapwg) {
-            // segment 0 from S0; its end is segment 1's start
-            Sout = sp.starts + ((size_t)nseq * (sp.P - 1) * HV + h) * DK * DV;
-        } else if (mode == 1) {
+        if (mapwg) {
             Sin = nullptr;
-            Sout = sp.maps + ((size_t)(nseq * (sp.P - 2) + seg - 1) * HV + h) * DK * DW;
+            Sout = sp.maps + ((size_t)(rank * (sp.P - 2) + seg - 1) * HV + h) * DK * DW;
+        } else if (mode == 1 && splitseq) {
+            // segment 0 from S0; its end is segment 1's start
+            Sout = sp.starts + ((size_t)rank * (sp.P - 1) * HV + h) * DK * DV;
         } else if (mode == 2) {
-            Sin = sp.starts + ((size_t)(nseq * (sp.P - 1) + seg - 1) * HV + h) * DK * DV;
+            Sin = sp.starts + ((size_t)(rank * (sp.P - 1) + seg - 1) * HV + h) * DK * DV;
             if (seg != sp.P - 1) Sout = nullptr;
         }
 #pragma unroll
@@ -1155,18 +1161,24 @@ hipError_t launch_prefill_chunked(const PrefillArgs &a, hipStream_t stream) {
     if (a.N == 0) return hipSuccess;
     const int rep = a.HV / a.HQK;
     const int mode = a.split.mode;
-    if (mode != 0 && (a.split.P < 3 || a.split.w0 < 1)) return hipErrorInvalidValue;
+    const int ns = mode == 0 ? 0 : a.split.ns;
+    if (mode != 0 && (a.split.P < 3 || a.split.w0 < 1 || ns < 1 || ns > a.N)) return hipErrorInvalidValue;
     const int PS = mode == 1 ? a.split.P - 2 : (mode == 2 ? a.split.P - 1 : 1);
-    const int DW = mode == 1 ? a.dv + DK : a.dv;
-    // first part of the grid: the narrow sequences (unsplit) or every sequence's segment 0 (map pass)
-    const int nfirst = mode == 0 ? a.narrow : (mode == 1 ? a.N : 0);
+    const int nfirst = mode == 0 ? a.narrow : 0;  // narrow sequences (unsplit)
     if (nfirst < 0 || nfirst > a.N) return hipErrorInvalidValue;
-    const int64_t NG = (int64_t)(mode == 0 ? a.N - nfirst : a.N) * PS * a.HQK;  // second part's groups
-    const int64_t M = (int64_t)rep * (DW / DVS);                                // workgroups per group
-    const int64_t NGa = (int64_t)(mode == 2 ? 0 : nfirst) * a.HQK;              // first part's groups
-    const int64_t Ma = (int64_t)rep * (a.dv / (mode == 0 ? DVS / 2 : DVS));
-    const int64_t nwg = 8 * Ma * ((NGa + 7) / 8) + 8 * M * ((NG + 7) / 8);
-    if (nwg > 0x7fffffffLL || NG > 0x7fffffffLL || NGa > 0x7fffffffLL) return hipErrorInvalidValue;
+    // part 0: the narrow sequences (unsplit) or the split ranks' segment 0 (map pass); part 1:
+    // the split ranks' segment maps; part 2, 64-column workgroups: the other sequences, or the
+    // split ranks' segments 1 .. P-1 (segment pass)
+    const int64_t NG0 = mode == 0 ? (int64_t)nfirst * a.HQK : (mode == 1 ? (int64_t)ns * a.HQK : 0);
+    const int64_t M0 = (int64_t)rep * (a.dv / (mode == 0 ? DVS / 2 : DVS));
+    const int64_t NG1 = mode == 1 ? (int64_t)ns * PS * a.HQK : 0;
+    const int64_t M1 = (int64_t)rep * ((a.dv + DK) / DVS);
+    const int64_t NG = mode == 0 ? (int64_t)(a.N - nfirst) * a.HQK
+                                 : (mode == 1 ? (int64_t)(a.N - ns) * a.HQK : (int64_t)ns * PS * a.HQK);
+    const int64_t M = (int64_t)rep * (a.dv / DVS);
+    const int64_t nwg = 8 * M0 * ((NG0 + 7) / 8) + 8 * M1 * ((NG1 + 7) / 8) + 8 * M * ((NG + 7) / 8);
+    if (nwg > 0x7fffffffLL || NG > 0x7fffffffLL || NG0 > 0x7fffffffLL || NG1 > 0x7fffffffLL)
+        return hipErrorInvalidValue;
     auto kern = a.split.mode != 0 ? (a.delta ? prefill_chunked_kernel<true, true> : prefill_chunked_kernel<false, true>)
                                   : (a.delta ? prefill_chunked_kernel<true, false> : prefill_chunked_kernel<false, false>);
     hipLaunchKernelGGL(kern, dim3((unsigned)nwg),

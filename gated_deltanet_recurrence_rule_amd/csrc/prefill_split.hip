@@ -9,7 +9,7 @@
 // start tables of segments 2 .. P-1; the segment pass then runs segments 1 .. P-1 at once
 // from their tables.
 //
-// One workgroup per (sequence, V head, 8 columns of dv): columns of the table evolve
+// One workgroup per (split sequence, V head, 8 columns of dv): columns of the table evolve
 // independently, so a column block chains on its own.  Per step it stages M (128 x 128
 // fp32, rows padded to 132 floats so that 16 rows read in one wave fall in distinct
 // banks) in LDS, the next step's M already on its way in registers; each thread forms
@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void split_chain_kernel(const float *__restric
                                                           int P, int HV, int DV) {
     __shared__ __attribute__((aligned(16))) float Ms[SDK * SLM];
     __shared__ __attribute__((aligned(16))) float Sb[SDK * SCB];
-    const int unit = blockIdx.x;  // n * HV + h
+    const int unit = blockIdx.x;  // rank * HV + h
     const int n = unit / HV, h = unit % HV;
     const int c0 = blockIdx.y * SCB;
     const int DW = DV + SDK;
@@ -89,11 +89,11 @@ __global__ __launch_bounds__(256) void split_chain_kernel(const float *__restric
 
 }  // namespace
 
-hipError_t launch_split_chain(const float *maps, float *starts, int32_t N, int32_t P, int32_t HV, int32_t dv,
+hipError_t launch_split_chain(const float *maps, float *starts, int32_t ns, int32_t P, int32_t HV, int32_t dv,
                               hipStream_t stream) {
-    if (N == 0 || P < 3) return hipSuccess;
-    if (dv % SCB != 0 || (int64_t)N * HV > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(split_chain_kernel, dim3((unsigned)(N * HV), (unsigned)(dv / SCB)), dim3(256), 0, stream,
+    if (ns == 0 || P < 3) return hipSuccess;
+    if (dv % SCB != 0 || (int64_t)ns * HV > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(split_chain_kernel, dim3((unsigned)(ns * HV), (unsigned)(dv / SCB)), dim3(256), 0, stream,
                        maps, starts, P, HV, dv);
     return hipGetLastError();
 }

@@ -156,6 +156,23 @@ size_t gdn_prefill_workspace_size(int32_t N, int64_t total_T, int32_t HQK, int32
                                   int32_t dk, int32_t dv, gdn_dtype dtype);
 
 /*
+ * gdn_prefill_workspace_size_lens -- the workspace for a packed batch whose host lengths are
+ * known (cu_seqlens_host, N + 1 int32 entries, read during the call only; NULL gives
+ * gdn_prefill_workspace_size).  At least gdn_prefill_workspace_size; more where the batch,
+ * unsplit by its sizes, has one sequence that would outlast the rest (the 262144-token
+ * sequence of a 65-sequence batch): a model of the time in chunk periods may then cut that
+ * sequence alone into P segments as above.  Its first segment is scanned while the other
+ * sequences run whole, beside the maps of its middle segments.  The extra part holds
+ * (P-2) HV dk (dv + dk) + (P-1) HV dk dv floats (20 MiB for that batch with 32 heads of
+ * d = 128, P = 5).  gdn_prefill, given the host lengths and a workspace of this size, takes
+ * that plan; given a smaller one of at least gdn_prefill_workspace_size bytes, it runs the
+ * batch unsplit, with the same results to rounding.  Launch order longest first is assumed:
+ * batches of more than 16384 sequences qualify only with non-increasing lengths.
+ */
+size_t gdn_prefill_workspace_size_lens(int32_t N, int64_t total_T, const int32_t *cu_seqlens_host, int32_t HQK,
+                                       int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype);
+
+/*
  * gdn_prefill -- run whole sequences of a packed batch (the handbook's
  * delta_rule(q, k, v, g, beta, S) -> (out, S) over a batch of sequences).
  *
@@ -182,7 +199,10 @@ size_t gdn_prefill_workspace_size(int32_t N, int64_t total_T, int32_t HQK, int32
  *   S_T         [N, HV, dk, dv] fp32, out: final tables, or NULL to skip.
  *               S_T may be the same pointer as S0 (in-place carry).
  *   workspace   device scratch of at least gdn_prefill_workspace_size() bytes,
- *               16-byte aligned (may be NULL when that size is 0).
+ *               16-byte aligned (may be NULL when that size is 0).  With the host
+ *               lengths given and workspace_bytes at least
+ *               gdn_prefill_workspace_size_lens(), a batch with one sequence that
+ *               would outlast the rest may run with that sequence split.
  *
  * Overlaps: o, S_T and the workspace (all workspace_bytes of it) are written, so each
  * must be disjoint from the others and from every input (q, k, v, g, beta, S0,
@@ -337,21 +357,25 @@ gdn_status gdn_gated_rmsnorm(const void *x, const void *z, const float *w, float
                              int64_t rows, int32_t dv, gdn_dtype dtype, hipStream_t stream);
 
 /*
- * gdn_prefill_kernel_name -- which kernel gdn_prefill runs for these sizes
- * (static text, for profiling and reports):
+ * gdn_prefill_kernel_name -- which kernel gdn_prefill runs for these sizes (static text, for
+ * profiling and reports), with a workspace of gdn_prefill_workspace_size_lens bytes where
+ * cu_seqlens_host (N + 1 int32 entries, read during the call only) is given, else of
+ * gdn_prefill_workspace_size bytes:
  *   "prefill_chunked"    bf16, dk = 128, dv a multiple of 64: chunks of 64 tokens
  *                        on bf16 MFMA with an fp32 table;
  *   "prefill_chunked_split"  the same kernel over split sequences (see
- *                        gdn_prefill_workspace_size), plus the chaining kernel;
+ *                        gdn_prefill_workspace_size and gdn_prefill_workspace_size_lens),
+ *                        plus the chaining kernel;
  *   "prefill_recurrent"  every other case: token-serial, fp32 arithmetic.
  */
-const char *gdn_prefill_kernel_name(int32_t N, int64_t total_T, int32_t HQK, int32_t HV,
-                                    int32_t dk, int32_t dv, gdn_dtype dtype);
+const char *gdn_prefill_kernel_name(int32_t N, int64_t total_T, const int32_t *cu_seqlens_host, int32_t HQK,
+                                    int32_t HV, int32_t dk, int32_t dv, gdn_dtype dtype);
 
 /*
  * gdn_prefill_narrow_count -- how many sequences gdn_prefill runs on workgroups of 32 value
  * columns instead of 64 (informational, for profiling and tests; it changes only the speed,
- * never the outputs).  Applies to "prefill_chunked" (not to split sequences):
+ * never the outputs), with a workspace of gdn_prefill_workspace_size_lens bytes where the host
+ * lengths are given.  Applies to "prefill_chunked" (not to split sequences):
  *   - every sequence, when the batch's 64-column workgroups (N x HV x dv / 64) would fill at
  *     most half the current device's compute units: twice as many still fit, and each chunk
  *     takes ~0.87 of the time on a workgroup with two column waves;

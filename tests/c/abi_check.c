@@ -37,7 +37,7 @@ int main(void) {
     s = gdn_gated_rmsnorm(buf, buf + 1024, buf + 2048, -1.0f, buf, 4, 32, GDN_F32, 0);
     CHECK(s == GDN_ERR_VALUE, "gated norm rejects eps < 0");
     /* the split plan: one 8192-token sequence with 16 heads takes the split path */
-    CHECK(strcmp(gdn_prefill_kernel_name(1, 8192, 16, 16, 128, 128, GDN_BF16), "prefill_chunked_split") == 0,
+    CHECK(strcmp(gdn_prefill_kernel_name(1, 8192, NULL, 16, 16, 128, 128, GDN_BF16), "prefill_chunked_split") == 0,
           "kernel name of a split batch");
     printf("%s\n", fails ? "FAILED" : "all ok");
     return fails ? 1 : 0;

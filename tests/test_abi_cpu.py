@@ -401,7 +401,7 @@ def test_split_workspace_plan(lib):
         return (maps + 255) // 256 * 256 + (starts + 255) // 256 * 256
 
     assert lib.gdn_prefill_workspace_size(1, 8192, 16, 16, 128, 128, 0) == plan_bytes(1, 16, 9)
-    assert lib.gdn_prefill_kernel_name(1, 8192, 16, 16, 128, 128, 0) == b"prefill_chunked_split"
+    assert lib.gdn_prefill_kernel_name(1, 8192, None, 16, 16, 128, 128, 0) == b"prefill_chunked_split"
     # 24 chunks: P = 5 with w0 = 1 (3 maps fit one round), a = 5: 2 x 5 + 3 x 1.2 + 3 = 16.6
     # periods against 0.87 x 24 = 20.9
     assert lib.gdn_prefill_workspace_size(1, 1500, 16, 16, 128, 128, 0) == plan_bytes(1, 16, 5)
@@ -409,16 +409,16 @@ def test_split_workspace_plan(lib):
     assert lib.gdn_prefill_workspace_size(1, 1000, 16, 16, 128, 128, 0) == plan_bytes(1, 16, 4)
     # 7 chunks: nothing beats 0.87 x 7 once the fixed cost of the two extra launches is paid
     assert lib.gdn_prefill_workspace_size(1, 400, 16, 16, 128, 128, 0) == 0
-    assert lib.gdn_prefill_kernel_name(1, 400, 16, 16, 128, 128, 0) == b"prefill_chunked"
+    assert lib.gdn_prefill_kernel_name(1, 400, None, 16, 16, 128, 128, 0) == b"prefill_chunked"
     # 2 x 16384 tokens, 32 heads: u = 128, so the maps of one middle segment take 2 rounds of
     # the other 128 units: P = 3, w0 = 2, a = 64: 3 x 64 + 1.2 x 2 + 3 = 197.4 against 222.7
     # (the launch order takes the first 256 bytes)
     assert lib.gdn_prefill_workspace_size(2, 32768, 16, 32, 128, 128, 0) == 256 + plan_bytes(2, 32, 3)
-    assert lib.gdn_prefill_kernel_name(2, 32768, 16, 32, 128, 128, 0) == b"prefill_chunked_split"
+    assert lib.gdn_prefill_kernel_name(2, 32768, None, 16, 32, 128, 128, 0) == b"prefill_chunked_split"
     assert lib.gdn_prefill_narrow_count(2, 32768, None, 16, 32, 128, 128, 0) == 0
     # the 4 x 16384 batch fills the device (256 workgroups): no split
     assert lib.gdn_prefill_workspace_size(4, 65536, 16, 32, 128, 128, 0) == 256
-    assert lib.gdn_prefill_kernel_name(4, 65536, 16, 32, 128, 128, 0) == b"prefill_chunked"
+    assert lib.gdn_prefill_kernel_name(4, 65536, None, 16, 32, 128, 128, 0) == b"prefill_chunked"
     # a batch of more than half the units (3 x 16384, 32 heads: 192 workgroups) never splits
     assert lib.gdn_prefill_workspace_size(3, 49152, 16, 32, 128, 128, 0) == 256
     # fp32 runs the token-serial kernel: never split
@@ -426,11 +426,13 @@ def test_split_workspace_plan(lib):
 
 
 def test_narrow_workgroup_rule(lib):
-    """Host rule for 32-column workgroups (no GPU here: 256 compute units assumed).  The
-    packed batch of 65 sequences with one of 262144 tokens narrows that one; a batch whose
-    64-column workgroups fill at most half the units narrows all (host lengths or not);
-    uniform batches that fill more, two equally long sequences, split sequences, fp32, and a
-    large batch without host lengths narrow none."""
+    """Host rule for 32-column workgroups (no GPU here: 256 compute units assumed), as reported
+    for a workspace of gdn_prefill_workspace_size_lens bytes.  A batch whose 64-column
+    workgroups fill at most half the units narrows all (host lengths or not); of two long
+    sequences of similar length the longer is narrowed; a batch with one sequence that would
+    outlast the rest has that one split instead (0); uniform batches that fill more, two equally
+    long sequences, small split batches, fp32, and a large batch without host lengths narrow
+    none."""
     import ctypes
 
     def count(lens, HQK=16, HV=32, dk=128, dv=128, dtype=0, host=True):
@@ -439,10 +441,12 @@ def test_narrow_workgroup_rule(lib):
         return lib.gdn_prefill_narrow_count(len(lens), int(cu[-1]), ptr, HQK, HV, dk, dv, dtype)
 
     from gated_deltanet_recurrence_rule_amd import workloads as W
-    assert count(list(W.varlen_lengths())) == 1
-    assert count([262144] + [1000] * 10) == 1
-    assert count([8192, 1000, 300, 257]) == 1
-    assert count([300, 1000, 8192, 257]) == 1  # the rule does not need sorted lengths
+    assert count([10000, 9000, 300, 200]) == 1
+    assert count([200, 9000, 10000, 300]) == 1  # the rule does not need sorted lengths
+    assert count([4000] * 6 + [100] * 100, HQK=2, HV=4) == 6
+    assert count(list(W.varlen_lengths())) == 0  # its 262144-token sequence is split instead
+    assert count([262144] + [1000] * 10) == 0
+    assert count([8192, 1000, 300, 257]) == 0
     assert count([16384] * 4) == 0
     assert count([16384] * 3) == 0  # a third of the device idle, but no sequence outlasts the others
     assert count([32768, 32768, 100]) == 0  # the second long sequence would stay on 64 columns
@@ -450,7 +454,42 @@ def test_narrow_workgroup_rule(lib):
     assert count([8192, 100], host=False) == 2
     assert count([8192], HQK=16, HV=16) == 0  # 32 workgroups: split into 9 segments instead
     assert count([8192, 1000, 300, 257], dtype=1) == 0  # fp32: token-serial kernel
-    assert count([8192, 1000, 300, 257], host=False) == 0
+    assert count([10000, 9000, 300, 200], host=False) == 0
+
+
+def test_longest_sequence_split_plan(lib):
+    """With the host lengths, a packed batch that the sizes alone leave unsplit may have its
+    longest sequence cut into segments (no GPU here: 256 compute units assumed).
+    The 65-sequence batch (64 lengths of 128 .. 32768 tokens and one of 262144), 32 V heads of
+    d = 128: the model takes P = 5, so the workspace grows by 3 maps of 128 x 256 and 4 start
+    tables of 128 x 128 per head for that one sequence; the kernel is then the split one.
+    Batches with no dominant sequence keep gdn_prefill_workspace_size's plan."""
+    import ctypes
+    from gated_deltanet_recurrence_rule_amd import workloads as W
+
+    def sizes(lens, HQK=16, HV=32, dtype=0, sort=False):
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        ptr = cu.ctypes.data_as(ctypes.c_void_p)
+        N, T = len(lens), int(cu[-1])
+        base = lib.gdn_prefill_workspace_size(N, T, HQK, HV, 128, 128, dtype)
+        lens_ws = lib.gdn_prefill_workspace_size_lens(N, T, ptr, HQK, HV, 128, 128, dtype)
+        name = lib.gdn_prefill_kernel_name(N, T, ptr, HQK, HV, 128, 128, dtype)
+        return base, lens_ws, name
+
+    per_head = 3 * 128 * 256 * 4 + 4 * 128 * 128 * 4
+    base, lens_ws, name = sizes(list(W.varlen_lengths()))
+    assert base == 512 and lens_ws == base + 32 * per_head and name == b"prefill_chunked_split"
+    base, lens_ws, name = sizes([300, 1000, 8192, 257])
+    assert lens_ws == base + 32 * per_head and name == b"prefill_chunked_split"
+    for lens in ([16384] * 4, [32768, 32768, 100], [10000, 9000, 300, 200]):
+        base, lens_ws, name = sizes(lens)
+        assert lens_ws == base and name == b"prefill_chunked", lens
+    base, lens_ws, name = sizes(list(W.varlen_lengths()), dtype=1)  # fp32: token-serial, no workspace
+    assert base == lens_ws and name == b"prefill_recurrent"
+    # without host lengths: the sizes' plan
+    N, T = 65, int(sum(W.varlen_lengths()))
+    assert lib.gdn_prefill_workspace_size_lens(N, T, None, 16, 32, 128, 128, 0) == 512
+    assert lib.gdn_prefill_kernel_name(N, T, None, 16, 32, 128, 128, 0) == b"prefill_chunked"
 
 
 def test_split_workspace_too_small_is_rejected(lib):

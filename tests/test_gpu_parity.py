@@ -153,8 +153,8 @@ _SIX_LONG = [4000] * 6 + [100] * 100
 
 
 @pytest.mark.parametrize("lens,HQK,HV,narrow", [
-    ([8192, 1000, 300, 257], 16, 32, 1),
-    ([300, 1000, 8192, 257], 16, 32, 1),
+    ([10000, 9000, 300, 200], 16, 32, 1),
+    ([200, 9000, 10000, 300], 16, 32, 1),
     (_SIX_LONG, 2, 4, 6),  # 12 narrow groups: two blocks of eight in the grid's narrow part
     (list(np.random.default_rng(3).permutation(_SIX_LONG)), 2, 4, 6),
 ], ids=["one_sorted", "one_unsorted", "six_sorted", "six_shuffled"])
@@ -166,7 +166,8 @@ def test_prefill_narrow_workgroups(lens, HQK, HV, narrow):
     lens = [int(x) for x in lens]
     _say(f"prefill narrow workgroups N={len(lens)} HQK={HQK} HV={HV}")
     inp = W.random_small(49, lens, HQK, HV, 128, 128, p_g0=0.1, p_beta1=0.1)
-    assert binding.prefill_kernel_name(inp.N, inp.total_T, HQK, HV, 128, 128, torch.bfloat16) == "prefill_chunked"
+    assert binding.prefill_kernel_name(inp.N, inp.total_T, HQK, HV, 128, 128, torch.bfloat16,
+                                       cu_seqlens_host=inp.cu_seqlens) == "prefill_chunked"
     assert binding.prefill_narrow_count(inp.cu_seqlens, HQK, HV, 128, 128, torch.bfloat16) == narrow
     d, o, S = _prefill(inp)
     o_ref, S_ref = oracle.run_inputs(inp)
@@ -175,6 +176,38 @@ def test_prefill_narrow_workgroups(lens, HQK, HV, narrow):
                              scale=inp.scale)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(S, S2)
+
+
+@pytest.mark.parametrize("lens,HQK,HV,g_mu", [
+    ([8192, 1000, 300, 257], 16, 32, 2.0),
+    ([300, 1000, 8192, 257], 16, 32, 2.0),
+    ([6000, 700, 500, 300, 100, 0, 64], 8, 16, 2.0),
+    ([64, 0, 6000, 100, 700, 300, 500], 8, 16, 8.0),   # decay close to 1: the maps far from zero
+], ids=["sorted", "unsorted", "seven", "seven_shuffled_weak_decay"])
+def test_prefill_longest_split(lens, HQK, HV, g_mu):
+    """A packed batch whose longest sequence would outlast the rest: given the host lengths and
+    the workspace gdn_prefill_workspace_size_lens reports, that sequence alone is cut into
+    segments (its first scanned beside the other sequences and the maps of its middle ones).
+    Every unit matches the oracle; so does the same call with only the workspace the sizes
+    alone call for, which runs the batch unsplit."""
+    _say(f"prefill longest split N={len(lens)} HQK={HQK} HV={HV} g_mu={g_mu}")
+    inp = W.random_small(50, lens, HQK, HV, 128, 128, p_g0=0.1, p_beta1=0.1, g_mu=g_mu)
+    assert binding.prefill_kernel_name(inp.N, inp.total_T, HQK, HV, 128, 128, torch.bfloat16,
+                                       cu_seqlens_host=inp.cu_seqlens) == "prefill_chunked_split"
+    assert binding.prefill_kernel_name(inp.N, inp.total_T, HQK, HV, 128, 128, torch.bfloat16) == "prefill_chunked"
+    assert binding.prefill_narrow_count(inp.cu_seqlens, HQK, HV, 128, 128, torch.bfloat16) == 0
+    small = binding.prefill_workspace_size(inp.N, inp.total_T, HQK, HV, 128, 128, torch.bfloat16)
+    big = binding.prefill_workspace_size(inp.N, inp.total_T, HQK, HV, 128, 128, torch.bfloat16,
+                                         cu_seqlens_host=inp.cu_seqlens)
+    assert big > small + (1 << 20)
+    d, o, S = _prefill(inp)
+    o_ref, S_ref = oracle.run_inputs(inp)
+    assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), "bf16", "longest split")
+    ws = torch.empty(max(small, 1), dtype=torch.uint8, device="cuda")
+    o2, S2 = binding.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu"],
+                             cu_seqlens_host=inp.cu_seqlens, S0=d["S0"], scale=inp.scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert_parity(to_f64(o2), to_f64(S2), o_ref, S_ref, inp.as_f64("v"), "bf16", "longest split, unsplit fallback")
 
 
 def test_prefill_unit_gates_and_extremes():
