@@ -195,8 +195,8 @@ def varlen_summary(kt_dir: str, only_cmd: str) -> list:
         f"whole call (first kernel start to last kernel end), {len(span)} calls (settle, warm-up and timed): "
         f"median {med:.1f} us, min {span[0]:.1f} us, max {span[-1]:.1f} us -> {tot / med:.1f} Mtok/s, "
         f"{ab / (med * 1e-6) / 1e9:.0f} GB/s algorithmic",
-        f"the longest sequence alone is {longest} tokens = {(longest + 63) // 64} chunks in series for each of "
-        f"its workgroups: {med / ((longest + 63) // 64) * 1e3:.0f} ns per chunk over the median call",
+        f"the longest sequence is {longest} tokens = {(longest + 63) // 64} chunks: the median call takes "
+        f"{med / ((longest + 63) // 64) * 1e3:.0f} ns per chunk of it",
     ]
     for name, us in parts.items():
         lines.append(f"{name}: {duration_stats(us)}")
