@@ -15,6 +15,7 @@ import pytest
 
 torch = pytest.importorskip("torch")
 
+import oracle
 from gated_deltanet_recurrence_rule_amd import binding, workloads as W
 from gdn_testutil import assert_parity, oracle_units, rows_f64, to_device, to_f64
 
@@ -72,6 +73,25 @@ def test_noalloc_equals_workspace_entry_on_two_calls():
     _say("noalloc call 3: fp32, token-serial kernel")
     o_ref, S_ref, o, S = _both(f32, variant="gated_linear")
     assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
+
+
+def test_noalloc_takes_the_lengths_plan():
+    """A packed batch whose longest sequence outlasts the rest: given the host lengths, the
+    allocation-free entry splits that sequence from its static scratch exactly as gdn_prefill_ex
+    does with the workspace gdn_prefill_workspace_size_lens reports (shuffled lengths: the order
+    kernel writes the scratch's first bytes, maps and start tables follow)."""
+    lens = [64, 0, 6000, 100, 700, 300, 500]
+    inp = W.random_small(80, lens, 8, 16, 128, 128, dtype="bf16")
+    assert binding.prefill_kernel_name(inp.N, inp.total_T, 8, 16, 128, 128, torch.bfloat16,
+                                       cu_seqlens_host=inp.cu_seqlens) == "prefill_chunked_split"
+    need = binding.prefill_workspace_size(inp.N, inp.total_T, 8, 16, 128, 128, torch.bfloat16,
+                                          cu_seqlens_host=inp.cu_seqlens)
+    assert 16 << 20 < need <= SCRATCH_BYTES
+    _say(f"noalloc, longest sequence split: {len(lens)} sequences (workspace {need} bytes)")
+    o_ref, S_ref, o, S = _both(inp)
+    assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
+    o_or, S_or = oracle.run_inputs(inp)
+    assert_parity(to_f64(o), to_f64(S), o_or, S_or, inp.as_f64("v"), "bf16", "noalloc longest split")
 
 
 def test_noalloc_rejects_workspace_beyond_the_scratch():
