@@ -486,6 +486,13 @@ def test_longest_sequence_split_plan(lib):
         assert lens_ws == base and name == b"prefill_chunked", lens
     base, lens_ws, name = sizes(list(W.varlen_lengths()), dtype=1)  # fp32: token-serial, no workspace
     assert base == lens_ws and name == b"prefill_recurrent"
+    # more sequences than the order kernel ranks (16384): launched in the given order, so the
+    # longest is split only when the lengths never increase
+    many = [1 << 20] + [64] * 16400
+    base, lens_ws, name = sizes(many)
+    assert base == 0 and lens_ws == 32 * per_head and name == b"prefill_chunked_split"
+    base, lens_ws, name = sizes(many[1:] + many[:1])
+    assert base == 0 and lens_ws == 0 and name == b"prefill_chunked"
     # without host lengths: the sizes' plan
     N, T = 65, int(sum(W.varlen_lengths()))
     assert lib.gdn_prefill_workspace_size_lens(N, T, None, 16, 32, 128, 128, 0) == 512
