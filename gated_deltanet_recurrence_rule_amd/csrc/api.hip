@@ -188,7 +188,7 @@ double chain_step(int64_t ns, int32_t HV, int32_t dv, int64_t cus) {
 // The plan from the sizes alone: only a batch whose (sequence, V head, 64-column) workgroups, u
 // of them, fill at most half the compute units is split, every sequence alike.  The plan
 // minimises a model of the time in chunk periods, with c the average chunks per sequence:
-//   unsplit, every sequence on 32-column workgroups (section on narrow workgroups): 0.87 c;
+//   unsplit, every sequence on 32-column workgroups (see narrow_sequences below): 0.87 c;
 //   split: the map pass scans segment 0 on u workgroups while the maps of segments 1 .. P-2
 //   (um workgroups each, the table widened by dk columns) take rm = ceil((P-2) um / (CUs - u))
 //   rounds of the rest, so segment 0 gets w0 = max(1, rm) units; the segment pass takes
