@@ -297,41 +297,49 @@ int32_t narrow_for_batch(int32_t N, int32_t HV, int32_t dv, const int32_t *cu_ho
     return narrow_sequences(length_stats(cu_host, N, u), N, u, cus, nullptr);
 }
 
-// The longest sequence of a packed batch alone cut into segments (ns = 1), for the batch the
-// sizes alone leave unsplit, when its host lengths are known and the launch order is longest
-// first.  With c_0, c_1 the two largest chunk counts, u (um) the sequence's 64-column
-// workgroups (with dk extra columns) and rest the other sequences' work, the model is
-//   map pass:     max(w0 a, c_1, (rest + (P-2) um a) / (CUs - u)), a = ceil(c_0 / (P - 1 + w0))
-//                 (segment 0 on u units; the maps, launched first, and the others on the rest),
-//   segment pass: ceil((P-1) u / CUs) a,
+// The k longest sequences of a packed batch cut into segments (ns = k, 1 <= k <= 8), for the batch
+// the sizes alone leave unsplit, when its host lengths are known and the launch order is longest
+// first.  With c_0 >= c_1 >= ... the chunk counts, u (um) a sequence's 64-column workgroups (with
+// dk extra columns), a_i = ceil(c_i / (P - 1 + w0)) and rest the unsplit sequences' work, the
+// model is
+//   map pass:     max(w0 a_0, c_k, (rest + sum_i<k (P-2) um a_i) / (CUs - k u))
+//                 (the segments 0 on k u units; the maps and the unsplit sequences on the rest),
+//   segment pass: ceil(k (P-1) u / CUs) a_0,
 // plus the chain and the fixed 3 as above.  Taken where it gains 3% over the unsplit plan.
-SplitPlan split_longest(const LengthStats &ls, int32_t HV, int32_t dk, int32_t dv, int64_t cus, double t_unsplit) {
+SplitPlan split_longest(const LengthStats &ls, int32_t N, int32_t HV, int32_t dk, int32_t dv, int64_t cus,
+                        double t_unsplit) {
     SplitPlan best;
     const int64_t u = (int64_t)HV * (dv / 64), um = (int64_t)HV * ((dv + dk) / 64);
-    if (ls.ntop < 2 || u <= 0 || 2 * u > cus) return best;
-    const int64_t c0 = ls.top[0], c1 = ls.top[1];
-    const double rest = ls.work - (double)c0 * (double)u;
-    const double step = chain_step(1, HV, dv, cus);
+    if (u <= 0 || 2 * u > cus) return best;
     double t_best = 0.97 * t_unsplit;
-    for (int32_t P = 3; P <= 16; ++P)
-        for (int32_t w0 = 1; w0 <= 16; ++w0) {
-            const int64_t a = (c0 + P - 2 + w0) / (P - 1 + w0);
-            const double pass1 = std::max(std::max((double)(w0 * a), (double)c1),
-                                          (rest + (double)((P - 2) * um * a)) / (double)(cus - u));
-            const double pass2 = (double)((((P - 1) * u + cus - 1) / cus) * a);
-            const double t = pass1 + pass2 + (P - 2) * step + 3.0;
-            if (t < t_best) {
-                t_best = t;
-                best.P = P;
-                best.w0 = w0;
-                best.ns = 1;
+    double rest = ls.work;
+    for (int32_t k = 1; k <= 8 && k <= N && k <= ls.ntop && k * u < cus; ++k) {
+        rest -= (double)ls.top[k - 1] * (double)u;
+        const double ck = k < ls.ntop ? (double)ls.top[k] : 0.0;
+        const double step = chain_step(k, HV, dv, cus);
+        for (int32_t P = 3; P <= 16; ++P)
+            for (int32_t w0 = 1; w0 <= 16; ++w0) {
+                const int64_t units = P - 1 + w0;
+                int64_t maps = 0;
+                for (int32_t i = 0; i < k; ++i) maps += (P - 2) * um * ((ls.top[i] + units - 1) / units);
+                const int64_t a0 = (ls.top[0] + units - 1) / units;
+                const double pass1 = std::max(std::max((double)(w0 * a0), ck),
+                                              (rest + (double)maps) / (double)(cus - k * u));
+                const double pass2 = (double)((((int64_t)k * (P - 1) * u + cus - 1) / cus) * a0);
+                const double t = pass1 + pass2 + (P - 2) * step + 3.0;
+                if (t < t_best) {
+                    t_best = t;
+                    best.P = P;
+                    best.w0 = w0;
+                    best.ns = k;
+                }
             }
-        }
+    }
     return best;
 }
 
 // The plan for a batch whose host lengths are known and whose launch order is longest first:
-// the sizes' plan where it splits, else the longest sequence split where that pays, else the
+// the sizes' plan where it splits, else the longest sequences split where that pays, else the
 // narrow rule.
 struct LengthPlan {
     SplitPlan split;
@@ -353,7 +361,7 @@ LengthPlan plan_for_lengths(int32_t N, int64_t total_T, const int32_t *cu_host, 
     const LengthStats ls = length_stats(cu_host, N, u);
     double t_unsplit = 0.0;
     lp.narrow = narrow_sequences(ls, N, u, cus, &t_unsplit);
-    const SplitPlan sl = split_longest(ls, HV, dk, dv, cus, t_unsplit);
+    const SplitPlan sl = split_longest(ls, N, HV, dk, dv, cus, t_unsplit);
     if (sl.P > 1) {
         lp.split = sl;
         lp.narrow = 0;

@@ -159,12 +159,12 @@ size_t gdn_prefill_workspace_size(int32_t N, int64_t total_T, int32_t HQK, int32
  * gdn_prefill_workspace_size_lens -- the workspace for a packed batch whose host lengths are
  * known (cu_seqlens_host, N + 1 int32 entries, read during the call only; NULL gives
  * gdn_prefill_workspace_size).  At least gdn_prefill_workspace_size; more where the batch,
- * unsplit by its sizes, has one sequence that would outlast the rest (the 262144-token
- * sequence of a 65-sequence batch): a model of the time in chunk periods may then cut that
- * sequence alone into P segments as above.  Its first segment is scanned while the other
- * sequences run whole, beside the maps of its middle segments.  The extra part holds
- * (P-2) HV dk (dv + dk) + (P-1) HV dk dv floats (20 MiB for that batch with 32 heads of
- * d = 128, P = 5).  gdn_prefill, given the host lengths and a workspace of this size, takes
+ * unsplit by its sizes, has sequences that would outlast the rest (the 262144-token sequence
+ * of a 65-sequence batch, two long prompts among short ones): a model of the time in chunk
+ * periods may then cut its k longest sequences (1 <= k <= 8) into P segments as above.  Their
+ * first segments are scanned while the other sequences run whole, beside the maps of their
+ * middle segments.  The extra part holds k (P-2) HV dk (dv + dk) + k (P-1) HV dk dv floats
+ * (20 MiB for that 65-sequence batch with 32 heads of d = 128: k = 1, P = 5).  gdn_prefill, given the host lengths and a workspace of this size, takes
  * that plan; given a smaller one of at least gdn_prefill_workspace_size bytes, it runs the
  * batch unsplit, with the same results to rounding.  Launch order longest first is assumed:
  * batches of more than 16384 sequences qualify only with non-increasing lengths.

@@ -441,9 +441,11 @@ def test_narrow_workgroup_rule(lib):
         return lib.gdn_prefill_narrow_count(len(lens), int(cu[-1]), ptr, HQK, HV, dk, dv, dtype)
 
     from gated_deltanet_recurrence_rule_amd import workloads as W
-    assert count([10000, 9000, 300, 200]) == 1
-    assert count([200, 9000, 10000, 300]) == 1  # the rule does not need sorted lengths
-    assert count([4000] * 6 + [100] * 100, HQK=2, HV=4) == 6
+    assert count([1000, 900, 300, 200]) == 1
+    assert count([200, 900, 1000, 300]) == 1  # the rule does not need sorted lengths
+    assert count([1000] * 6 + [100] * 100, HQK=2, HV=4) == 6
+    assert count([4000] * 6 + [100] * 100, HQK=2, HV=4) == 0  # long enough to split the six instead
+    assert count([10000, 9000, 300, 200]) == 0  # the two longest split
     assert count(list(W.varlen_lengths())) == 0  # its 262144-token sequence is split instead
     assert count([262144] + [1000] * 10) == 0
     assert count([8192, 1000, 300, 257]) == 0
@@ -454,12 +456,12 @@ def test_narrow_workgroup_rule(lib):
     assert count([8192, 100], host=False) == 2
     assert count([8192], HQK=16, HV=16) == 0  # 32 workgroups: split into 9 segments instead
     assert count([8192, 1000, 300, 257], dtype=1) == 0  # fp32: token-serial kernel
-    assert count([10000, 9000, 300, 200], host=False) == 0
+    assert count([1000, 900, 300, 200], host=False) == 0
 
 
 def test_longest_sequence_split_plan(lib):
     """With the host lengths, a packed batch that the sizes alone leave unsplit may have its
-    longest sequence cut into segments (no GPU here: 256 compute units assumed).
+    longest sequences cut into segments (no GPU here: 256 compute units assumed).
     The 65-sequence batch (64 lengths of 128 .. 32768 tokens and one of 262144), 32 V heads of
     d = 128: the model takes P = 5, so the workspace grows by 3 maps of 128 x 256 and 4 start
     tables of 128 x 128 per head for that one sequence; the kernel is then the split one.
@@ -481,7 +483,10 @@ def test_longest_sequence_split_plan(lib):
     assert base == 512 and lens_ws == base + 32 * per_head and name == b"prefill_chunked_split"
     base, lens_ws, name = sizes([300, 1000, 8192, 257])
     assert lens_ws == base + 32 * per_head and name == b"prefill_chunked_split"
-    for lens in ([16384] * 4, [32768, 32768, 100], [10000, 9000, 300, 200]):
+    # the two longest of three: P = 3, one map and two start tables per head for each
+    base, lens_ws, name = sizes([32768, 32768, 100])
+    assert lens_ws == base + 2 * 32 * (128 * 256 * 4 + 2 * 128 * 128 * 4) and name == b"prefill_chunked_split"
+    for lens in ([16384] * 4, [16384] * 3, [1000, 900, 300, 200]):
         base, lens_ws, name = sizes(lens)
         assert lens_ws == base and name == b"prefill_chunked", lens
     base, lens_ws, name = sizes(list(W.varlen_lengths()), dtype=1)  # fp32: token-serial, no workspace

@@ -149,12 +149,12 @@ def test_prefill_every_tail_length():
     assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), "bf16", "every tail length")
 
 
-_SIX_LONG = [4000] * 6 + [100] * 100
+_SIX_LONG = [1000] * 6 + [100] * 100
 
 
 @pytest.mark.parametrize("lens,HQK,HV,narrow", [
-    ([10000, 9000, 300, 200], 16, 32, 1),
-    ([200, 9000, 10000, 300], 16, 32, 1),
+    ([1000, 900, 300, 200], 16, 32, 1),
+    ([200, 900, 1000, 300], 16, 32, 1),
     (_SIX_LONG, 2, 4, 6),  # 12 narrow groups: two blocks of eight in the grid's narrow part
     (list(np.random.default_rng(3).permutation(_SIX_LONG)), 2, 4, 6),
 ], ids=["one_sorted", "one_unsorted", "six_sorted", "six_shuffled"])
@@ -183,13 +183,16 @@ def test_prefill_narrow_workgroups(lens, HQK, HV, narrow):
     ([300, 1000, 8192, 257], 16, 32, 2.0),
     ([6000, 700, 500, 300, 100, 0, 64], 8, 16, 2.0),
     ([64, 0, 6000, 100, 700, 300, 500], 8, 16, 8.0),   # decay close to 1: the maps far from zero
-], ids=["sorted", "unsorted", "seven", "seven_shuffled_weak_decay"])
+    ([200, 9000, 300, 10000], 16, 32, 8.0),             # the two longest split, of unequal length
+    (list(np.random.default_rng(4).permutation([4000] * 6 + [100] * 100)), 2, 4, 2.0),  # six split
+], ids=["sorted", "unsorted", "seven", "seven_shuffled_weak_decay", "two_unequal_weak_decay", "six_of_106"])
 def test_prefill_longest_split(lens, HQK, HV, g_mu):
-    """A packed batch whose longest sequence would outlast the rest: given the host lengths and
-    the workspace gdn_prefill_workspace_size_lens reports, that sequence alone is cut into
-    segments (its first scanned beside the other sequences and the maps of its middle ones).
-    Every unit matches the oracle; so does the same call with only the workspace the sizes
-    alone call for, which runs the batch unsplit."""
+    """A packed batch whose longest sequences would outlast the rest: given the host lengths and
+    the workspace gdn_prefill_workspace_size_lens reports, those sequences are cut into segments
+    (their first segments scanned beside the other sequences and the maps of their middle ones).
+    Every unit matches the oracle; so does the same call with only the workspace the sizes alone
+    call for, which runs the batch unsplit."""
+    lens = [int(x) for x in lens]
     _say(f"prefill longest split N={len(lens)} HQK={HQK} HV={HV} g_mu={g_mu}")
     inp = W.random_small(50, lens, HQK, HV, 128, 128, p_g0=0.1, p_beta1=0.1, g_mu=g_mu)
     assert binding.prefill_kernel_name(inp.N, inp.total_T, HQK, HV, 128, 128, torch.bfloat16,
