@@ -284,7 +284,7 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     //    that would outlast the rest of the batch finishes sooner on twice the workgroups; part
     //    2 holds the other sequences on 64-column workgroups.
     //  * Split sequences: the first sp.ns launch ranks (every sequence of a small batch, or the
-    //    longest of a packed one) are cut into P = sp.P >= 3 segments of whole chunks; with cps =
+    //    k longest of a packed one) are cut into P = sp.P >= 3 segments of whole chunks; with cps =
     //    ceil(chunks / (P - 1 + w0)), segment 0 is w0 cps chunks long and segment s >= 1 takes
     //    chunks [(w0 + s - 1) cps, (w0 + s) cps).
     //    - map pass (sp.mode 1): part 0 scans segment 0 of the split ranks from S0, writing its
