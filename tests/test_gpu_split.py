@@ -1,8 +1,10 @@
 """GPU parity of split sequences: a batch too small to fill the GPU has each sequence cut
-into segments whose affine maps (S_out = M S_in + B, from the recurrence of the handbook
-page "7. Gated DeltaNet: the token-by-token recurrence", section "The formula") are formed in
-parallel, chained, and then every segment rescanned from its start table.  The result must
-match the float64 oracle's token loop to the same tolerances as the unsplit path.
+into segments.  The first is scanned from the start table while the affine maps of the middle
+ones (S_out = M S_in + B, from the recurrence of the handbook page "7. Gated DeltaNet: the
+token-by-token recurrence", section "The formula") are formed in parallel; the maps are
+chained from the first segment's final table, and every later segment is then scanned from
+its start table.  The result must match the float64 oracle's token loop to the same
+tolerances as the unsplit path.
 """
 import sys
 
