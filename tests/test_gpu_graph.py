@@ -100,6 +100,53 @@ def test_prefill_graph_replays():
         _ = (o_e.float() * 2).sum().item()
 
 
+@pytest.mark.parametrize("lens,HQK,HV,host", [
+    ([3000], 1, 2, False),                        # the sizes' plan splits every sequence
+    ([64, 0, 6000, 100, 700, 300, 500], 8, 16, True),  # the host lengths split the longest
+], ids=["split_by_sizes", "longest_split_by_lengths"])
+def test_split_prefill_graph_replays(lens, HQK, HV, host):
+    """Split sequences under capture: the segment-map pass, the chain and the segment pass (and,
+    for the shuffled batch, the order kernel) in one graph, the maps and start tables in the
+    caller's workspace."""
+    _say(f"graph: split prefill {lens} HQK={HQK} HV={HV}, 3 replays")
+    inputs = [W.random_small(130 + i, lens, HQK, HV, 128, 128, dtype="bf16", s0=True) for i in range(3)]
+    devs = [to_device(x) for x in inputs]
+    hl = inputs[0].cu_seqlens if host else None
+    assert binding.prefill_kernel_name(len(lens), sum(lens), HQK, HV, 128, 128, torch.bfloat16,
+                                       cu_seqlens_host=hl) == "prefill_chunked_split"
+    static = {k: v.clone() for k, v in devs[0].items() if v is not None}
+    o_static = torch.empty_like(static["v"])
+    ST_static = torch.empty_like(static["S0"])
+    nws = binding.prefill_workspace_size(len(lens), sum(lens), HQK, HV, 128, 128, torch.bfloat16,
+                                         cu_seqlens_host=hl)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+
+    def call():
+        binding.prefill(static["q"], static["k"], static["v"], static["g"], static["beta"], cu_seqlens=static["cu"],
+                        cu_seqlens_host=hl, S0=static["S0"], o=o_static, S_T=ST_static, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for i, (inp, d) in enumerate(zip(inputs, devs)):
+        for k in ("q", "k", "v", "g", "beta", "S0"):
+            static[k].copy_(d[k])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        o_e, S_e = binding.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu"],
+                                   cu_seqlens_host=hl, S0=d["S0"])
+        torch.cuda.synchronize()
+        assert torch.equal(o_static, o_e), f"replay {i}: reads differ from the eager call"
+        assert torch.equal(ST_static, S_e), f"replay {i}: tables differ from the eager call"
+        _ = (o_e.float() * 2).sum().item()
+
+
 def test_block_parts_graph_replays():
     """The causal convolution + SiLU (carried state in and out) and the gated RMS norm of its v
     channels, captured together."""
