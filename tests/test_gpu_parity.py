@@ -260,6 +260,23 @@ def test_prefill_longest_first_order(host_lengths):
     assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), "bf16", "order")
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 32)])
+def test_prefill_beyond_the_sorted_batch_size(dtype, d):
+    """More sequences than the order kernel sorts (16384): the workspace has no order part,
+    the sequences launch in the given (unsorted) order, and every one, the empty ones
+    included, still matches the oracle."""
+    rng = np.random.default_rng(11)
+    N = 16384 + 37
+    lens = [int(x) for x in rng.integers(0, 80, size=N)]
+    _say(f"prefill beyond the sorted size: N={N} {dtype} d={d} T={sum(lens)}")
+    inp = W.random_small(48, lens, 1, 1, d, d, dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    assert binding.prefill_workspace_size(N, inp.total_T, 1, 1, d, d, tdt) == 0
+    _, o, S = _prefill(inp)
+    o_ref, S_ref = oracle.run_inputs(inp)
+    assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), dtype, "beyond the sorted size")
+
+
 def test_prefill_equal_lengths_without_cu_seqlens():
     inp = W.random_small(44, [33, 33, 33], 2, 4, 64, 64)
     d = to_device(inp)
