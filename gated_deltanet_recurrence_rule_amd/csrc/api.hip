@@ -179,10 +179,12 @@ struct SplitPlan {
     int32_t P = 1, w0 = 1, ns = 0;
 };
 
-// Chain steps in chunk periods: one workgroup per (split sequence, V head, 8 columns), two per CU.
+// Chain steps in chunk periods: one workgroup per (split sequence, V head, 16 columns), one per
+// CU at the register count of the longer chains.  1.2 periods per step and round was measured on
+// an earlier, slower chain; the current one takes ~0.8, and the plans hardly change with it.
 double chain_step(int64_t ns, int32_t HV, int32_t dv, int64_t cus) {
-    const int64_t wgs = ns * HV * (dv / 8);
-    return 1.2 * (double)((wgs + 2 * cus - 1) / (2 * cus));
+    const int64_t wgs = ns * HV * (dv / 16);
+    return 1.2 * (double)((wgs + cus - 1) / cus);
 }
 
 // The plan from the sizes alone: only a batch whose (sequence, V head, 64-column) workgroups, u

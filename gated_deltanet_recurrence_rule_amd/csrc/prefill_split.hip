@@ -9,11 +9,15 @@
 // start tables of segments 2 .. P-1; the segment pass then runs segments 1 .. P-1 at once
 // from their tables.
 //
-// One workgroup per (split sequence, V head, 8 columns of dv): columns of the table evolve
-// independently, so a column block chains on its own.  Per step it stages M (128 x 128
-// fp32, rows padded to 132 floats so that 16 rows read in one wave fall in distinct
-// banks) in LDS, the next step's M already on its way in registers; each thread forms
-// 4 columns of one row of M S + B with fp32 FMAs.
+// One workgroup per (split sequence, V head, 16 columns of dv): columns of the table evolve
+// independently, so a column block chains on its own.  Each step is the product M S_in on
+// fp32 MFMA (16 x 16 x 4), B loaded as the accumulators' start value: wave w forms rows
+// 32 w .. 32 w + 31.  M comes from memory straight into the A operands, the next two steps'
+// already on their way while this one multiplies; S_in sits in LDS transposed (one padded row
+// per column), double-buffered, so a step needs one barrier.  The contraction index is
+// permuted: in k-step 4 q + e, lane group g (lanes 16 g .. 16 g + 15) carries
+// k = 16 q + 4 g + e, so that a lane reads 4 consecutive floats of its M row (and of its
+// S_in column) per load, and the four groups together 64 consecutive bytes of the row.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -22,69 +26,110 @@ namespace gdn {
 namespace {
 
 constexpr int SDK = 128;      // dk of the chunked path
-constexpr int SLM = SDK + 4;  // padded LDS row of M
-constexpr int SCB = 8;        // columns per workgroup
+constexpr int SCB = 16;       // columns per workgroup
+constexpr int SLT = SDK + 4;  // padded LDS row (one column of S_in)
+constexpr int kMaxSplitSegments = 16;  // the planners choose P in 3 .. 16
 
-__global__ __launch_bounds__(256) void split_chain_kernel(const float *__restrict__ maps, float *__restrict__ starts,
-                                                          int P, int HV, int DV) {
-    __shared__ __attribute__((aligned(16))) float Ms[SDK * SLM];
-    __shared__ __attribute__((aligned(16))) float Sb[SDK * SCB];
+// NS = P - 2 chain steps, fully unrolled: the maps of steps j + 1 and j + 2 are in flight
+// while step j multiplies (three register sets in rotation), with no branch between a
+// load and its use.
+template <int NS>
+__global__ __launch_bounds__(256) void split_chain_kernel(const float *maps, float *starts, int HV, int DV) {
+    constexpr int P = NS + 2;
+    __shared__ __attribute__((aligned(16))) float St[2][SCB * SLT];
     const int unit = blockIdx.x;  // rank * HV + h
     const int n = unit / HV, h = unit % HV;
     const int c0 = blockIdx.y * SCB;
     const int DW = DV + SDK;
-    const int tid = threadIdx.x;
-    const int c4 = tid & 1, r = tid >> 1;  // columns c0 + 4 c4 .. + 3 of row r
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
 
     // start table of segment j (1 .. P-1) and map of segment j (1 .. P-2)
     auto sin_at = [&](int j) { return starts + ((size_t)(n * (P - 1) + j - 1) * HV + h) * SDK * DV; };
     auto map_at = [&](int j) { return maps + ((size_t)(n * (P - 2) + j - 1) * HV + h) * SDK * DW; };
-    // segment 1 starts where the map pass's scan of segment 0 ended
-    for (int idx = tid; idx < SDK * SCB; idx += 256) {
-        const int row = idx / SCB, col = idx % SCB;
-        Sb[idx] = sin_at(1)[(size_t)row * DV + c0 + col];
-    }
-    // M of the next step is loaded into registers while this step computes (16 float4 per
-    // thread), then stored to LDS once every thread is done reading the current one.
-    constexpr int NLD = SDK * SDK / 4 / 256;
-    f32x4 mreg[NLD];
-    auto load_m = [&](int j) {
+    // Operands of one step: A = M rows 32 w + 16 b + r16, k = 16 q + 4 g + e (8 float4 per
+    // row block); the accumulators start from B at rows 32 w + 16 b + 4 g + i, column c0 + r16.
+    f32x4 m[3][2][8], bv[3][2];
+    auto load = [&](int j) {
         const float *map = map_at(j);
+        const int slot = j % 3;
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int f = tid + 256 * i;
-            const int rr = f / (SDK / 4), kq = f % (SDK / 4);
-            mreg[i] = *reinterpret_cast<const f32x4 *>(map + (size_t)rr * DW + DV + 4 * kq);
+        for (int b = 0; b < 2; ++b) {
+            const float *rp = map + (size_t)(32 * w + 16 * b + r16) * DW + DV + 4 * g;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) m[slot][b][q] = *reinterpret_cast<const f32x4 *>(rp + 16 * q);
+            const float *bp = map + (size_t)(32 * w + 16 * b + 4 * g) * DW + c0 + r16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bv[slot][b][i] = bp[(size_t)i * DW];
         }
     };
-    auto store_m = [&]() {
+    load(1);
+    if (NS >= 2) load(2);
+    // segment 1 starts where the map pass's scan of segment 0 ended (all loads issued
+    // before the first wait)
+    {
+        float sv[SDK * SCB / 256];
+        const float *s1 = sin_at(1);
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int f = tid + 256 * i;
-            const int rr = f / (SDK / 4), kq = f % (SDK / 4);
-            *reinterpret_cast<f32x4 *>(&Ms[rr * SLM + 4 * kq]) = mreg[i];
+        for (int i = 0; i < SDK * SCB / 256; ++i) {
+            const int idx = tid + 256 * i;
+            sv[i] = s1[(size_t)(idx / SCB) * DV + c0 + idx % SCB];
         }
-    };
-    if (P > 2) load_m(1);
-    for (int j = 1; j + 1 < P; ++j) {
-        const float *map = map_at(j);
-        __syncthreads();  // Sb holds S_in(j); every read of Ms is done
-        store_m();
-        __syncthreads();
-        if (j + 2 < P) load_m(j + 1);
-        f32x4 acc = *reinterpret_cast<const f32x4 *>(map + (size_t)r * DW + c0 + 4 * c4);
-        for (int k = 0; k < SDK; k += 4) {
-            const f32x4 m0 = *reinterpret_cast<const f32x4 *>(&Ms[r * SLM + k]);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const f32x4 sv = *reinterpret_cast<const f32x4 *>(&Sb[(k + kk) * SCB + 4 * c4]);
-                acc += m0[kk] * sv;
-            }
+        for (int i = 0; i < SDK * SCB / 256; ++i) {
+            const int idx = tid + 256 * i;
+            St[0][(idx % SCB) * SLT + idx / SCB] = sv[i];
         }
-        __syncthreads();  // every read of Sb done
-        *reinterpret_cast<f32x4 *>(&Sb[r * SCB + 4 * c4]) = acc;
-        *reinterpret_cast<f32x4 *>(sin_at(j + 1) + (size_t)r * DV + c0 + 4 * c4) = acc;
     }
+    __syncthreads();
+#pragma unroll
+    for (int j = 1; j <= NS; ++j) {
+        if (j + 2 <= NS) load(j + 2);
+        __builtin_amdgcn_sched_barrier(0);  // the loads first, ahead of this step's products
+        const int slot = j % 3;
+        const float *src = St[(j - 1) & 1];
+        float *dst = St[j & 1];
+        f32x4 sv[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) sv[q] = *reinterpret_cast<const f32x4 *>(&src[r16 * SLT + 16 * q + 4 * g]);
+        // two accumulators per row block (k-steps 0..15 and 16..31): four independent chains
+        f32x4 acc[2][2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            acc[b][0] = bv[slot][b];
+            acc[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int b = 0; b < 2; ++b)
+                        acc[b][hh] = __builtin_amdgcn_mfma_f32_16x16x4f32(m[slot][b][q + 4 * hh][e],
+                                                                         sv[q + 4 * hh][e], acc[b][hh], 0, 0, 0);
+        float *out = sin_at(j + 1);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const f32x4 res = acc[b][0] + acc[b][1];
+            const int row = 32 * w + 16 * b + 4 * g;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) out[(size_t)(row + i) * DV + c0 + r16] = res[i];
+            *reinterpret_cast<f32x4 *>(&dst[r16 * SLT + row]) = res;
+        }
+        __syncthreads();  // dst complete for the next step; every read of src done
+    }
+}
+
+template <int NS>
+void launch_chain_steps(const float *maps, float *starts, int32_t ns, int32_t P, int32_t HV, int32_t dv,
+                        hipStream_t stream) {
+    if constexpr (NS > 1) {
+        if (P - 2 < NS) return launch_chain_steps<NS - 1>(maps, starts, ns, P, HV, dv, stream);
+    }
+    hipLaunchKernelGGL(split_chain_kernel<NS>, dim3((unsigned)(ns * HV), (unsigned)(dv / SCB)), dim3(256), 0, stream,
+                       maps, starts, HV, dv);
 }
 
 }  // namespace
@@ -92,9 +137,8 @@ __global__ __launch_bounds__(256) void split_chain_kernel(const float *__restric
 hipError_t launch_split_chain(const float *maps, float *starts, int32_t ns, int32_t P, int32_t HV, int32_t dv,
                               hipStream_t stream) {
     if (ns == 0 || P < 3) return hipSuccess;
-    if (dv % SCB != 0 || (int64_t)ns * HV > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(split_chain_kernel, dim3((unsigned)(ns * HV), (unsigned)(dv / SCB)), dim3(256), 0, stream,
-                       maps, starts, P, HV, dv);
+    if (P > kMaxSplitSegments || dv % SCB != 0 || (int64_t)ns * HV > 0x7fffffffLL) return hipErrorInvalidValue;
+    launch_chain_steps<kMaxSplitSegments - 2>(maps, starts, ns, P, HV, dv, stream);
     return hipGetLastError();
 }
 
