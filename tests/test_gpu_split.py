@@ -98,6 +98,27 @@ def test_split_prefill_weak_decay(lens, HQK, HV, P):
     assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), "bf16", f"split weak decay P={P}")
 
 
+# One sequence, one head: the planner picks every segment count from 4 to 16 as the length
+# grows (P = 3 is covered above), so each unrolled chain kernel (P - 2 steps) runs once.
+_EVERY_P = [(4, 1024), (5, 1280), (6, 1152), (7, 1664), (8, 2048), (9, 2304), (10, 3200), (11, 4096),
+            (12, 4608), (13, 4992), (14, 6272), (15, 7552), (16, 8192)]
+
+
+@pytest.mark.parametrize("P,T", _EVERY_P, ids=lambda x: str(x))
+def test_split_prefill_every_segment_count(P, T):
+    """Weak decay (maps far from zero), one head: every chain length the planner can choose."""
+    _say(f"split prefill, every segment count: P={P} T={T}")
+    inp = W.random_small(86 + P, [T], 1, 1, 128, 128, dtype="bf16", s0=True, g_mu=8.0, g_sd=1.0)
+    assert _split_plan_P(inp) == P
+    d = to_device(inp)
+    o, S = binding.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu"],
+                           cu_seqlens_host=inp.cu_seqlens, S0=d["S0"], scale=inp.scale)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.run(inp.as_f64("q"), inp.as_f64("k"), inp.as_f64("v"), inp.as_f64("g"),
+                              inp.as_f64("beta"), inp.cu_seqlens, inp.as_f64("S0"), scale=inp.scale)
+    assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), "bf16", f"split every P={P}")
+
+
 def test_split_prefill_equal_lengths_in_place_raw_gates():
     """cu_seqlens NULL (equal lengths), the final table written over the start table, gates from
     raw projections: the split path reads S0 only before its segment pass."""
