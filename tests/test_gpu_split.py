@@ -119,6 +119,23 @@ def test_split_prefill_every_segment_count(P, T):
     assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), "bf16", f"split every P={P}")
 
 
+@pytest.mark.parametrize("lens,HQK,HV,P", [([2048, 2048], 1, 2, 8), ([1500, 1500], 1, 3, 6)],
+                         ids=["2x2048_h1-2", "2x1500_h1-3"])
+def test_split_prefill_weak_decay_dv64(lens, HQK, HV, P):
+    """dv = 64 (four 16-column chain blocks of a 192-column map row), grouped heads, two split
+    sequences, maps far from zero."""
+    _say(f"split prefill, weak decay, dv=64: lens={lens} HQK={HQK} HV={HV}")
+    inp = W.random_small(87, lens, HQK, HV, 128, 64, dtype="bf16", s0=True, g_mu=8.0, g_sd=1.0)
+    assert _split_plan_P(inp) == P
+    d = to_device(inp)
+    o, S = binding.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu"],
+                           cu_seqlens_host=inp.cu_seqlens, S0=d["S0"], scale=inp.scale)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.run(inp.as_f64("q"), inp.as_f64("k"), inp.as_f64("v"), inp.as_f64("g"),
+                              inp.as_f64("beta"), inp.cu_seqlens, inp.as_f64("S0"), scale=inp.scale)
+    assert_parity(to_f64(o), to_f64(S), o_ref, S_ref, inp.as_f64("v"), "bf16", f"split weak decay dv=64 P={P}")
+
+
 def test_split_prefill_equal_lengths_in_place_raw_gates():
     """cu_seqlens NULL (equal lengths), the final table written over the start table, gates from
     raw projections: the split path reads S0 only before its segment pass."""
